@@ -1,0 +1,245 @@
+// C ABI of the PACK3D forward (declarations and contracts in pack3d.h).
+// Host-side argument validation, workspace layout and kernel launches.
+#include <math.h>
+#include <string.h>
+
+#include "launch.hpp"
+
+using namespace pk;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+size_t elem_size(int dtype) { return dtype == PACK3D_BF16 ? 2 : 4; }
+
+// Validates a descriptor and derives the kernel geometry.
+int make_geo(const pack3d_desc *d, Geo *g) {
+  if (!d) return PACK3D_ERR_INVALID_ARG;
+  if (d->B <= 0 || d->N <= 0 || d->H <= 0 || d->D <= 0) return PACK3D_ERR_INVALID_ARG;
+  if (d->dtype != PACK3D_F32 && d->dtype != PACK3D_BF16) return PACK3D_ERR_INVALID_ARG;
+  if (d->exclusion < PACK3D_EXCL_NONE || d->exclusion > PACK3D_EXCL_NEIGHBOURHOOD_BLOCKS)
+    return PACK3D_ERR_INVALID_ARG;
+  if (!(d->rope_base > 0.0f) || !isfinite(d->rope_base)) return PACK3D_ERR_INVALID_ARG;
+  if (!isfinite(d->scale)) return PACK3D_ERR_INVALID_ARG;
+  for (int a = 0; a < 3; a++)
+    if (d->grid[a] <= 0 || d->block[a] <= 0) return PACK3D_ERR_SHAPE;
+  if (d->D % 6 != 0) return PACK3D_ERR_SHAPE;
+  const int64_t sites = (int64_t)d->grid[0] * d->grid[1] * d->grid[2];
+  if (sites != d->N) return PACK3D_ERR_SHAPE;
+  // element offsets are int64 in every kernel; keep token / site / summary
+  // counts and per-row sizes inside int32
+  if ((int64_t)d->B * d->N * d->H > ((int64_t)1 << 40)) return PACK3D_ERR_SHAPE;
+  if ((int64_t)d->N * 27 > INT32_MAX || (int64_t)d->H * d->D > 1024) return PACK3D_ERR_SHAPE;
+  memset(g, 0, sizeof(*g));
+  g->B = d->B;
+  g->N = d->N;
+  g->H = d->H;
+  g->D = d->D;
+  g->Z = d->grid[0];
+  g->Y = d->grid[1];
+  g->X = d->grid[2];
+  g->bz = d->block[0];
+  g->by = d->block[1];
+  g->bx = d->block[2];
+  g->Mz = (g->Z + g->bz - 1) / g->bz;
+  g->My = (g->Y + g->by - 1) / g->by;
+  g->Mx = (g->X + g->bx - 1) / g->bx;
+  const int64_t M = (int64_t)g->Mz * g->My * g->Mx;
+  const int64_t vol = (int64_t)g->bz * g->by * g->bx;
+  if (M > INT32_MAX / 2 || vol > INT32_MAX / 2) return PACK3D_ERR_SHAPE;
+  g->M = (int)M;
+  g->vol = (int)vol;
+  g->P = d->D / 6;
+  g->scale = d->scale > 0.0f ? d->scale : (float)(1.0 / sqrt((double)d->D));
+  g->rope_base = d->rope_base;
+  g->excl = d->exclusion;
+  g->slot_off = (int64_t)kAlign;
+  g->table_off = (int64_t)align_up(kAlign + (size_t)sites * 4);
+  return PACK3D_OK;
+}
+
+size_t geometry_bytes(const Geo &g) {
+  return align_up((size_t)g.table_off + (size_t)(g.Z + g.Y + g.X) * g.P * 8);
+}
+
+size_t summary_bytes(const Geo &g, int dtype) {
+  return align_up((size_t)g.B * g.H * g.M * g.D * elem_size(dtype));
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PACK3D_OK : PACK3D_ERR_HIP; }
+
+// Synchronises and reads the status word when the caller asked for it.
+int validate_coords(const pack3d_desc *d, const void *geom, hipStream_t s) {
+  if (!(d->flags & PACK3D_VALIDATE)) return PACK3D_OK;
+  int32_t status = 0;
+  if (hipMemcpyAsync(&status, geom, sizeof(status), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return PACK3D_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return PACK3D_ERR_HIP;
+  return status ? PACK3D_ERR_COORDS : PACK3D_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pack3d_abi_version(void) { return PACK3D_ABI_VERSION; }
+
+const char *pack3d_strerror(int status) {
+  switch (status) {
+    case PACK3D_OK: return "success";
+    case PACK3D_ERR_INVALID_ARG: return "invalid argument (null pointer, non-positive size or bad enum)";
+    case PACK3D_ERR_SHAPE: return "invalid shape (N != Z*Y*X, D not a multiple of 6, block < 1, or size limits)";
+    case PACK3D_ERR_WORKSPACE: return "workspace too small";
+    case PACK3D_ERR_UNSUPPORTED: return "dtype / head-dim / exclusion combination not built";
+    case PACK3D_ERR_HIP: return "HIP runtime or launch failure";
+    case PACK3D_ERR_COORDS: return "coordinate off the grid or duplicated";
+    default: return "unknown pack3d status";
+  }
+}
+
+int64_t pack3d_num_summaries(const pack3d_desc *desc) {
+  Geo g;
+  int rc = make_geo(desc, &g);
+  return rc ? rc : (int64_t)g.M;
+}
+
+int pack3d_geometry_layout(const pack3d_desc *desc, size_t *slot_offset, size_t *table_offset,
+                           size_t *bytes) {
+  Geo g;
+  int rc = make_geo(desc, &g);
+  if (rc) return rc;
+  if (slot_offset) *slot_offset = (size_t)g.slot_off;
+  if (table_offset) *table_offset = (size_t)g.table_off;
+  if (bytes) *bytes = geometry_bytes(g);
+  return PACK3D_OK;
+}
+
+int pack3d_geometry_bytes(const pack3d_desc *desc, size_t *bytes) {
+  if (!bytes) return PACK3D_ERR_INVALID_ARG;
+  return pack3d_geometry_layout(desc, nullptr, nullptr, bytes);
+}
+
+int pack3d_workspace_bytes(const pack3d_desc *desc, size_t *bytes) {
+  Geo g;
+  if (!bytes) return PACK3D_ERR_INVALID_ARG;
+  int rc = make_geo(desc, &g);
+  if (rc) return rc;
+  *bytes = geometry_bytes(g) + 2 * summary_bytes(g, desc->dtype);
+  return PACK3D_OK;
+}
+
+int pack3d_index_build(const pack3d_desc *desc, const int32_t *coords, void *geom,
+                       int32_t *nbr_out, int32_t *block_out, int32_t *rank_out, void *stream) {
+  Geo g;
+  int rc = make_geo(desc, &g);
+  if (rc) return rc;
+  if (!coords || !geom) return PACK3D_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = hip_status(launch_index(g, coords, geom, nbr_out, block_out, rank_out, s));
+  if (rc) return rc;
+  return validate_coords(desc, geom, s);
+}
+
+int pack3d_rope_coords(const pack3d_desc *desc, const int32_t *coords, const void *x,
+                       void *x_rot, void *stream) {
+  Geo g;
+  int rc = make_geo(desc, &g);
+  if (rc) return rc;
+  if (!coords || !x || !x_rot) return PACK3D_ERR_INVALID_ARG;
+  return hip_status(launch_rope(g, desc->dtype, coords, x, x_rot, static_cast<hipStream_t>(stream)));
+}
+
+int pack3d_block_summarize(const pack3d_desc *desc, const void *geom, const void *k,
+                           const void *v, void *k_sum, void *v_sum, void *stream) {
+  Geo g;
+  int rc = make_geo(desc, &g);
+  if (rc) return rc;
+  if (!geom || !k || !v || !k_sum || !v_sum) return PACK3D_ERR_INVALID_ARG;
+  return hip_status(launch_summarize(g, desc->dtype, geom, k, v, k_sum, v_sum,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int pack3d_local_attn(const pack3d_desc *desc, const void *geom, const void *q, const void *k,
+                      const void *v, void *o_local, void *stream) {
+  Geo g;
+  int rc = make_geo(desc, &g);
+  if (rc) return rc;
+  if (!geom || !q || !k || !v || !o_local) return PACK3D_ERR_INVALID_ARG;
+  bool ok = false;
+  hipError_t e = launch_local(g, desc->dtype, geom, q, k, v, nullptr, nullptr, o_local,
+                              static_cast<hipStream_t>(stream), &ok);
+  if (!ok) return PACK3D_ERR_UNSUPPORTED;
+  return hip_status(e);
+}
+
+int pack3d_global_attn(const pack3d_desc *desc, const void *geom, const int32_t *coords,
+                       const void *q, const void *k_sum, const void *v_sum, void *o_global,
+                       void *stream) {
+  Geo g;
+  int rc = make_geo(desc, &g);
+  if (rc) return rc;
+  if (!geom || !coords || !q || !k_sum || !v_sum || !o_global) return PACK3D_ERR_INVALID_ARG;
+  bool ok = false;
+  hipError_t e = launch_global(g, desc->dtype, geom, coords, q, k_sum, v_sum, o_global,
+                               static_cast<hipStream_t>(stream), &ok);
+  if (!ok) return PACK3D_ERR_UNSUPPORTED;
+  return hip_status(e);
+}
+
+int pack3d_mix(const pack3d_desc *desc, const void *gate, const void *o_local,
+               const void *o_global, void *o, void *stream) {
+  Geo g;
+  int rc = make_geo(desc, &g);
+  if (rc) return rc;
+  if (!gate || !o_local || !o_global || !o) return PACK3D_ERR_INVALID_ARG;
+  return hip_status(
+      launch_mix(g, desc->dtype, gate, o_local, o_global, o, static_cast<hipStream_t>(stream)));
+}
+
+int pack3d_forward(const pack3d_desc *desc, const int32_t *coords, const void *q, const void *k,
+                   const void *v, const void *gate, void *o, void *ws, size_t ws_bytes,
+                   void *stream, void *const *stage_events) {
+  Geo g;
+  int rc = make_geo(desc, &g);
+  if (rc) return rc;
+  if (!coords || !q || !k || !v || !gate || !o || !ws) return PACK3D_ERR_INVALID_ARG;
+  const size_t gbytes = geometry_bytes(g), sbytes = summary_bytes(g, desc->dtype);
+  if (ws_bytes < gbytes + 2 * sbytes) return PACK3D_ERR_WORKSPACE;
+  // shape support is decided before anything is enqueued
+  {
+    const bool mfma = desc->dtype == PACK3D_BF16 && desc->exclusion == PACK3D_EXCL_NONE &&
+                      (g.D == 48 || g.D == 96);
+    const bool valu = g.D == 6 || g.D == 12 || g.D == 24 || g.D == 48 || g.D == 96;
+    if (!mfma && !valu) return PACK3D_ERR_UNSUPPORTED;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *base = static_cast<char *>(ws);
+  void *geom = base;
+  void *ksum = base + gbytes;
+  void *vsum = base + gbytes + sbytes;
+  auto mark = [&](int idx) -> int {
+    if (!stage_events) return PACK3D_OK;
+    return hip_status(hipEventRecord(static_cast<hipEvent_t>(stage_events[idx]), s));
+  };
+  bool ok = true;
+  if ((rc = mark(0))) return rc;
+  if ((rc = hip_status(launch_index(g, coords, geom, nullptr, nullptr, nullptr, s)))) return rc;
+  if ((rc = mark(1))) return rc;
+  if ((rc = validate_coords(desc, geom, s))) return rc;
+  if ((rc = mark(2))) return rc;
+  if ((rc = hip_status(launch_summarize(g, desc->dtype, geom, k, v, ksum, vsum, s)))) return rc;
+  if ((rc = mark(3))) return rc;
+  if ((rc = mark(4))) return rc;
+  if ((rc = hip_status(launch_global(g, desc->dtype, geom, coords, q, ksum, vsum, o, s, &ok))))
+    return rc;
+  if (!ok) return PACK3D_ERR_UNSUPPORTED;
+  if ((rc = mark(5))) return rc;
+  if ((rc = mark(6))) return rc;
+  if ((rc = hip_status(launch_local(g, desc->dtype, geom, q, k, v, gate, o, o, s, &ok)))) return rc;
+  if (!ok) return PACK3D_ERR_UNSUPPORTED;
+  return mark(7);
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Device-side helpers shared by the PACK3D gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pack3d.h"
+
+namespace pk {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Problem geometry, derived once on the host from pack3d_desc and passed to
+// kernels by value.
+struct Geo {
+  int B, N, H, D;
+  int Z, Y, X;
+  int bz, by, bx;
+  int Mz, My, Mx;
+  int M;          // number of summaries
+  int P;          // rotation planes per axis = D / 6
+  int vol;        // bz * by * bx
+  float scale;    // softmax scale
+  float rope_base;
+  int excl;       // pack3d_exclusion
+  // geometry buffer offsets (bytes)
+  int64_t slot_off, table_off;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+__device__ __forceinline__ const int32_t *slot_map(const void *geom, const Geo &g) {
+  return reinterpret_cast<const int32_t *>(static_cast<const char *>(geom) + g.slot_off);
+}
+__device__ __forceinline__ const float2 *rope_table(const void *geom, const Geo &g) {
+  return reinterpret_cast<const float2 *>(static_cast<const char *>(geom) + g.table_off);
+}
+// (cos, sin) for axis a at coordinate c, plane p.
+__device__ __forceinline__ float2 rope_cs(const float2 *tab, const Geo &g, int a, int c, int p) {
+  int start = a == 0 ? 0 : (a == 1 ? g.Z : g.Z + g.Y);
+  return tab[(int64_t)(start + c) * g.P + p];
+}
+// The same value computed directly: angle c * base^(-2p/(D/3)) in double,
+// cos and sin in double, rounded to fp32.
+__device__ __forceinline__ float2 rope_cs_direct(float base, int D, int c, int p) {
+  double theta = pow((double)base, -2.0 * (double)p / (double)(D / 3));
+  double phi = (double)c * theta;
+  double s, co;
+  sincos(phi, &s, &co);
+  return make_float2((float)co, (float)s);
+}
+// Rotate the channel pair (x0, x1) by (cos, sin).
+__device__ __forceinline__ void rotate(float &x0, float &x1, float2 cs) {
+  float y0 = x0 * cs.x - x1 * cs.y;
+  float y1 = x0 * cs.y + x1 * cs.x;
+  x0 = y0;
+  x1 = y1;
+}
+
+__device__ __forceinline__ int site_of(const Geo &g, int z, int y, int x) {
+  return (z * g.Y + y) * g.X + x;
+}
+__device__ __forceinline__ int block_of(const Geo &g, int z, int y, int x) {
+  return ((z / g.bz) * g.My + (y / g.by)) * g.Mx + (x / g.bx);
+}
+// Whether summary m is withheld from a query at (z,y,x).
+__device__ __forceinline__ bool summary_excluded(const Geo &g, int z, int y, int x, int m) {
+  if (g.excl == PACK3D_EXCL_NONE) return false;
+  if (g.excl == PACK3D_EXCL_OWN_BLOCK) return m == block_of(g, z, y, x);
+  int mz = m / (g.My * g.Mx), my = (m / g.Mx) % g.My, mx = m % g.Mx;
+  int lz = max(z - 1, 0) / g.bz, hz = min(z + 1, g.Z - 1) / g.bz;
+  int ly = max(y - 1, 0) / g.by, hy = min(y + 1, g.Y - 1) / g.by;
+  int lx = max(x - 1, 0) / g.bx, hx = min(x + 1, g.X - 1) / g.bx;
+  return mz >= lz && mz <= hz && my >= ly && my <= hy && mx >= lx && mx <= hx;
+}
+
+}  // namespace pk

@@ -1,0 +1,267 @@
+// Query-to-summary attention on bf16 matrix cores (Geometry Matters in Packed
+// 3D Attention, project page Ch. 3, Contract 2; paper summary §3.5, §B.10).
+//
+// The global branch is a dense contraction -- every query against all M
+// summaries -- so it runs as a flash-style loop on v_mfma_f32_32x32x16_bf16
+// with an fp32 online softmax and never forms the token x summary score
+// matrix (paper summary §3.5).
+//
+// Layout of the work. A workgroup of 4 waves owns 128 consecutive tokens
+// (packed order) of one (batch, head); a wave owns 32 of them. Summary tiles
+// of 64 rows of k_sum and v_sum go through LDS (v_sum stored transposed).
+// Per 32-summary sub-tile a wave computes the TRANSPOSED scores
+// S^T = Ksum * Q~^T (32 summaries x 32 queries), so every lane holds 16
+// scores of ONE query and the running maximum, the rescale and the final
+// normalisation are lane-local. The k_sum rows are loaded in the order
+// r -> r with bits 2 and 3 swapped, which makes the score registers come out
+// exactly in the operand order of the next product O^T += Vsum^T * P^T: the
+// probabilities go from registers straight into the matrix core, no shuffle.
+//
+// Softmax details. Scores are in log2 units (the query is pre-multiplied by
+// scale*log2(e)). The running maximum m is folded into the matrix product by
+// seeding the accumulator with -m, so the scores arrive already shifted.
+// The maximum is only raised when a tile exceeds it by more than 8 (a factor
+// 256 in probability, harmless in fp32 sums and bf16 operands), which after
+// the first tile almost never happens; the result is the same softmax up to
+// rounding. For D = 48 the output tile has 16 spare rows; row 48 of the
+// transposed value tile is all ones so the matrix core also returns the
+// softmax denominator. Each query's arithmetic depends only on its own row
+// and the summaries, never on which tokens share its tile, so a repack of
+// the tokens permutes the output bit for bit.
+#include "launch.hpp"
+
+namespace pk {
+
+namespace {
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
+constexpr int kTS = 64;       // summaries per LDS tile
+constexpr int kWaves = 4;
+constexpr int kQW = 32;  // queries per wave
+
+__device__ __forceinline__ int swap23(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(256) void k_global_mfma(Geo g, const void *geom,
+                                                     const int32_t *__restrict__ coords,
+                                                     const bf16 *__restrict__ q,
+                                                     const bf16 *__restrict__ ks,
+                                                     const bf16 *__restrict__ vs,
+                                                     bf16 *__restrict__ out, int ntiles) {
+  constexpr int DA = D / 3;
+  constexpr int KD = D / 16;                // 16-deep steps of Ksum * Q~^T
+  constexpr bool ONES = (D % 32) != 0;      // spare output rows carry the denominator
+  constexpr int DT = (D + 31) / 32;         // 32-row tiles of O^T
+  constexpr int DPAD = DT * 32;
+  constexpr int KP = D + 8;                 // LDS pitch of a Ksum row (elements)
+  constexpr int VP = kTS + 8;               // LDS pitch of a Vsum^T row (elements)
+  static_assert(D % 16 == 0 && DA % 8 == 0, "D must be a multiple of 48");
+  __shared__ __attribute__((aligned(16))) bf16 sK[kTS * KP];
+  __shared__ __attribute__((aligned(16))) bf16 sVt[DPAD * VP];
+
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = w % ntiles;
+  const int bh = w / ntiles;
+  const int h = bh % g.H, b = bh / g.H;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int hi = lane >> 5;  // which half of the wave
+  const int qi = tile * (kWaves * kQW) + wv * kQW + (lane & 31);
+  const bool active = qi < g.N;
+  // a token whose coordinate is off the grid takes no part: zero query,
+  // zero output row (only reachable without PACK3D_VALIDATE)
+  bool cok = false;
+  const int64_t sbase = ((int64_t)b * g.H + h) * g.M * D;
+
+  // constant spare rows of the transposed value tile (never overwritten)
+  for (int e = threadIdx.x; e < (DPAD - D) * kTS; e += 256) {
+    const int r = D + e / kTS, c = e % kTS;
+    sVt[r * VP + c] = (bf16)((ONES && r == D) ? 1.0f : 0.0f);
+  }
+
+  // Query fragments: lane holds channels 16c + 8*hi .. +7 of its query,
+  // rotated at the token's own coordinate, scaled, rounded to bf16.
+  bf16x8 qf[KD];
+  {
+    const float2 *tab = rope_table(geom, g);
+    const float qscale = g.scale * kLog2e;
+    int c3[3] = {0, 0, 0};
+    if (active) {
+      c3[0] = coords[3 * (int64_t)qi];
+      c3[1] = coords[3 * (int64_t)qi + 1];
+      c3[2] = coords[3 * (int64_t)qi + 2];
+      cok = c3[0] >= 0 && c3[1] >= 0 && c3[2] >= 0 && c3[0] < g.Z && c3[1] < g.Y && c3[2] < g.X;
+      if (!cok) c3[0] = c3[1] = c3[2] = 0;
+    }
+    const int64_t off = (((int64_t)b * g.N + qi) * g.H + h) * D;
+#pragma unroll
+    for (int c = 0; c < KD; c++) {
+      const int d0 = 16 * c + 8 * hi;
+      const int a = d0 / DA, p0 = (d0 % DA) / 2;
+      float x[8];
+      if (cok) {
+        const bf16x8 raw = *reinterpret_cast<const bf16x8 *>(q + off + d0);
+#pragma unroll
+        for (int e = 0; e < 8; e++) x[e] = (float)raw[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; e++) x[e] = 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        rotate(x[2 * u], x[2 * u + 1], rope_cs(tab, g, a, c3[a], p0 + u));
+        qf[c][2 * u] = (bf16)(x[2 * u] * qscale);
+        qf[c][2 * u + 1] = (bf16)(x[2 * u + 1] * qscale);
+      }
+    }
+  }
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; t++)
+#pragma unroll
+    for (int j = 0; j < 16; j++) acc[t][j] = 0.f;
+  f32x16 cneg;  // -m in every register: seeds the score accumulator
+#pragma unroll
+  for (int j = 0; j < 16; j++) cneg[j] = 0.f;
+  float m = 0.f;       // running maximum (log2 units); valid once started
+  bool started = false;
+  float lsum = 0.f;    // denominator partial when no spare row carries it
+
+  const int rowK = swap23(lane & 31);
+
+  for (int m0 = 0; m0 < g.M; m0 += kTS) {
+    const int nm = min(kTS, g.M - m0);
+    __syncthreads();
+    // stage Ksum rows [m0, m0+64) and Vsum^T columns, zero past M
+    for (int e = threadIdx.x; e < kTS * (D / 8); e += 256) {
+      const int r = e / (D / 8), ch = e % (D / 8);
+      bf16x8 kv, vv;
+      if (r < nm) {
+        kv = *reinterpret_cast<const bf16x8 *>(ks + sbase + (int64_t)(m0 + r) * D + 8 * ch);
+        vv = *reinterpret_cast<const bf16x8 *>(vs + sbase + (int64_t)(m0 + r) * D + 8 * ch);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; u++) kv[u] = vv[u] = (bf16)0.0f;
+      }
+      *reinterpret_cast<bf16x8 *>(&sK[r * KP + 8 * ch]) = kv;
+#pragma unroll
+      for (int u = 0; u < 8; u++) sVt[(8 * ch + u) * VP + r] = vv[u];
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int sub = 0; sub < kTS / 32; sub++) {
+      if (m0 + 32 * sub >= g.M) break;
+      // S^T - m for this 32-summary sub-tile
+      f32x16 s = cneg;
+#pragma unroll
+      for (int c = 0; c < KD; c++) {
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8 *>(&sK[(32 * sub + rowK) * KP + 16 * c + 8 * hi]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s, 0, 0, 0);
+      }
+      if (m0 + 32 * sub + 32 > g.M) {  // past-the-end summaries take no part
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+          const int r = (j >> 2) * 8 + hi * 4 + (j & 3);
+          if (m0 + 32 * sub + swap23(r) >= g.M) s[j] = -INFINITY;
+        }
+      }
+      float tmax = s[0];
+#pragma unroll
+      for (int j = 1; j < 16; j++) tmax = fmaxf(tmax, s[j]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      // raise the maximum only when needed (always on the first sub-tile)
+      const bool need = !started || tmax > kTau;
+      if (__ballot(need)) {
+        const float shift = need ? tmax : 0.f;
+        const float alpha = started ? __builtin_amdgcn_exp2f(-shift) : 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; j++) s[j] -= shift;
+#pragma unroll
+        for (int t = 0; t < DT; t++)
+#pragma unroll
+          for (int j = 0; j < 16; j++) acc[t][j] *= alpha;
+        lsum *= alpha;
+        m = started ? m + shift : shift;
+        started = true;
+#pragma unroll
+        for (int j = 0; j < 16; j++) cneg[j] = -m;
+      }
+      bf16x8 pf[2];
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        const float p = __builtin_amdgcn_exp2f(s[j]);
+        if (!ONES) lsum += p;
+        pf[j >> 3][j & 7] = (bf16)p;
+      }
+#pragma unroll
+      for (int t = 0; t < DT; t++) {
+#pragma unroll
+        for (int c2 = 0; c2 < 2; c2++) {
+          const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(
+              &sVt[(32 * t + (lane & 31)) * VP + 32 * sub + 16 * c2 + 8 * hi]);
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c2], acc[t], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // denominator: spare row D (lanes 0..31, register 8 of the last tile), or
+  // the two half-wave partial sums
+  float den;
+  if (ONES)
+    den = __shfl(acc[DT - 1][8], lane & 31);
+  else
+    den = lsum + __shfl_xor(lsum, 32);
+  const float inv = (den > 0.f && cok) ? 1.0f / den : 0.f;
+  if (!active) return;
+  bf16 *orow = out + (((int64_t)b * g.N + qi) * g.H + h) * D;
+#pragma unroll
+  for (int t = 0; t < DT; t++) {
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) {
+      const int d = 32 * t + 8 * jj + 4 * hi;
+      if (d < D) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 o4;
+#pragma unroll
+        for (int u = 0; u < 4; u++) o4[u] = (bf16)(acc[t][4 * jj + u] * inv);
+        *reinterpret_cast<bf16x4 *>(orow + d) = o4;
+      }
+    }
+  }
+}
+
+hipError_t launch_global_valu(const Geo &g, int dtype, const void *geom, const int32_t *coords,
+                              const void *q, const void *ks, const void *vs, void *out,
+                              hipStream_t s, bool *supported);
+
+namespace {
+template <int D>
+hipError_t run_global_mfma(const Geo &g, const void *geom, const int32_t *coords, const void *q,
+                           const void *ks, const void *vs, void *out, hipStream_t s) {
+  const int ntiles = (g.N + kWaves * kQW - 1) / (kWaves * kQW);
+  const int64_t nwg = (int64_t)ntiles * g.B * g.H;
+  hipLaunchKernelGGL((k_global_mfma<D>), dim3((unsigned)nwg), dim3(256), 0, s, g, geom, coords,
+                     static_cast<const bf16 *>(q), static_cast<const bf16 *>(ks),
+                     static_cast<const bf16 *>(vs), static_cast<bf16 *>(out), ntiles);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_global(const Geo &g, int dtype, const void *geom, const int32_t *coords,
+                         const void *q, const void *ks, const void *vs, void *out, hipStream_t s,
+                         bool *supported) {
+  if (dtype == PACK3D_BF16 && g.excl == PACK3D_EXCL_NONE) {
+    *supported = true;
+    if (g.D == 48) return run_global_mfma<48>(g, geom, coords, q, ks, vs, out, s);
+    if (g.D == 96) return run_global_mfma<96>(g, geom, coords, q, ks, vs, out, s);
+  }
+  return launch_global_valu(g, dtype, geom, coords, q, ks, vs, out, s, supported);
+}
+
+}  // namespace pk

@@ -1,0 +1,74 @@
+// Geometry metadata: slot map, coordinate checks, RoPE table and the optional
+// neighbour / block / within-block-slot exports. Tokens are indexed by their
+// grid coordinate, never by memory order (Geometry Matters in Packed 3D
+// Attention, paper summary §B.1; project page Ch. 4, Prop. 2).
+#include "launch.hpp"
+
+namespace pk {
+
+// Clears the status word and slot map and fills the RoPE table.
+__global__ void k_geom_init(Geo g, int32_t *status, int32_t *slot, float2 *tab) {
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t S = (int64_t)g.Z * g.Y * g.X;
+  if (t == 0) status[0] = 0;
+  if (t < S) slot[t] = -1;
+  int64_t T = (int64_t)(g.Z + g.Y + g.X) * g.P;
+  if (t < T) {
+    int row = (int)(t / g.P), p = (int)(t % g.P);
+    int c = row < g.Z ? row : (row < g.Z + g.Y ? row - g.Z : row - g.Z - g.Y);
+    tab[t] = rope_cs_direct(g.rope_base, g.D, c, p);
+  }
+}
+
+// slot[site(c_i)] = i; bit 0 of the status word marks an off-grid
+// coordinate, bit 1 a site claimed twice (the first claim stays).
+__global__ void k_geom_scatter(Geo g, const int32_t *coords, int32_t *status, int32_t *slot) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= g.N) return;
+  int z = coords[3 * (int64_t)i], y = coords[3 * (int64_t)i + 1], x = coords[3 * (int64_t)i + 2];
+  if (z < 0 || y < 0 || x < 0 || z >= g.Z || y >= g.Y || x >= g.X) {
+    atomicOr(status, 1);
+    return;
+  }
+  int old = atomicCAS(&slot[site_of(g, z, y, x)], -1, i);
+  if (old != -1) atomicOr(status, 2);
+}
+
+__global__ void k_geom_export(Geo g, const int32_t *coords, const int32_t *slot, int32_t *nbr,
+                              int32_t *blk, int32_t *rank) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= g.N) return;
+  int z = coords[3 * (int64_t)i], y = coords[3 * (int64_t)i + 1], x = coords[3 * (int64_t)i + 2];
+  bool in = !(z < 0 || y < 0 || x < 0 || z >= g.Z || y >= g.Y || x >= g.X);
+  if (blk) blk[i] = in ? block_of(g, z, y, x) : -1;
+  if (rank) rank[i] = in ? ((z % g.bz) * g.by + (y % g.by)) * g.bx + (x % g.bx) : -1;
+  if (nbr) {
+    for (int k = 0; k < 27; k++) {
+      int zz = z + k / 9 - 1, yy = y + (k / 3) % 3 - 1, xx = x + k % 3 - 1;
+      bool ok = in && zz >= 0 && yy >= 0 && xx >= 0 && zz < g.Z && yy < g.Y && xx < g.X;
+      nbr[(int64_t)i * 27 + k] = ok ? slot[site_of(g, zz, yy, xx)] : -1;
+    }
+  }
+}
+
+hipError_t launch_index(const Geo &g, const int32_t *coords, void *geom, int32_t *nbr,
+                        int32_t *blk, int32_t *rank, hipStream_t s) {
+  char *base = static_cast<char *>(geom);
+  int32_t *status = reinterpret_cast<int32_t *>(base);
+  int32_t *slot = reinterpret_cast<int32_t *>(base + g.slot_off);
+  float2 *tab = reinterpret_cast<float2 *>(base + g.table_off);
+  int64_t S = (int64_t)g.Z * g.Y * g.X;
+  int64_t T = (int64_t)(g.Z + g.Y + g.X) * g.P;
+  int64_t n = S > T ? S : T;
+  const int TB = 256;
+  hipLaunchKernelGGL(k_geom_init, dim3((unsigned)((n + TB - 1) / TB)), dim3(TB), 0, s, g, status,
+                     slot, tab);
+  hipLaunchKernelGGL(k_geom_scatter, dim3((unsigned)((g.N + TB - 1) / TB)), dim3(TB), 0, s, g,
+                     coords, status, slot);
+  if (nbr || blk || rank)
+    hipLaunchKernelGGL(k_geom_export, dim3((unsigned)((g.N + TB - 1) / TB)), dim3(TB), 0, s, g,
+                       coords, slot, nbr, blk, rank);
+  return hipGetLastError();
+}
+
+}  // namespace pk

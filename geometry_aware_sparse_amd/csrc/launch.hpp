@@ -1,0 +1,37 @@
+// Host-side launchers of the PACK3D kernels (one per kernel family); each
+// returns the hipError_t of its launch. Shapes are validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+
+namespace pk {
+
+hipError_t launch_index(const Geo &g, const int32_t *coords, void *geom, int32_t *nbr,
+                        int32_t *blk, int32_t *rank, hipStream_t s);
+hipError_t launch_rope(const Geo &g, int dtype, const int32_t *coords, const void *x, void *y,
+                       hipStream_t s);
+hipError_t launch_summarize(const Geo &g, int dtype, const void *geom, const void *k,
+                            const void *v, void *ks, void *vs, hipStream_t s);
+// gate / oglob may be null (plain local output); when set the kernel writes
+// (1-g)*O_local + g*O_global. oglob may equal out.
+hipError_t launch_local(const Geo &g, int dtype, const void *geom, const void *q, const void *k,
+                        const void *v, const void *gate, const void *oglob, void *out,
+                        hipStream_t s, bool *supported);
+hipError_t launch_global(const Geo &g, int dtype, const void *geom, const int32_t *coords,
+                         const void *q, const void *ks, const void *vs, void *out, hipStream_t s,
+                         bool *supported);
+hipError_t launch_mix(const Geo &g, int dtype, const void *gate, const void *ol, const void *og,
+                      void *o, hipStream_t s);
+
+// Work-item index of this workgroup such that consecutive work items land on
+// the same XCD: the hardware deals workgroups round-robin over the 8 XCDs, so
+// XCD x receives every 8th workgroup; give it one contiguous range instead.
+__device__ __forceinline__ int xcd_remap(int wg, int nwg) {
+  const int NX = 8;
+  int x = wg % NX, idx = wg / NX;
+  int base = x * (nwg / NX) + min(x, nwg % NX);
+  return base + idx;
+}
+
+}  // namespace pk

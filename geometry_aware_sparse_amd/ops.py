@@ -1,0 +1,185 @@
+"""Torch-tensor front end of the C entry points (marshalling only)."""
+import ctypes as C
+
+import torch
+
+from ._lib import (PACK3D_BF16, PACK3D_F32, PACK3D_NUM_STAGES, PACK3D_VALIDATE, Desc,
+                   Pack3DError, library)
+
+_DTYPES = {PACK3D_F32: torch.float32, PACK3D_BF16: torch.bfloat16}
+
+
+def make_desc(B, N, H, D, grid, block, dtype=PACK3D_BF16, rope_base=10000.0, scale=0.0,
+              exclusion=0, validate=False):
+    if isinstance(dtype, torch.dtype):
+        dtype = {torch.float32: PACK3D_F32, torch.bfloat16: PACK3D_BF16}[dtype]
+    d = Desc()
+    d.B, d.N, d.H, d.D = int(B), int(N), int(H), int(D)
+    d.grid[:] = [int(x) for x in grid]
+    d.block[:] = [int(x) for x in block]
+    d.rope_base = float(rope_base)
+    d.scale = float(scale)
+    d.dtype = int(dtype)
+    d.exclusion = int(exclusion)
+    d.flags = PACK3D_VALIDATE if validate else 0
+    return d
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise Pack3DError(rc, what)
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _need(t, name, desc, shape, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    want = dtype if dtype is not None else _DTYPES[desc.dtype]
+    if t.dtype != want:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {want}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _bnhd(desc):
+    return (desc.B, desc.N, desc.H, desc.D)
+
+
+def pack3d_num_summaries(desc):
+    m = library().pack3d_num_summaries(C.byref(desc))
+    _check(0 if m >= 0 else int(m), "pack3d_num_summaries")
+    return int(m)
+
+
+def pack3d_geometry_layout(desc):
+    so, to, nb = C.c_size_t(), C.c_size_t(), C.c_size_t()
+    _check(library().pack3d_geometry_layout(C.byref(desc), C.byref(so), C.byref(to), C.byref(nb)),
+           "pack3d_geometry_layout")
+    return so.value, to.value, nb.value
+
+
+def pack3d_geometry_bytes(desc):
+    n = C.c_size_t()
+    _check(library().pack3d_geometry_bytes(C.byref(desc), C.byref(n)), "pack3d_geometry_bytes")
+    return n.value
+
+
+def pack3d_workspace_bytes(desc):
+    n = C.c_size_t()
+    _check(library().pack3d_workspace_bytes(C.byref(desc), C.byref(n)), "pack3d_workspace_bytes")
+    return n.value
+
+
+def slot_map_view(desc, geom):
+    """The int32 slot map inside a geometry buffer, as a tensor view."""
+    so, _, _ = pack3d_geometry_layout(desc)
+    S = desc.grid[0] * desc.grid[1] * desc.grid[2]
+    return geom[so:so + 4 * S].view(torch.int32)
+
+
+def pack3d_index_build(desc, coords, geom=None, neighbours=False, blocks=False, ranks=False):
+    """Returns (geom, nbr, block, rank); the last three are None unless asked."""
+    _need(coords, "coords", desc, (desc.N, 3), torch.int32)
+    nb = pack3d_geometry_bytes(desc)
+    if geom is None:
+        geom = torch.empty(nb, dtype=torch.uint8, device=coords.device)
+    elif geom.numel() * geom.element_size() < nb or not geom.is_cuda:
+        raise ValueError("geometry buffer too small or not on the GPU")
+    dev = coords.device
+    nbr = torch.empty((desc.N, 27), dtype=torch.int32, device=dev) if neighbours else None
+    blk = torch.empty(desc.N, dtype=torch.int32, device=dev) if blocks else None
+    rank = torch.empty(desc.N, dtype=torch.int32, device=dev) if ranks else None
+    _check(library().pack3d_index_build(C.byref(desc), _ptr(coords), _ptr(geom), _ptr(nbr),
+                                        _ptr(blk), _ptr(rank), _stream()), "pack3d_index_build")
+    return geom, nbr, blk, rank
+
+
+def pack3d_rope_coords(desc, coords, x, out=None):
+    _need(coords, "coords", desc, (desc.N, 3), torch.int32)
+    _need(x, "x", desc, _bnhd(desc))
+    out = torch.empty_like(x) if out is None else out
+    _need(out, "out", desc, _bnhd(desc))
+    _check(library().pack3d_rope_coords(C.byref(desc), _ptr(coords), _ptr(x), _ptr(out),
+                                        _stream()), "pack3d_rope_coords")
+    return out
+
+
+def pack3d_block_summarize(desc, geom, k, v):
+    _need(k, "k", desc, _bnhd(desc))
+    _need(v, "v", desc, _bnhd(desc))
+    M = pack3d_num_summaries(desc)
+    ks = torch.empty((desc.B, desc.H, M, desc.D), dtype=k.dtype, device=k.device)
+    vs = torch.empty_like(ks)
+    _check(library().pack3d_block_summarize(C.byref(desc), _ptr(geom), _ptr(k), _ptr(v), _ptr(ks),
+                                            _ptr(vs), _stream()), "pack3d_block_summarize")
+    return ks, vs
+
+
+def pack3d_local_attn(desc, geom, q, k, v, out=None):
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, desc, _bnhd(desc))
+    out = torch.empty_like(q) if out is None else out
+    _need(out, "out", desc, _bnhd(desc))
+    _check(library().pack3d_local_attn(C.byref(desc), _ptr(geom), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(out), _stream()), "pack3d_local_attn")
+    return out
+
+
+def pack3d_global_attn(desc, geom, coords, q, ks, vs, out=None):
+    _need(coords, "coords", desc, (desc.N, 3), torch.int32)
+    _need(q, "q", desc, _bnhd(desc))
+    M = pack3d_num_summaries(desc)
+    _need(ks, "k_sum", desc, (desc.B, desc.H, M, desc.D))
+    _need(vs, "v_sum", desc, (desc.B, desc.H, M, desc.D))
+    out = torch.empty_like(q) if out is None else out
+    _need(out, "out", desc, _bnhd(desc))
+    _check(library().pack3d_global_attn(C.byref(desc), _ptr(geom), _ptr(coords), _ptr(q),
+                                        _ptr(ks), _ptr(vs), _ptr(out), _stream()),
+           "pack3d_global_attn")
+    return out
+
+
+def pack3d_mix(desc, gate, o_local, o_global, out=None):
+    _need(gate, "gate", desc, (desc.B, desc.N, desc.H))
+    _need(o_local, "o_local", desc, _bnhd(desc))
+    _need(o_global, "o_global", desc, _bnhd(desc))
+    out = torch.empty_like(o_local) if out is None else out
+    _need(out, "out", desc, _bnhd(desc))
+    _check(library().pack3d_mix(C.byref(desc), _ptr(gate), _ptr(o_local), _ptr(o_global),
+                                _ptr(out), _stream()), "pack3d_mix")
+    return out
+
+
+def pack3d_forward(desc, coords, q, k, v, gate, out=None, workspace=None, stage_events=None):
+    """The whole operator. stage_events: None or a list of
+    2*PACK3D_NUM_STAGES torch.cuda.Event(enable_timing=True) objects."""
+    _need(coords, "coords", desc, (desc.N, 3), torch.int32)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, desc, _bnhd(desc))
+    _need(gate, "gate", desc, (desc.B, desc.N, desc.H))
+    out = torch.empty_like(q) if out is None else out
+    _need(out, "out", desc, _bnhd(desc))
+    nb = pack3d_workspace_bytes(desc)
+    if workspace is None:
+        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != 2 * PACK3D_NUM_STAGES:
+            raise ValueError("stage_events needs 2*PACK3D_NUM_STAGES events")
+        ev = (C.c_void_p * len(stage_events))(*[C.c_void_p(e.cuda_event) for e in stage_events])
+    _check(library().pack3d_forward(C.byref(desc), _ptr(coords), _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(gate), _ptr(out), _ptr(workspace), C.c_size_t(ws_bytes),
+                                    _stream(), ev), "pack3d_forward")
+    return out

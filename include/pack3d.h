@@ -1,0 +1,204 @@
+/*
+ * pack3d.h -- C ABI of the PACK3D local-global attention forward on gfx950.
+ *
+ * The operator (Geometry Matters in Packed 3D Attention; "project page" =
+ * the Pack3D site, "paper summary" = the arXiv 2610.38694 abstract page):
+ * tokens of a 3D grid are stored in any memory order (raster, Morton,
+ * block-contiguous, random) and each carries its integer grid coordinate
+ * (project page Ch. 1; paper summary §3.1, §B.1). Queries and keys are
+ * rotated with axial RoPE at those coordinates, never at the memory index
+ * (project page Ch. 3, Contract 3). Each query attends exactly to its 3x3x3
+ * coordinate neighbourhood (Contract 1) and to every block summary, built by
+ * rotating keys first and mean-pooling them per contiguous 3D block
+ * (Contract 2 and "Rotate first, then pool"; paper summary §3.2, §B.5). A
+ * tokenwise gate mixes the two branches (paper summary §3.3).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers named q, k, v, gate, o, x, k_sum, v_sum, geom, coords, ws and
+ *    the *_out arrays are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or retains device memory.
+ *  - Layouts (row-major, C order):
+ *      q, k, v, o, o_local, o_global, x : [B, N, H, D] in packed memory order
+ *      gate                             : [B, N, H] (gate logits G)
+ *      coords                           : int32 [N, 3] = (z, y, x) of the
+ *                                         token stored at each position; one
+ *                                         packing shared by the whole batch
+ *      k_sum, v_sum                     : [B, H, M, D], summaries in block-id
+ *                                         order m = (mz*My + my)*Mx + mx
+ *    Element type of q/k/v/gate/o/x/k_sum/v_sum is desc->dtype.
+ *  - stream is a hipStream_t passed as void* (NULL = default stream). Every
+ *    call only enqueues work on it and returns; results are ready when the
+ *    stream reaches that point. Calls are reentrant: the library keeps no
+ *    mutable global state.
+ *  - Return value: PACK3D_OK or a negative pack3d_status. Argument checks run
+ *    on the host before anything is enqueued; nothing is launched when they
+ *    fail. Coordinate errors are detected on the device: kernels never read
+ *    out of bounds (an off-grid or empty site simply takes no part), and the
+ *    error is reported to the host only when desc->flags has PACK3D_VALIDATE
+ *    (the call then synchronises the stream).
+ *
+ * Readings taken where the pages are silent (their formulas did not survive):
+ * RoPE channels are three contiguous chunks of D/3 for z, y, x; plane p of a
+ * chunk is the channel pair (2p, 2p+1) turned by c_axis * base^(-2p/(D/3));
+ * the neighbourhood is Chebyshev radius 1 including the query, clipped at the
+ * grid edge; the softmax scale defaults to 1/sqrt(D) in both branches;
+ * summaries are arithmetic means over the members present (blocks tile the
+ * grid from coordinate 0; edge blocks may be partial); every query attends to
+ * all M summaries by default; the gate is g = sigmoid(G) per token and head
+ * and O = (1-g)*O_local + g*O_global.
+ */
+#ifndef PACK3D_H
+#define PACK3D_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PACK3D_ABI_VERSION 1
+
+typedef enum pack3d_status {
+  PACK3D_OK = 0,
+  PACK3D_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad enum */
+  PACK3D_ERR_SHAPE = -2,       /* N != Z*Y*X, D % 6 != 0, block < 1, size overflow */
+  PACK3D_ERR_WORKSPACE = -3,   /* workspace smaller than pack3d_workspace_bytes */
+  PACK3D_ERR_UNSUPPORTED = -4, /* dtype / D / exclusion combination not built */
+  PACK3D_ERR_HIP = -5,         /* a HIP launch or runtime call failed */
+  PACK3D_ERR_COORDS = -6       /* coordinate off the grid or duplicated (VALIDATE only) */
+} pack3d_status;
+
+typedef enum pack3d_dtype { PACK3D_F32 = 0, PACK3D_BF16 = 1 } pack3d_dtype;
+
+/* Which summaries a query may not attend to. The pages say both that the
+ * summaries carry only the nonlocal context (paper summary §3.2) and that
+ * every query attends to all of them (project page Ch. 3, Contract 2; the
+ * N^2/v interaction count of paper summary §B.10); NONE follows the latter. */
+typedef enum pack3d_exclusion {
+  PACK3D_EXCL_NONE = 0,                /* attend to all M summaries (default) */
+  PACK3D_EXCL_OWN_BLOCK = 1,           /* skip the block holding the query */
+  PACK3D_EXCL_NEIGHBOURHOOD_BLOCKS = 2 /* skip every block meeting the clipped 3x3x3 */
+} pack3d_exclusion;
+
+#define PACK3D_VALIDATE 0x1u /* synchronise and report coordinate errors */
+
+typedef struct pack3d_desc {
+  int32_t B, N, H, D;  /* batch, tokens, heads, head dim (D % 6 == 0)         */
+  int32_t grid[3];     /* Z, Y, X; every grid site holds one token: N == Z*Y*X */
+  int32_t block[3];    /* bz, by, bx >= 1: summary block shape                  */
+  float rope_base;     /* RoPE base (10000 in the measured workloads); > 0      */
+  float scale;         /* softmax scale; <= 0 selects 1/sqrt(D)                  */
+  int32_t dtype;       /* pack3d_dtype of every float tensor                     */
+  int32_t exclusion;   /* pack3d_exclusion                                       */
+  uint32_t flags;      /* PACK3D_VALIDATE                                        */
+} pack3d_desc;
+
+/* Library ABI version (PACK3D_ABI_VERSION). */
+int pack3d_abi_version(void);
+
+/* Human-readable text for a pack3d_status; never NULL. */
+const char *pack3d_strerror(int status);
+
+/* Number of summaries M = ceil(Z/bz)*ceil(Y/by)*ceil(X/bx) for desc, or a
+ * negative pack3d_status when desc is invalid. */
+int64_t pack3d_num_summaries(const pack3d_desc *desc);
+
+/* ---------------------------------------------------------------------------
+ * Geometry metadata (what a repack must carry with each token: coordinate,
+ * neighbourhood edges, block membership and within-block slot; project page
+ * Ch. 4, Prop. 2). It lives in one caller buffer `geom` of
+ * pack3d_geometry_bytes() bytes, 256-byte aligned, laid out as:
+ *   [0, 256)               int32 status word (bit 0: coordinate off the grid,
+ *                          bit 1: coordinate duplicated), then padding
+ *   [slot_offset, ...)     int32 slot map [Z*Y*X]: slot[(z*Y + y)*X + x] =
+ *                          memory position of the token at (z,y,x), -1 if none
+ *   [table_offset, ...)    float32 RoPE table [(Z+Y+X) * (D/6)][2]: entry
+ *                          (axis_start + c)*(D/6) + p holds (cos, sin) of
+ *                          c * base^(-2p/(D/3)), evaluated in double and
+ *                          rounded; axis_start is 0, Z, Z+Y for z, y, x
+ * Offsets are reported by pack3d_geometry_layout. */
+int pack3d_geometry_bytes(const pack3d_desc *desc, size_t *bytes);
+int pack3d_geometry_layout(const pack3d_desc *desc, size_t *slot_offset, size_t *table_offset,
+                           size_t *bytes);
+
+/* Builds the geometry metadata from the coordinates: clears the status word
+ * and slot map, scatters slot[site(c_i)] = i, flags off-grid or repeated
+ * coordinates and fills the RoPE table. Optional outputs (device, may be
+ * NULL), all int32 over memory positions i:
+ *   nbr_out   [N, 27]: memory position of the neighbour at offset
+ *             (k/9 - 1, (k/3)%3 - 1, k%3 - 1), -1 off the grid or empty
+ *   block_out [N]: block id floor(z/bz)*My*Mx + floor(y/by)*Mx + floor(x/bx)
+ *   rank_out  [N]: within-block slot ((z%bz)*by + y%by)*bx + x%bx
+ * Index results are exact integers. Under PACK3D_VALIDATE returns
+ * PACK3D_ERR_COORDS when the status word is non-zero. */
+int pack3d_index_build(const pack3d_desc *desc, const int32_t *coords, void *geom,
+                       int32_t *nbr_out, int32_t *block_out, int32_t *rank_out, void *stream);
+
+/* Axial RoPE at grid coordinates, materialised (project page Ch. 3,
+ * Contract 3; paper summary §B.2): x_rot = R(c_i) x_i for every batch, token
+ * and head; x_rot may equal x (in place) but may not partially overlap it.
+ * Computed in fp32 from cos/sin evaluated in double; bf16 output is rounded
+ * to nearest even. The other entry points take UNROTATED q and k and rotate
+ * them as they load them; this call exists for tests and for callers that
+ * want rotated tensors. */
+int pack3d_rope_coords(const pack3d_desc *desc, const int32_t *coords, const void *x,
+                       void *x_rot, void *stream);
+
+/* Rotate-then-pool block summaries (project page Ch. 3, "Rotate first, then
+ * pool"; paper summary §3.2, §B.5): k_sum[b,h,m] = mean over the members j of
+ * block m of R(c_j) k[b,j,h]; v_sum[b,h,m] = mean of v[b,j,h]. Members are
+ * summed in fp32 in within-block-slot order, so the result does not depend on
+ * the packing. geom must hold metadata built by pack3d_index_build for the
+ * same desc. Blocks with no member present get zeros. */
+int pack3d_block_summarize(const pack3d_desc *desc, const void *geom, const void *k,
+                           const void *v, void *k_sum, void *v_sum, void *stream);
+
+/* Exact local attention (project page Ch. 3, Contract 1; paper summary §3.2,
+ * §3.5): for each token i, head h, softmax over the valid tokens j of the
+ * 3x3x3 coordinate neighbourhood of scale * <R(c_i) q_i, R(c_j) k_j>, then
+ * the weighted sum of the unrotated v_j. fp32 softmax and accumulation;
+ * neighbours are visited in the fixed offset order. o_local may not alias
+ * q, k or v. */
+int pack3d_local_attn(const pack3d_desc *desc, const void *geom, const void *q, const void *k,
+                      const void *v, void *o_local, void *stream);
+
+/* Query-to-summary attention (project page Ch. 3, Contract 2; paper summary
+ * §3.5, §B.10): for each token i, head h, softmax over the summaries m (all
+ * of them, or those desc->exclusion leaves) of
+ * scale * <R(c_i) q_i, k_sum[b,h,m]>, then the weighted sum of v_sum[b,h,m];
+ * zero when every summary is excluded. bf16 with D in {48, 96} and no
+ * exclusion runs on bf16 matrix cores with an fp32 online softmax; every
+ * other case runs an fp32 vector kernel. o_global may not alias q. */
+int pack3d_global_attn(const pack3d_desc *desc, const void *geom, const int32_t *coords,
+                       const void *q, const void *k_sum, const void *v_sum, void *o_global,
+                       void *stream);
+
+/* Tokenwise mix (paper summary §3.3): g = 1/(1+exp(-gate[b,i,h])),
+ * o = (1-g)*o_local + g*o_global, elementwise in fp32. o may alias o_local
+ * or o_global exactly. */
+int pack3d_mix(const pack3d_desc *desc, const void *gate, const void *o_local,
+               const void *o_global, void *o, void *stream);
+
+/* Workspace needed by pack3d_forward: the geometry metadata followed by the
+ * two summary tensors, each 256-byte aligned. */
+int pack3d_workspace_bytes(const pack3d_desc *desc, size_t *bytes);
+
+/* The whole forward, stream-ordered: index build, summaries, global branch
+ * (written into o), then local branch fused with the mix (reads o, writes
+ * o). Equivalent to the staged calls above; o must not alias q, k, v or
+ * gate. ws: device workspace of at least pack3d_workspace_bytes bytes
+ * (ws_bytes says how large it is). stage_events: NULL, or an array of
+ * 2*PACK3D_NUM_STAGES hipEvent_t (as void*) that are recorded on stream
+ * before and after each stage (index, summarize, global, local+mix), for
+ * timing. */
+#define PACK3D_NUM_STAGES 4
+int pack3d_forward(const pack3d_desc *desc, const int32_t *coords, const void *q, const void *k,
+                   const void *v, const void *gate, void *o, void *ws, size_t ws_bytes,
+                   void *stream, void *const *stage_events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PACK3D_H */
