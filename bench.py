@@ -1,0 +1,212 @@
+"""PACK3D forward benchmark on one MI355X.
+
+A step is one pack3d_forward over one batch of seeded synthetic input that is
+already resident in HBM: index build, rotate-then-pool summaries, the
+query-to-summary branch on bf16 matrix cores, and the local branch fused
+with the gated mix. The default workload is the 65,536-token volume (grid
+32 x 32 x 64, batch 1, 8 heads, head dim 48, 2x2x2 blocks -> 8,192
+summaries, bf16, block-contiguous packing).
+
+Prints one JSON line: throughput in tokens/s, the roofline of the dominant
+kernel (the global branch: algorithmic flops per launch over its average
+launch time, timed with HIP events recorded by pack3d_forward on the launch
+stream), per-stage times and HBM-roofline fractions, and the CPU oracle
+timed on a bounded sample of the same workload on this host's cores.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+  python bench.py --copy-calibration    # plain device copy, for counter scaling
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+METRIC = "PACK3D fwd tokens/sec at 65,536 tokens, 1 MI355X; % of HBM/MFMA roofline"
+STAGES = ("index", "summarize", "global", "local_mix")
+DOMINANT_SRC = os.path.join(ROOT, "geometry_aware_sparse_amd", "csrc", "global_mfma.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_global_mfma.json")
+
+
+def algorithmic(w, es=2):
+    """Algorithmic work per launch of each stage: what the method must read,
+    write or compute once (bytes / flops), not what a kernel happens to move."""
+    B, N, H, D, M = w.B, w.N, w.H, w.D, w.M
+    row = H * D * es
+    return {
+        # coords (12 B/token) read, slot map (4 B/site) written, RoPE table
+        "index": {"bytes": N * 12 + N * 4},
+        # K and V read once, slot map read, summaries written
+        "summarize": {"bytes": B * N * 2 * row + N * 4 + B * M * 2 * row},
+        # Q read, O_glob written, coords read, summaries read once; 4*D flops
+        # per (token, head, summary) pair (QK^T and PV)
+        "global": {"bytes": B * N * 2 * row + N * 12 + B * M * 2 * row,
+                   "flops": 4.0 * B * H * N * M * D},
+        # Q, K, V read, O_glob and gate read (fused mix), O written, slot map
+        "local_mix": {"bytes": B * N * (5 * row + H * es) + N * 4},
+    }
+
+
+def _sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, or None when the kernel source has changed
+    since the counters were taken."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != _sha(DOMINANT_SRC):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, coords, q, k, v, g, target_s=15.0):
+    """The oracle as it stands, on a bounded sample: rotations and summaries
+    over every token, local/global/mix at a seeded sample of query tokens."""
+    import numpy as np
+
+    import oracle
+    od = oracle.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block, rope_base=w.rope_base)
+    rng = np.random.default_rng(0)
+    # two short probes separate the fixed cost (rotations, summaries) from the
+    # per-token cost, to size the sample for ~target_s of work
+    t = []
+    for n_probe in (64, 512):
+        probe = rng.choice(w.N, n_probe, replace=False).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.forward(od, coords, q, k, v, g, rows=probe)
+        t.append(time.perf_counter() - t0)
+    per_row = max((t[1] - t[0]) / 448.0, 1e-7)
+    fixed = max(t[0] - 64 * per_row, 0.0)
+    n = int(min(w.N, max(512, (target_s - fixed) / per_row)))
+    rows = rng.choice(w.N, n, replace=False).astype(np.int32)
+    t0 = time.perf_counter()
+    oracle.forward(od, coords, q, k, v, g, rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": w.B * n / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": (f"fp64 C oracle, full forward of {w.name} with rotations and summaries over "
+                       f"all {w.N} tokens and local/global/mix at {n} seeded query tokens "
+                       f"(x batch {w.B}); {dt:.1f} s wall")}
+
+
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain device-to-device copy of known size, for scaling the HBM
+    counters (FETCH_SIZE / WRITE_SIZE) of rocprofv3."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the PACK3D "
+              "forward here is a single-GPU operator and this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import geometry_aware_sparse_amd as gas
+    import pack3d_inputs as pi
+
+    w = pi.workload(args.workload)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    es = 2 if w.dtype == "bf16" else 4
+    coords = pi.packing_coords(w.grid, w.packing, block=w.block, seed=w.seed("perm"))
+    q, k, v, g = pi.pack_fields(pi.make_fields(w), coords, w.grid)
+    dev = torch.device("cuda:0")
+    dc = torch.from_numpy(coords).to(dev)
+    dq, dk, dv, dg = (torch.from_numpy(a).to(dev).to(dt).contiguous() for a in (q, k, v, g))
+    d = gas.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block, dtype=dt, rope_base=w.rope_base)
+    ws = torch.empty(gas.pack3d_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(dq)
+    nev = 2 * gas.PACK3D_NUM_STAGES
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+              for _ in range(args.steps)]
+    for evs in events:  # materialise the HIP events before handing them over
+        for e in evs:
+            e.record()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        gas.pack3d_forward(d, dc, dq, dk, dv, dg, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        gas.pack3d_forward(d, dc, dq, dk, dv, dg, out=out, workspace=ws, stage_events=events[s])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    stage_ms = {}
+    for si, name in enumerate(STAGES):
+        stage_ms[name] = float(np.mean([evs[2 * si].elapsed_time(evs[2 * si + 1])
+                                        for evs in events]))
+    work = algorithmic(w, es)
+    gflops = work["global"]["flops"]
+    g_s = stage_ms["global"] * 1e-3
+    achieved = gflops / g_s / 1e12
+    roofline = {"bound": "mfma", "kernel": "k_global_mfma<48>", "achieved": round(achieved, 1),
+                "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4), "traffic": measured_traffic(),
+                "traffic_unit": "bytes/launch"}
+    stage_roof = {}
+    for name in STAGES:
+        gbs = work[name]["bytes"] / (stage_ms[name] * 1e-3) / 1e9
+        stage_roof[name] = {"ms": round(stage_ms[name], 4), "algorithmic_bytes": work[name]["bytes"],
+                            "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    line = {
+        "metric": METRIC, "value": round(w.tokens / (ms_step * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "grid_zyx": list(w.grid), "batch": w.B, "heads": w.H,
+                   "head_dim": w.D, "block": list(w.block), "summaries": w.M,
+                   "tokens": w.tokens, "packing": w.packing, "values": w.values},
+        "roofline": roofline,
+        "stages": stage_roof,
+        "wall_s_timed_region": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, coords, q, k, v, g)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

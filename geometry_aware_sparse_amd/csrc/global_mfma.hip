@@ -37,15 +37,15 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 constexpr int kTS = 64;       // summaries per LDS tile
 constexpr int kWaves = 4;
-constexpr int kQW = 32;  // queries per wave
 
 __device__ __forceinline__ int swap23(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 }  // namespace
 
-template <int D>
-__global__ __launch_bounds__(256) void k_global_mfma(Geo g, const void *geom,
+// G = 32-query groups per wave; both groups share every LDS fragment read.
+template <int D, int G>
+__global__ __launch_bounds__(256, 2) void k_global_mfma(Geo g, const void *geom,
                                                      const int32_t *__restrict__ coords,
                                                      const bf16 *__restrict__ q,
                                                      const bf16 *__restrict__ ks,
@@ -58,9 +58,14 @@ __global__ __launch_bounds__(256) void k_global_mfma(Geo g, const void *geom,
   constexpr int DPAD = DT * 32;
   constexpr int KP = D + 8;                 // LDS pitch of a Ksum row (elements)
   constexpr int VP = kTS + 8;               // LDS pitch of a Vsum^T row (elements)
+  constexpr int QPW = 32 * G;               // queries per wave
+  constexpr int NKC = kTS * D / 8;          // 16-byte Ksum chunks per tile
+  constexpr int NVC = (kTS / 2) * (D / 8);  // Vsum chunk pairs (two summaries) per tile
+  constexpr int KPT = (NKC + 255) / 256;
+  constexpr int VPT = (NVC + 255) / 256;
   static_assert(D % 16 == 0 && DA % 8 == 0, "D must be a multiple of 48");
-  __shared__ __attribute__((aligned(16))) bf16 sK[kTS * KP];
-  __shared__ __attribute__((aligned(16))) bf16 sVt[DPAD * VP];
+  __shared__ __attribute__((aligned(16))) bf16 sK[2][kTS * KP];
+  __shared__ __attribute__((aligned(16))) bf16 sVt[2][DPAD * VP];
 
   const int w = xcd_remap(blockIdx.x, gridDim.x);
   const int tile = w % ntiles;
@@ -68,169 +73,254 @@ __global__ __launch_bounds__(256) void k_global_mfma(Geo g, const void *geom,
   const int h = bh % g.H, b = bh / g.H;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int hi = lane >> 5;  // which half of the wave
-  const int qi = tile * (kWaves * kQW) + wv * kQW + (lane & 31);
-  const bool active = qi < g.N;
-  // a token whose coordinate is off the grid takes no part: zero query,
-  // zero output row (only reachable without PACK3D_VALIDATE)
-  bool cok = false;
   const int64_t sbase = ((int64_t)b * g.H + h) * g.M * D;
+  const int tid = threadIdx.x;
 
-  // constant spare rows of the transposed value tile (never overwritten)
-  for (int e = threadIdx.x; e < (DPAD - D) * kTS; e += 256) {
-    const int r = D + e / kTS, c = e % kTS;
-    sVt[r * VP + c] = (bf16)((ONES && r == D) ? 1.0f : 0.0f);
+  // constant spare rows of the transposed value tiles (never overwritten)
+  if constexpr (DPAD > D) {
+    for (int e = tid; e < 2 * (DPAD - D) * kTS; e += 256) {
+      const int bufi = e / ((DPAD - D) * kTS), rem = e % ((DPAD - D) * kTS);
+      const int r = D + rem / kTS, c = rem % kTS;
+      sVt[bufi][r * VP + c] = (bf16)((ONES && r == D) ? 1.0f : 0.0f);
+    }
   }
 
   // Query fragments: lane holds channels 16c + 8*hi .. +7 of its query,
-  // rotated at the token's own coordinate, scaled, rounded to bf16.
-  bf16x8 qf[KD];
+  // rotated at the token's own coordinate, scaled, rounded to bf16. A token
+  // whose coordinate is off the grid takes no part (zero query, zero output
+  // row; only reachable without PACK3D_VALIDATE).
+  bf16x8 qf[G][KD];
+  bool active[G], cok[G];
+  int qi[G];
   {
     const float2 *tab = rope_table(geom, g);
     const float qscale = g.scale * kLog2e;
-    int c3[3] = {0, 0, 0};
-    if (active) {
-      c3[0] = coords[3 * (int64_t)qi];
-      c3[1] = coords[3 * (int64_t)qi + 1];
-      c3[2] = coords[3 * (int64_t)qi + 2];
-      cok = c3[0] >= 0 && c3[1] >= 0 && c3[2] >= 0 && c3[0] < g.Z && c3[1] < g.Y && c3[2] < g.X;
-      if (!cok) c3[0] = c3[1] = c3[2] = 0;
-    }
-    const int64_t off = (((int64_t)b * g.N + qi) * g.H + h) * D;
 #pragma unroll
-    for (int c = 0; c < KD; c++) {
-      const int d0 = 16 * c + 8 * hi;
-      const int a = d0 / DA, p0 = (d0 % DA) / 2;
-      float x[8];
-      if (cok) {
-        const bf16x8 raw = *reinterpret_cast<const bf16x8 *>(q + off + d0);
-#pragma unroll
-        for (int e = 0; e < 8; e++) x[e] = (float)raw[e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; e++) x[e] = 0.f;
+    for (int gi = 0; gi < G; gi++) {
+      qi[gi] = tile * (kWaves * QPW) + wv * QPW + gi * 32 + (lane & 31);
+      active[gi] = qi[gi] < g.N;
+      cok[gi] = false;
+      int c3[3] = {0, 0, 0};
+      if (active[gi]) {
+        c3[0] = coords[3 * (int64_t)qi[gi]];
+        c3[1] = coords[3 * (int64_t)qi[gi] + 1];
+        c3[2] = coords[3 * (int64_t)qi[gi] + 2];
+        cok[gi] = c3[0] >= 0 && c3[1] >= 0 && c3[2] >= 0 && c3[0] < g.Z && c3[1] < g.Y &&
+                  c3[2] < g.X;
+        if (!cok[gi]) c3[0] = c3[1] = c3[2] = 0;
       }
+      const int64_t off = (((int64_t)b * g.N + qi[gi]) * g.H + h) * D;
 #pragma unroll
-      for (int u = 0; u < 4; u++) {
-        rotate(x[2 * u], x[2 * u + 1], rope_cs(tab, g, a, c3[a], p0 + u));
-        qf[c][2 * u] = (bf16)(x[2 * u] * qscale);
-        qf[c][2 * u + 1] = (bf16)(x[2 * u + 1] * qscale);
+      for (int c = 0; c < KD; c++) {
+        const int d0 = 16 * c + 8 * hi;
+        const int a = d0 / DA, p0 = (d0 % DA) / 2;
+        float x[8];
+        if (cok[gi]) {
+          const bf16x8 raw = *reinterpret_cast<const bf16x8 *>(q + off + d0);
+#pragma unroll
+          for (int e = 0; e < 8; e++) x[e] = (float)raw[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; e++) x[e] = 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          rotate(x[2 * u], x[2 * u + 1], rope_cs(tab, g, a, c3[a], p0 + u));
+          qf[gi][c][2 * u] = (bf16)(x[2 * u] * qscale);
+          qf[gi][c][2 * u + 1] = (bf16)(x[2 * u + 1] * qscale);
+        }
       }
     }
   }
 
-  f32x16 acc[DT];
-#pragma unroll
-  for (int t = 0; t < DT; t++)
-#pragma unroll
-    for (int j = 0; j < 16; j++) acc[t][j] = 0.f;
-  f32x16 cneg;  // -m in every register: seeds the score accumulator
-#pragma unroll
-  for (int j = 0; j < 16; j++) cneg[j] = 0.f;
-  float m = 0.f;       // running maximum (log2 units); valid once started
-  bool started = false;
-  float lsum = 0.f;    // denominator partial when no spare row carries it
-
-  const int rowK = swap23(lane & 31);
-
-  for (int m0 = 0; m0 < g.M; m0 += kTS) {
+  // Tile staging through registers: global loads for tile t+1 are issued
+  // before the arithmetic on tile t and written to the other LDS buffer
+  // after it, so one barrier per tile suffices.
+  bf16x8 pk[KPT], pv[VPT][2];
+  auto load_tile = [&](int m0) {
     const int nm = min(kTS, g.M - m0);
-    __syncthreads();
-    // stage Ksum rows [m0, m0+64) and Vsum^T columns, zero past M
-    for (int e = threadIdx.x; e < kTS * (D / 8); e += 256) {
+#pragma unroll
+    for (int u = 0; u < KPT; u++) {
+      const int e = tid + 256 * u;
       const int r = e / (D / 8), ch = e % (D / 8);
-      bf16x8 kv, vv;
-      if (r < nm) {
-        kv = *reinterpret_cast<const bf16x8 *>(ks + sbase + (int64_t)(m0 + r) * D + 8 * ch);
-        vv = *reinterpret_cast<const bf16x8 *>(vs + sbase + (int64_t)(m0 + r) * D + 8 * ch);
-      } else {
+      if (e < NKC && r < nm)
+        pk[u] = *reinterpret_cast<const bf16x8 *>(ks + sbase + (int64_t)(m0 + r) * D + 8 * ch);
+      else
 #pragma unroll
-        for (int u = 0; u < 8; u++) kv[u] = vv[u] = (bf16)0.0f;
-      }
-      *reinterpret_cast<bf16x8 *>(&sK[r * KP + 8 * ch]) = kv;
-#pragma unroll
-      for (int u = 0; u < 8; u++) sVt[(8 * ch + u) * VP + r] = vv[u];
+        for (int x = 0; x < 8; x++) pk[u][x] = (bf16)0.0f;
     }
-    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < VPT; u++) {
+      const int e = tid + 256 * u;
+      const int rp = e / (D / 8), ch = e % (D / 8);
+#pragma unroll
+      for (int y = 0; y < 2; y++) {
+        if (e < NVC && 2 * rp + y < nm)
+          pv[u][y] = *reinterpret_cast<const bf16x8 *>(vs + sbase + (int64_t)(m0 + 2 * rp + y) * D +
+                                                       8 * ch);
+        else
+#pragma unroll
+          for (int x = 0; x < 8; x++) pv[u][y][x] = (bf16)0.0f;
+      }
+    }
+  };
+  auto store_tile = [&](int bufi) {
+#pragma unroll
+    for (int u = 0; u < KPT; u++) {
+      const int e = tid + 256 * u;
+      if (e < NKC) {
+        const int r = e / (D / 8), ch = e % (D / 8);
+        *reinterpret_cast<bf16x8 *>(&sK[bufi][r * KP + 8 * ch]) = pk[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; u++) {
+      const int e = tid + 256 * u;
+      if (e < NVC) {
+        const int rp = e / (D / 8), ch = e % (D / 8);
+#pragma unroll
+        for (int x = 0; x < 8; x++) {
+          bf16x2 two;
+          two[0] = pv[u][0][x];
+          two[1] = pv[u][1][x];
+          *reinterpret_cast<bf16x2 *>(&sVt[bufi][(8 * ch + x) * VP + 2 * rp]) = two;
+        }
+      }
+    }
+  };
 
+  f32x16 acc[G][DT];
+  f32x16 cneg[G];  // -m in every register: seeds the score accumulator
+  float m[G], lsum[G];
+#pragma unroll
+  for (int gi = 0; gi < G; gi++) {
+#pragma unroll
+    for (int t = 0; t < DT; t++)
+#pragma unroll
+      for (int j = 0; j < 16; j++) acc[gi][t][j] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; j++) cneg[gi][j] = 0.f;
+    m[gi] = 0.f;
+    lsum[gi] = 0.f;
+  }
+  bool started = false;  // the first sub-tile sets the running maximum
+  const int rowK = swap23(lane & 31);
+  const int ntile_s = (g.M + kTS - 1) / kTS;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int ts = 0; ts < ntile_s; ts++) {
+    const int bufi = ts & 1;
+    const int m0 = ts * kTS;
+    if (ts + 1 < ntile_s) load_tile(m0 + kTS);
+    const bf16 *cK = sK[bufi];
+    const bf16 *cV = sVt[bufi];
 #pragma unroll
     for (int sub = 0; sub < kTS / 32; sub++) {
       if (m0 + 32 * sub >= g.M) break;
-      // S^T - m for this 32-summary sub-tile
-      f32x16 s = cneg;
+      // S^T - m for this 32-summary sub-tile, both query groups
+      f32x16 s[G];
+#pragma unroll
+      for (int gi = 0; gi < G; gi++) s[gi] = cneg[gi];
 #pragma unroll
       for (int c = 0; c < KD; c++) {
         const bf16x8 kf =
-            *reinterpret_cast<const bf16x8 *>(&sK[(32 * sub + rowK) * KP + 16 * c + 8 * hi]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s, 0, 0, 0);
+            *reinterpret_cast<const bf16x8 *>(&cK[(32 * sub + rowK) * KP + 16 * c + 8 * hi]);
+#pragma unroll
+        for (int gi = 0; gi < G; gi++)
+          s[gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[gi][c], s[gi], 0, 0, 0);
       }
       if (m0 + 32 * sub + 32 > g.M) {  // past-the-end summaries take no part
 #pragma unroll
         for (int j = 0; j < 16; j++) {
           const int r = (j >> 2) * 8 + hi * 4 + (j & 3);
-          if (m0 + 32 * sub + swap23(r) >= g.M) s[j] = -INFINITY;
+          if (m0 + 32 * sub + swap23(r) >= g.M)
+#pragma unroll
+            for (int gi = 0; gi < G; gi++) s[gi][j] = -INFINITY;
         }
       }
-      float tmax = s[0];
+      float tmax[G];
+      bool need[G];
+      bool any = false;
 #pragma unroll
-      for (int j = 1; j < 16; j++) tmax = fmaxf(tmax, s[j]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      // raise the maximum only when needed (always on the first sub-tile)
-      const bool need = !started || tmax > kTau;
-      if (__ballot(need)) {
-        const float shift = need ? tmax : 0.f;
-        const float alpha = started ? __builtin_amdgcn_exp2f(-shift) : 0.f;
+      for (int gi = 0; gi < G; gi++) {
+        float t0 = s[gi][0];
 #pragma unroll
-        for (int j = 0; j < 16; j++) s[j] -= shift;
-#pragma unroll
-        for (int t = 0; t < DT; t++)
-#pragma unroll
-          for (int j = 0; j < 16; j++) acc[t][j] *= alpha;
-        lsum *= alpha;
-        m = started ? m + shift : shift;
-        started = true;
-#pragma unroll
-        for (int j = 0; j < 16; j++) cneg[j] = -m;
+        for (int j = 1; j < 16; j++) t0 = fmaxf(t0, s[gi][j]);
+        tmax[gi] = fmaxf(t0, __shfl_xor(t0, 32));
+        // raise the maximum only when needed (always on the first sub-tile)
+        need[gi] = !started || tmax[gi] > kTau;
+        any = any || need[gi];
       }
-      bf16x8 pf[2];
+      if (__ballot(any)) {
 #pragma unroll
-      for (int j = 0; j < 16; j++) {
-        const float p = __builtin_amdgcn_exp2f(s[j]);
-        if (!ONES) lsum += p;
-        pf[j >> 3][j & 7] = (bf16)p;
+        for (int gi = 0; gi < G; gi++) {
+          const float shift = need[gi] ? tmax[gi] : 0.f;
+          const float alpha = started ? __builtin_amdgcn_exp2f(-shift) : 0.f;
+#pragma unroll
+          for (int j = 0; j < 16; j++) s[gi][j] -= shift;
+#pragma unroll
+          for (int t = 0; t < DT; t++)
+#pragma unroll
+            for (int j = 0; j < 16; j++) acc[gi][t][j] *= alpha;
+          lsum[gi] *= alpha;
+          m[gi] = started ? m[gi] + shift : shift;
+#pragma unroll
+          for (int j = 0; j < 16; j++) cneg[gi][j] = -m[gi];
+        }
+        started = true;
+      }
+      bf16x8 pf[G][2];
+#pragma unroll
+      for (int gi = 0; gi < G; gi++) {
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+          const float p = __builtin_amdgcn_exp2f(s[gi][j]);
+          if (!ONES) lsum[gi] += p;
+          pf[gi][j >> 3][j & 7] = (bf16)p;
+        }
       }
 #pragma unroll
       for (int t = 0; t < DT; t++) {
 #pragma unroll
         for (int c2 = 0; c2 < 2; c2++) {
           const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(
-              &sVt[(32 * t + (lane & 31)) * VP + 32 * sub + 16 * c2 + 8 * hi]);
-          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c2], acc[t], 0, 0, 0);
+              &cV[(32 * t + (lane & 31)) * VP + 32 * sub + 16 * c2 + 8 * hi]);
+#pragma unroll
+          for (int gi = 0; gi < G; gi++)
+            acc[gi][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[gi][c2], acc[gi][t], 0, 0, 0);
         }
       }
     }
+    if (ts + 1 < ntile_s) store_tile(bufi ^ 1);
+    __syncthreads();
   }
 
-  // denominator: spare row D (lanes 0..31, register 8 of the last tile), or
-  // the two half-wave partial sums
-  float den;
-  if (ONES)
-    den = __shfl(acc[DT - 1][8], lane & 31);
-  else
-    den = lsum + __shfl_xor(lsum, 32);
-  const float inv = (den > 0.f && cok) ? 1.0f / den : 0.f;
-  if (!active) return;
-  bf16 *orow = out + (((int64_t)b * g.N + qi) * g.H + h) * D;
 #pragma unroll
-  for (int t = 0; t < DT; t++) {
+  for (int gi = 0; gi < G; gi++) {
+    // denominator: spare row D (lanes 0..31, register 8 of the last tile),
+    // or the two half-wave partial sums
+    float den;
+    if (ONES)
+      den = __shfl(acc[gi][DT - 1][8], lane & 31);
+    else
+      den = lsum[gi] + __shfl_xor(lsum[gi], 32);
+    const float inv = (den > 0.f && cok[gi]) ? 1.0f / den : 0.f;
+    if (!active[gi]) continue;
+    bf16 *orow = out + (((int64_t)b * g.N + qi[gi]) * g.H + h) * D;
 #pragma unroll
-    for (int jj = 0; jj < 4; jj++) {
-      const int d = 32 * t + 8 * jj + 4 * hi;
-      if (d < D) {
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        bf16x4 o4;
+    for (int t = 0; t < DT; t++) {
 #pragma unroll
-        for (int u = 0; u < 4; u++) o4[u] = (bf16)(acc[t][4 * jj + u] * inv);
-        *reinterpret_cast<bf16x4 *>(orow + d) = o4;
+      for (int jj = 0; jj < 4; jj++) {
+        const int d = 32 * t + 8 * jj + 4 * hi;
+        if (d < D) {
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          bf16x4 o4;
+#pragma unroll
+          for (int u = 0; u < 4; u++) o4[u] = (bf16)(acc[gi][t][4 * jj + u] * inv);
+          *reinterpret_cast<bf16x4 *>(orow + d) = o4;
+        }
       }
     }
   }
@@ -241,12 +331,12 @@ hipError_t launch_global_valu(const Geo &g, int dtype, const void *geom, const i
                               hipStream_t s, bool *supported);
 
 namespace {
-template <int D>
+template <int D, int G>
 hipError_t run_global_mfma(const Geo &g, const void *geom, const int32_t *coords, const void *q,
                            const void *ks, const void *vs, void *out, hipStream_t s) {
-  const int ntiles = (g.N + kWaves * kQW - 1) / (kWaves * kQW);
+  const int ntiles = (g.N + kWaves * 32 * G - 1) / (kWaves * 32 * G);
   const int64_t nwg = (int64_t)ntiles * g.B * g.H;
-  hipLaunchKernelGGL((k_global_mfma<D>), dim3((unsigned)nwg), dim3(256), 0, s, g, geom, coords,
+  hipLaunchKernelGGL((k_global_mfma<D, G>), dim3((unsigned)nwg), dim3(256), 0, s, g, geom, coords,
                      static_cast<const bf16 *>(q), static_cast<const bf16 *>(ks),
                      static_cast<const bf16 *>(vs), static_cast<bf16 *>(out), ntiles);
   return hipGetLastError();
@@ -258,8 +348,8 @@ hipError_t launch_global(const Geo &g, int dtype, const void *geom, const int32_
                          bool *supported) {
   if (dtype == PACK3D_BF16 && g.excl == PACK3D_EXCL_NONE) {
     *supported = true;
-    if (g.D == 48) return run_global_mfma<48>(g, geom, coords, q, ks, vs, out, s);
-    if (g.D == 96) return run_global_mfma<96>(g, geom, coords, q, ks, vs, out, s);
+    if (g.D == 48) return run_global_mfma<48, 2>(g, geom, coords, q, ks, vs, out, s);
+    if (g.D == 96) return run_global_mfma<96, 1>(g, geom, coords, q, ks, vs, out, s);
   }
   return launch_global_valu(g, dtype, geom, coords, q, ks, vs, out, s, supported);
 }

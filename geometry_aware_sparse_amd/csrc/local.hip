@@ -146,6 +146,161 @@ __global__ __launch_bounds__(TZ *TY *TX) void k_local(Geo g, const void *geom, c
   }
 }
 
+// bf16 variant for head dims that are multiples of 16: two lanes per query,
+// each owning half of the channels. Dot products use v_dot2_f32_bf16 on
+// packed pairs (the rotated, scaled query is rounded to bf16), the two halves
+// meet through one lane swap per neighbour, and the value sum pairs
+// neighbours (k, k+1) so that one v_dot2 accumulates two neighbours for one
+// channel. Halves the per-lane registers of the one-lane-per-query kernel, so
+// four waves per SIMD stay resident.
+template <int D, int TZ, int TY, int TX>
+__global__ __launch_bounds__(2 * TZ *TY *TX) void k_local_pair(
+    Geo g, const void *geom, const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+    const bf16 *__restrict__ v, const bf16 *gate, const bf16 *oglob, bf16 *out, int ntz, int nty,
+    int ntx) {
+  constexpr int HZ = TZ + 2, HY = TY + 2, HX = TX + 2, NH = HZ * HY * HX, NQ = TZ * TY * TX;
+  constexpr int NT = 2 * NQ;
+  constexpr int DA = D / 3;
+  constexpr int DH = D / 2;            // channels per lane
+  constexpr int PITCH = D;             // LDS row pitch (elements), 16-byte aligned rows
+  static_assert(D % 16 == 0 && DA % 8 == 0, "head dim must be a multiple of 48");
+  __shared__ __attribute__((aligned(16))) bf16 sK[NH * PITCH];
+  __shared__ __attribute__((aligned(16))) bf16 sV[NH * PITCH];
+  __shared__ int sSlot[NH];
+
+  const int ntiles = ntz * nty * ntx;
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = w % g.H;
+  const int tile = (w / g.H) % ntiles;
+  const int b = w / (g.H * ntiles);
+  const int z0 = (tile / (nty * ntx)) * TZ, y0 = ((tile / ntx) % nty) * TY, x0 = (tile % ntx) * TX;
+  const int32_t *slot = slot_map(geom, g);
+  const float2 *tab = rope_table(geom, g);
+  const int64_t bN = (int64_t)b * g.N;
+
+  // Stage K~ (rotated, bf16) and V of the halo box, 8 channels per step.
+  for (int e = threadIdx.x; e < NH * (D / 8); e += NT) {
+    const int hs = e / (D / 8), ch = e % (D / 8);
+    const int hz = hs / (HY * HX), hy = (hs / HX) % HY, hx = hs % HX;
+    const int z = z0 - 1 + hz, y = y0 - 1 + hy, x = x0 - 1 + hx;
+    int j = -1;
+    if (z >= 0 && y >= 0 && x >= 0 && z < g.Z && y < g.Y && x < g.X) j = slot[site_of(g, z, y, x)];
+    if (ch == 0) sSlot[hs] = j;
+    bf16x8 ko, vo;
+    if (j >= 0) {
+      const int64_t off = ((bN + j) * g.H + h) * D + ch * 8;
+      const bf16x8 kr = *reinterpret_cast<const bf16x8 *>(k + off);
+      vo = *reinterpret_cast<const bf16x8 *>(v + off);
+      const int c3[3] = {z, y, x};
+      const int a = (ch * 8) / DA, p0 = ((ch * 8) % DA) / 2;
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        float k0 = (float)kr[2 * u], k1 = (float)kr[2 * u + 1];
+        rotate(k0, k1, rope_cs(tab, g, a, c3[a], p0 + u));
+        ko[2 * u] = (bf16)k0;
+        ko[2 * u + 1] = (bf16)k1;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; u++) ko[u] = vo[u] = (bf16)0.0f;
+    }
+    *reinterpret_cast<bf16x8 *>(&sK[hs * PITCH + ch * 8]) = ko;
+    *reinterpret_cast<bf16x8 *>(&sV[hs * PITCH + ch * 8]) = vo;
+  }
+  __syncthreads();
+
+  const int qn = threadIdx.x >> 1, hh = threadIdx.x & 1;
+  const int tz = qn / (TY * TX), ty = (qn / TX) % TY, tx = qn % TX;
+  const int qs = ((tz + 1) * HY + (ty + 1)) * HX + (tx + 1);
+  const int i = sSlot[qs];  // both lanes of a query see the same value
+  if (i < 0) return;
+  const int c3[3] = {z0 + tz, y0 + ty, x0 + tx};
+  const float qscale = g.scale * kLog2e;
+  const int64_t off = ((bN + i) * g.H + h) * D + hh * DH;
+
+  bf16x2 qp[DH / 2];
+#pragma unroll
+  for (int c8 = 0; c8 < DH / 8; c8++) {
+    const bf16x8 raw = *reinterpret_cast<const bf16x8 *>(q + off + 8 * c8);
+    const int d0 = hh * DH + 8 * c8, a = d0 / DA, p0 = (d0 % DA) / 2;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      float x0v = (float)raw[2 * u], x1v = (float)raw[2 * u + 1];
+      rotate(x0v, x1v, rope_cs(tab, g, a, c3[a], p0 + u));
+      qp[4 * c8 + u][0] = (bf16)(x0v * qscale);
+      qp[4 * c8 + u][1] = (bf16)(x1v * qscale);
+    }
+  }
+
+  // logits (log2 units) in canonical offset order k = (dz+1)*9 + (dy+1)*3 + dx+1
+  float lg[27];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kk = 0; kk < 27; kk++) {
+    const int hs = qs + ((kk / 9) - 1) * HY * HX + (((kk / 3) % 3) - 1) * HX + (kk % 3) - 1;
+    const bf16x2 *kr = reinterpret_cast<const bf16x2 *>(sK + hs * PITCH + hh * DH);
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < DH / 2; j++) acc = __builtin_amdgcn_fdot2_f32_bf16(qp[j], kr[j], acc, false);
+    acc += __shfl_xor(acc, 1);
+    lg[kk] = sSlot[hs] >= 0 ? acc : -INFINITY;
+    mx = fmaxf(mx, lg[kk]);
+  }
+  float pr[28];
+  float den = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < 27; kk++) {
+    pr[kk] = __builtin_amdgcn_exp2f(lg[kk] - mx);  // exactly 0 for an invalid neighbour
+    den += pr[kk];
+  }
+  pr[27] = 0.f;
+  float o[DH];
+#pragma unroll
+  for (int d = 0; d < DH; d++) o[d] = 0.f;
+  // neighbours in pairs (2j, 2j+1); the last pair's second member has weight 0
+#pragma unroll
+  for (int kp = 0; kp < 14; kp++) {
+    const int k0 = 2 * kp, k1 = kp < 13 ? 2 * kp + 1 : 2 * kp;
+    const int hs0 = qs + ((k0 / 9) - 1) * HY * HX + (((k0 / 3) % 3) - 1) * HX + (k0 % 3) - 1;
+    const int hs1 = qs + ((k1 / 9) - 1) * HY * HX + (((k1 / 3) % 3) - 1) * HX + (k1 % 3) - 1;
+    bf16x2 pp;
+    pp[0] = (bf16)pr[2 * kp];
+    pp[1] = (bf16)pr[2 * kp + 1];
+    const uint32_t *A = reinterpret_cast<const uint32_t *>(sV + hs0 * PITCH + hh * DH);
+    const uint32_t *Bv = reinterpret_cast<const uint32_t *>(sV + hs1 * PITCH + hh * DH);
+#pragma unroll
+    for (int j = 0; j < DH / 2; j++) {
+      const uint32_t a = A[j], bb = Bv[j];
+      const uint32_t lo = (a & 0xffffu) | (bb << 16), hi2 = (a >> 16) | (bb & 0xffff0000u);
+      o[2 * j] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2, lo), o[2 * j], false);
+      o[2 * j + 1] =
+          __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2, hi2), o[2 * j + 1], false);
+    }
+  }
+  const float inv = 1.0f / den;
+  if (gate) {
+    const float gl = (float)gate[(bN + i) * g.H + h];
+    const float gg = 1.0f / (1.0f + expf(-gl));
+#pragma unroll
+    for (int c8 = 0; c8 < DH / 8; c8++) {
+      const bf16x8 og = *reinterpret_cast<const bf16x8 *>(oglob + off + 8 * c8);
+      bf16x8 r;
+#pragma unroll
+      for (int u = 0; u < 8; u++)
+        r[u] = (bf16)((1.0f - gg) * (o[8 * c8 + u] * inv) + gg * (float)og[u]);
+      *reinterpret_cast<bf16x8 *>(out + off + 8 * c8) = r;
+    }
+  } else {
+#pragma unroll
+    for (int c8 = 0; c8 < DH / 8; c8++) {
+      bf16x8 r;
+#pragma unroll
+      for (int u = 0; u < 8; u++) r[u] = (bf16)(o[8 * c8 + u] * inv);
+      *reinterpret_cast<bf16x8 *>(out + off + 8 * c8) = r;
+    }
+  }
+}
+
 namespace {
 
 template <typename T, int D, int TZ, int TY, int TX>
@@ -160,6 +315,19 @@ hipError_t run_local(const Geo &g, const void *geom, const void *q, const void *
   return hipGetLastError();
 }
 
+template <int D, int TZ, int TY, int TX>
+hipError_t run_local_pair(const Geo &g, const void *geom, const void *q, const void *k,
+                          const void *v, const void *gate, const void *og, void *out,
+                          hipStream_t s) {
+  const int ntz = (g.Z + TZ - 1) / TZ, nty = (g.Y + TY - 1) / TY, ntx = (g.X + TX - 1) / TX;
+  const int64_t nwg = (int64_t)g.B * ntz * nty * ntx * g.H;
+  hipLaunchKernelGGL((k_local_pair<D, TZ, TY, TX>), dim3((unsigned)nwg), dim3(2 * TZ * TY * TX), 0,
+                     s, g, geom, static_cast<const bf16 *>(q), static_cast<const bf16 *>(k),
+                     static_cast<const bf16 *>(v), static_cast<const bf16 *>(gate),
+                     static_cast<const bf16 *>(og), static_cast<bf16 *>(out), ntz, nty, ntx);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_local(const Geo &g, int dtype, const void *geom, const void *q, const void *k,
@@ -171,8 +339,8 @@ hipError_t launch_local(const Geo &g, int dtype, const void *geom, const void *q
       case 6: return run_local<bf16, 6, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
       case 12: return run_local<bf16, 12, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
       case 24: return run_local<bf16, 24, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
-      case 48: return run_local<bf16, 48, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
-      case 96: return run_local<bf16, 96, 2, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
+      case 48: return run_local_pair<48, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
+      case 96: return run_local_pair<96, 2, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
     }
   } else {
     switch (g.D) {
