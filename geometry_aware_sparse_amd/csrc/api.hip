@@ -55,6 +55,7 @@ int make_geo(const pack3d_desc *d, Geo *g) {
   g->scale = d->scale > 0.0f ? d->scale : (float)(1.0 / sqrt((double)d->D));
   g->rope_base = d->rope_base;
   g->excl = d->exclusion;
+  g->flags = d->flags;
   g->slot_off = (int64_t)kAlign;
   g->table_off = (int64_t)align_up(kAlign + (size_t)sites * 4);
   return PACK3D_OK;

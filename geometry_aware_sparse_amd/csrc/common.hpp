@@ -26,6 +26,7 @@ struct Geo {
   float scale;    // softmax scale
   float rope_base;
   int excl;       // pack3d_exclusion
+  unsigned flags; // pack3d_desc flags
   // geometry buffer offsets (bytes)
   int64_t slot_off, table_off;
 };

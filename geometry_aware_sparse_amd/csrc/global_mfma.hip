@@ -18,23 +18,27 @@
 // probabilities go from registers straight into the matrix core, no shuffle.
 //
 // Softmax details. Scores are in log2 units (the query is pre-multiplied by
-// scale*log2(e)). The running maximum m is folded into the matrix product by
-// seeding the accumulator with -m, so the scores arrive already shifted.
-// The maximum is only raised when a tile exceeds it by more than 8 (a factor
-// 256 in probability, harmless in fp32 sums and bf16 operands), which after
-// the first tile almost never happens; the result is the same softmax up to
-// rounding. For D = 48 the output tile has 16 spare rows; row 48 of the
-// transposed value tile is all ones so the matrix core also returns the
-// softmax denominator. Each query's arithmetic depends only on its own row
-// and the summaries, never on which tokens share its tile, so a repack of
-// the tokens permutes the output bit for bit.
+// scale*log2(e)). Subtracting a running maximum only guards exp against
+// overflow and underflow; fp32 and bf16 share one 8-bit exponent range, so
+// as long as every score stays below 2^7 and the denominator stays well
+// above the underflow limit, p = exp2(s) with no maximum at all gives the
+// same softmax up to rounding. That is the fast path: no maximum, no
+// rescale, the matrix core accumulates straight from exp2. For D = 48 the
+// output tile has 16 spare rows; row 48 of the transposed value tile is all
+// ones, so the matrix core also returns the denominator. A query whose
+// denominator comes out non-finite or below 2^-100 is recomputed by an exact
+// two-pass path (maximum first, then the sums with the maximum subtracted)
+// that reads the summaries straight from global memory; queries that passed
+// keep their fast-path result. The choice is made per query, and each
+// query's arithmetic depends only on its own row and the summaries, never on
+// which tokens share its tile, so a repack of the tokens permutes the output
+// bit for bit.
 #include "launch.hpp"
 
 namespace pk {
 
 namespace {
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 constexpr int kTS = 64;       // summaries per LDS tile
 constexpr int kWaves = 4;
 
@@ -45,12 +49,12 @@ __device__ __forceinline__ int swap23(int r) {
 
 // G = 32-query groups per wave; both groups share every LDS fragment read.
 template <int D, int G>
-__global__ __launch_bounds__(256, 2) void k_global_mfma(Geo g, const void *geom,
-                                                     const int32_t *__restrict__ coords,
-                                                     const bf16 *__restrict__ q,
-                                                     const bf16 *__restrict__ ks,
-                                                     const bf16 *__restrict__ vs,
-                                                     bf16 *__restrict__ out, int ntiles) {
+__global__ __launch_bounds__(256, D == 48 ? 2 : 3) void k_global_mfma(Geo g, const void *geom,
+                                                        const int32_t *__restrict__ coords,
+                                                        const bf16 *__restrict__ q,
+                                                        const bf16 *__restrict__ ks,
+                                                        const bf16 *__restrict__ vs,
+                                                        bf16 *__restrict__ out, int ntiles) {
   constexpr int DA = D / 3;
   constexpr int KD = D / 16;                // 16-deep steps of Ksum * Q~^T
   constexpr bool ONES = (D % 32) != 0;      // spare output rows carry the denominator
@@ -190,23 +194,22 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(Geo g, const void *geom,
   };
 
   f32x16 acc[G][DT];
-  f32x16 cneg[G];  // -m in every register: seeds the score accumulator
-  float m[G], lsum[G];
+  float lsum[G];
 #pragma unroll
   for (int gi = 0; gi < G; gi++) {
 #pragma unroll
     for (int t = 0; t < DT; t++)
 #pragma unroll
       for (int j = 0; j < 16; j++) acc[gi][t][j] = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; j++) cneg[gi][j] = 0.f;
-    m[gi] = 0.f;
     lsum[gi] = 0.f;
   }
-  bool started = false;  // the first sub-tile sets the running maximum
+  const f32x16 zero16 = {};
   const int rowK = swap23(lane & 31);
   const int ntile_s = (g.M + kTS - 1) / kTS;
 
+  // ---- fast path: p = exp2(s), no running maximum ----
+  const bool force_exact = (g.flags & PACK3D_EXACT_SOFTMAX) != 0;  // uniform
+  if (!force_exact) {
   load_tile(0);
   store_tile(0);
   __syncthreads();
@@ -219,17 +222,15 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(Geo g, const void *geom,
 #pragma unroll
     for (int sub = 0; sub < kTS / 32; sub++) {
       if (m0 + 32 * sub >= g.M) break;
-      // S^T - m for this 32-summary sub-tile, both query groups
       f32x16 s[G];
-#pragma unroll
-      for (int gi = 0; gi < G; gi++) s[gi] = cneg[gi];
 #pragma unroll
       for (int c = 0; c < KD; c++) {
         const bf16x8 kf =
             *reinterpret_cast<const bf16x8 *>(&cK[(32 * sub + rowK) * KP + 16 * c + 8 * hi]);
 #pragma unroll
         for (int gi = 0; gi < G; gi++)
-          s[gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[gi][c], s[gi], 0, 0, 0);
+          s[gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[gi][c], c == 0 ? zero16 : s[gi],
+                                                          0, 0, 0);
       }
       if (m0 + 32 * sub + 32 > g.M) {  // past-the-end summaries take no part
 #pragma unroll
@@ -239,37 +240,6 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(Geo g, const void *geom,
 #pragma unroll
             for (int gi = 0; gi < G; gi++) s[gi][j] = -INFINITY;
         }
-      }
-      float tmax[G];
-      bool need[G];
-      bool any = false;
-#pragma unroll
-      for (int gi = 0; gi < G; gi++) {
-        float t0 = s[gi][0];
-#pragma unroll
-        for (int j = 1; j < 16; j++) t0 = fmaxf(t0, s[gi][j]);
-        tmax[gi] = fmaxf(t0, __shfl_xor(t0, 32));
-        // raise the maximum only when needed (always on the first sub-tile)
-        need[gi] = !started || tmax[gi] > kTau;
-        any = any || need[gi];
-      }
-      if (__ballot(any)) {
-#pragma unroll
-        for (int gi = 0; gi < G; gi++) {
-          const float shift = need[gi] ? tmax[gi] : 0.f;
-          const float alpha = started ? __builtin_amdgcn_exp2f(-shift) : 0.f;
-#pragma unroll
-          for (int j = 0; j < 16; j++) s[gi][j] -= shift;
-#pragma unroll
-          for (int t = 0; t < DT; t++)
-#pragma unroll
-            for (int j = 0; j < 16; j++) acc[gi][t][j] *= alpha;
-          lsum[gi] *= alpha;
-          m[gi] = started ? m[gi] + shift : shift;
-#pragma unroll
-          for (int j = 0; j < 16; j++) cneg[gi][j] = -m[gi];
-        }
-        started = true;
       }
       bf16x8 pf[G][2];
 #pragma unroll
@@ -296,18 +266,149 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(Geo g, const void *geom,
     if (ts + 1 < ntile_s) store_tile(bufi ^ 1);
     __syncthreads();
   }
+  }
 
+  // denominator: spare row D (lanes 0..31, register 8 of the last tile), or
+  // the two half-wave partial sums. A query passes when its denominator lies
+  // in [2^-100, 2^100] (far from underflow, and far enough from overflow that
+  // p*v sums cannot overflow for any sane value) and every accumulator of it,
+  // in both half-waves, is finite.
+  constexpr float kMinDen = 7.8886091e-31f;  // 2^-100
+  constexpr float kMaxDen = 1.2676506e30f;   // 2^100
+  bool redo[G];
+  bool any_redo = false;
 #pragma unroll
   for (int gi = 0; gi < G; gi++) {
-    // denominator: spare row D (lanes 0..31, register 8 of the last tile),
-    // or the two half-wave partial sums
     float den;
     if (ONES)
       den = __shfl(acc[gi][DT - 1][8], lane & 31);
     else
       den = lsum[gi] + __shfl_xor(lsum[gi], 32);
-    const float inv = (den > 0.f && cok[gi]) ? 1.0f / den : 0.f;
-    if (!active[gi]) continue;
+    int bad = !(den >= kMinDen && den <= kMaxDen);
+#pragma unroll
+    for (int t = 0; t < DT; t++)
+#pragma unroll
+      for (int j = 0; j < 16; j++) bad |= !__builtin_isfinite(acc[gi][t][j]);
+    bad |= __shfl_xor(bad, 32);
+    redo[gi] = cok[gi] && (force_exact || bad);
+    any_redo = any_redo || redo[gi];
+    const float inv = (cok[gi] && !redo[gi]) ? 1.0f / den : 0.f;
+    if (active[gi] && !redo[gi]) {
+      bf16 *orow = out + (((int64_t)b * g.N + qi[gi]) * g.H + h) * D;
+#pragma unroll
+      for (int t = 0; t < DT; t++) {
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+          const int d = 32 * t + 8 * jj + 4 * hi;
+          if (d < D) {
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            bf16x4 o4;
+#pragma unroll
+            for (int u = 0; u < 4; u++) o4[u] = (bf16)(acc[gi][t][4 * jj + u] * inv);
+            *reinterpret_cast<bf16x4 *>(orow + d) = o4;
+          }
+        }
+      }
+    }
+  }
+  if (!__ballot(any_redo)) return;
+
+  // ---- exact two-pass path for the queries that failed (rare) ----
+  // Reads summary fragments straight from global memory; no barriers, so
+  // only the waves that need it run it.
+  float mrow[G];
+#pragma unroll
+  for (int gi = 0; gi < G; gi++) mrow[gi] = -INFINITY;
+  for (int m0 = 0; m0 < g.M; m0 += 32) {
+    const bool rvalid = m0 + rowK < g.M;
+    f32x16 s[G];
+#pragma unroll
+    for (int c = 0; c < KD; c++) {
+      bf16x8 kf;
+      if (rvalid)
+        kf = *reinterpret_cast<const bf16x8 *>(ks + sbase + (int64_t)(m0 + rowK) * D + 16 * c + 8 * hi);
+      else
+#pragma unroll
+        for (int x = 0; x < 8; x++) kf[x] = (bf16)0.0f;
+#pragma unroll
+      for (int gi = 0; gi < G; gi++)
+        s[gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[gi][c], c == 0 ? zero16 : s[gi], 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const int r = (j >> 2) * 8 + hi * 4 + (j & 3);
+      if (m0 + swap23(r) < g.M)
+#pragma unroll
+        for (int gi = 0; gi < G; gi++) mrow[gi] = fmaxf(mrow[gi], s[gi][j]);
+    }
+  }
+  f32x16 cneg[G];
+#pragma unroll
+  for (int gi = 0; gi < G; gi++) {
+    mrow[gi] = fmaxf(mrow[gi], __shfl_xor(mrow[gi], 32));
+#pragma unroll
+    for (int j = 0; j < 16; j++) cneg[gi][j] = -mrow[gi];
+#pragma unroll
+    for (int t = 0; t < DT; t++)
+#pragma unroll
+      for (int j = 0; j < 16; j++) acc[gi][t][j] = 0.f;
+    lsum[gi] = 0.f;
+  }
+  for (int m0 = 0; m0 < g.M; m0 += 32) {
+    const bool rvalid = m0 + rowK < g.M;
+    f32x16 s[G];
+#pragma unroll
+    for (int gi = 0; gi < G; gi++) s[gi] = cneg[gi];
+#pragma unroll
+    for (int c = 0; c < KD; c++) {
+      bf16x8 kf;
+      if (rvalid)
+        kf = *reinterpret_cast<const bf16x8 *>(ks + sbase + (int64_t)(m0 + rowK) * D + 16 * c + 8 * hi);
+      else
+#pragma unroll
+        for (int x = 0; x < 8; x++) kf[x] = (bf16)0.0f;
+#pragma unroll
+      for (int gi = 0; gi < G; gi++)
+        s[gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[gi][c], s[gi], 0, 0, 0);
+    }
+    bf16x8 pf[G][2];
+#pragma unroll
+    for (int gi = 0; gi < G; gi++) {
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        const int r = (j >> 2) * 8 + hi * 4 + (j & 3);
+        const float p = (m0 + swap23(r) < g.M) ? __builtin_amdgcn_exp2f(s[gi][j]) : 0.f;
+        if (!ONES) lsum[gi] += p;
+        pf[gi][j >> 3][j & 7] = (bf16)p;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < DT; t++) {
+      const int d = 32 * t + (lane & 31);
+#pragma unroll
+      for (int c2 = 0; c2 < 2; c2++) {
+        bf16x8 vf;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const int row = m0 + 16 * c2 + 8 * hi + e;
+          vf[e] = (row < g.M && d < D) ? vs[sbase + (int64_t)row * D + d]
+                                       : (bf16)((ONES && d == D) ? 1.0f : 0.0f);
+        }
+#pragma unroll
+        for (int gi = 0; gi < G; gi++)
+          acc[gi][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[gi][c2], acc[gi][t], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int gi = 0; gi < G; gi++) {
+    float den;
+    if (ONES)
+      den = __shfl(acc[gi][DT - 1][8], lane & 31);
+    else
+      den = lsum[gi] + __shfl_xor(lsum[gi], 32);
+    if (!(active[gi] && redo[gi])) continue;
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
     bf16 *orow = out + (((int64_t)b * g.N + qi[gi]) * g.H + h) * D;
 #pragma unroll
     for (int t = 0; t < DT; t++) {

@@ -82,6 +82,12 @@ typedef enum pack3d_exclusion {
 } pack3d_exclusion;
 
 #define PACK3D_VALIDATE 0x1u /* synchronise and report coordinate errors */
+/* Global branch on matrix cores: by default scores go through exp2 without a
+ * running maximum (exact up to rounding while every score is below 2^7 in
+ * log2 units) and any query whose softmax denominator leaves the safe range
+ * is redone by an exact two-pass softmax. This flag sends every query
+ * through the two-pass softmax (maximum first, then the sums). */
+#define PACK3D_EXACT_SOFTMAX 0x2u
 
 typedef struct pack3d_desc {
   int32_t B, N, H, D;  /* batch, tokens, heads, head dim (D % 6 == 0)         */

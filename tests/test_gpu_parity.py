@@ -160,3 +160,64 @@ def test_all_summaries_excluded_gives_local_only_mix():
     ks, vs = gas.pack3d_block_summarize(d, geom, to_dev(k, dt), to_dev(v, dt))
     og = gas.pack3d_global_attn(d, geom, dc, dq, ks, vs)
     assert torch.count_nonzero(og).item() == 0
+
+
+MFMA_CASES = [CASES[1], CASES[2], CASES[3], CASES[8]]
+
+
+@pytest.mark.parametrize("w", MFMA_CASES, ids=[c.name for c in MFMA_CASES])
+def test_global_exact_softmax_flag(w):
+    """Every query through the two-pass softmax (maximum first) matches the
+    oracle, and so does the default path."""
+    import geometry_aware_sparse_amd as gas
+    coords, q, k, v, g = inputs(w)
+    d, od = desc_pair(w)
+    de = gas.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block, dtype=gas.PACK3D_BF16,
+                       exact_softmax=True)
+    dt = tdtype(w)
+    dc, dq = to_dev(coords, torch.int32), to_dev(q, dt)
+    geom, _, _, _ = gas.pack3d_index_build(d, dc)
+    ks, vs = gas.pack3d_block_summarize(d, geom, to_dev(k, dt), to_dev(v, dt))
+    fast = gas.pack3d_global_attn(d, geom, dc, dq, ks, vs)
+    exact = gas.pack3d_global_attn(de, geom, dc, dq, ks, vs)
+    slot, _, _ = oracle.index(od, coords)
+    oks, ovs = oracle.summaries(od, slot, oracle.rope_axial(od, coords, k), v)
+    ref = oracle.global_(od, coords, oracle.rope_axial(od, coords, q), oks, ovs)
+    assert_close(w, host(exact), ref, "exact softmax")
+    assert_close(w, host(fast), ref, "default softmax")
+
+
+def test_global_overflowing_scores_fall_back_per_query():
+    """Queries whose scores overflow exp2 without a maximum are redone by the
+    two-pass softmax: every query whose largest score (log2 units) is at
+    least 110 -- its denominator is then above 2^100 -- equals the forced
+    two-pass row bit for bit; ordinary rows keep the one-pass result; nothing
+    is non-finite."""
+    import geometry_aware_sparse_amd as gas
+    w = CASES[2]
+    coords, q, k, v, g = inputs(w)
+    big = np.zeros(w.N, bool)
+    big[::7] = True
+    q = q.copy()
+    q[:, big] *= 64.0  # scores far beyond 2^7 in log2 units for most of these tokens
+    d, od = desc_pair(w)
+    de = gas.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block, dtype=gas.PACK3D_BF16,
+                       exact_softmax=True)
+    dt = tdtype(w)
+    dc, dq = to_dev(coords, torch.int32), to_dev(q, dt)
+    geom, _, _, _ = gas.pack3d_index_build(d, dc)
+    ks, vs = gas.pack3d_block_summarize(d, geom, to_dev(k, dt), to_dev(v, dt))
+    fast = gas.pack3d_global_attn(d, geom, dc, dq, ks, vs)
+    exact = gas.pack3d_global_attn(de, geom, dc, dq, ks, vs)
+    assert torch.isfinite(fast.float()).all()
+    # largest score of every (b, i, h) in log2 units, from the oracle's values
+    slot, _, _ = oracle.index(od, coords)
+    oks, _ = oracle.summaries(od, slot, oracle.rope_axial(od, coords, k), v)
+    qr = oracle.rope_axial(od, coords, q)
+    smax = np.einsum("bnhd,bhmd->bnhm", qr, oks).max(axis=-1) * (np.log2(np.e) / np.sqrt(w.D))
+    must = torch.from_numpy(smax >= 110.0).to("cuda")
+    assert must.sum().item() > 100
+    f, e = fast.float(), exact.float()
+    assert torch.equal(f[must], e[must])
+    ordinary = torch.from_numpy(np.broadcast_to(~big[None, :, None], smax.shape).copy()).to("cuda")
+    assert (f[ordinary] - e[ordinary]).abs().max().item() < 2e-2
