@@ -14,7 +14,8 @@ from ._lib import (PACK3D_BF16, PACK3D_EXCL_NEIGHBOURHOOD_BLOCKS, PACK3D_EXCL_NO
 from .ops import (make_desc, pack3d_block_summarize, pack3d_forward, pack3d_geometry_bytes,
                   pack3d_geometry_layout, pack3d_global_attn, pack3d_index_build,
                   pack3d_local_attn, pack3d_mix, pack3d_num_summaries, pack3d_rope_coords,
-                  pack3d_workspace_bytes, slot_map_view)
+                  pack3d_workspace_bytes, slot_map_view, ksum_from_rows, ksum_shape,
+                  ksum_to_rows, vsum_from_rows, vsum_shape, vsum_to_rows)
 
 library()  # load now: no silent fallback when the HIP library is absent
 
@@ -25,4 +26,6 @@ __all__ = [
     "pack3d_block_summarize", "pack3d_forward", "pack3d_geometry_bytes", "pack3d_geometry_layout",
     "pack3d_global_attn", "pack3d_index_build", "pack3d_local_attn", "pack3d_mix",
     "pack3d_num_summaries", "pack3d_rope_coords", "pack3d_workspace_bytes", "slot_map_view",
+    "ksum_from_rows", "ksum_shape", "ksum_to_rows", "vsum_from_rows", "vsum_shape",
+    "vsum_to_rows",
 ]

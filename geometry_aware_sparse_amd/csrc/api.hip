@@ -65,8 +65,14 @@ size_t geometry_bytes(const Geo &g) {
   return align_up((size_t)g.table_off + (size_t)(g.Z + g.Y + g.X) * g.P * 8);
 }
 
-size_t summary_bytes(const Geo &g, int dtype) {
-  return align_up((size_t)g.B * g.H * g.M * g.D * elem_size(dtype));
+// k_sum [B, H, Mp/32, Dp/8, 32, 8] and v_sum [B, H, Mp/8, D, 8],
+// Mp = 32*ceil(M/32), Dp = 8*ceil(D/8)
+size_t ksum_bytes(const Geo &g, int dtype) {
+  return align_up((size_t)g.B * g.H * ((g.M + 31) / 32 * 32) * ((g.D + 7) / 8 * 8) *
+                  elem_size(dtype));
+}
+size_t vsum_bytes(const Geo &g, int dtype) {
+  return align_up((size_t)g.B * g.H * ((g.M + 31) / 32 * 32) * g.D * elem_size(dtype));
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PACK3D_OK : PACK3D_ERR_HIP; }
@@ -127,7 +133,7 @@ int pack3d_workspace_bytes(const pack3d_desc *desc, size_t *bytes) {
   if (!bytes) return PACK3D_ERR_INVALID_ARG;
   int rc = make_geo(desc, &g);
   if (rc) return rc;
-  *bytes = geometry_bytes(g) + 2 * summary_bytes(g, desc->dtype);
+  *bytes = geometry_bytes(g) + ksum_bytes(g, desc->dtype) + vsum_bytes(g, desc->dtype);
   return PACK3D_OK;
 }
 
@@ -206,8 +212,9 @@ int pack3d_forward(const pack3d_desc *desc, const int32_t *coords, const void *q
   int rc = make_geo(desc, &g);
   if (rc) return rc;
   if (!coords || !q || !k || !v || !gate || !o || !ws) return PACK3D_ERR_INVALID_ARG;
-  const size_t gbytes = geometry_bytes(g), sbytes = summary_bytes(g, desc->dtype);
-  if (ws_bytes < gbytes + 2 * sbytes) return PACK3D_ERR_WORKSPACE;
+  const size_t gbytes = geometry_bytes(g), kbytes = ksum_bytes(g, desc->dtype),
+               vbytes = vsum_bytes(g, desc->dtype);
+  if (ws_bytes < gbytes + kbytes + vbytes) return PACK3D_ERR_WORKSPACE;
   // shape support is decided before anything is enqueued
   {
     const bool mfma = desc->dtype == PACK3D_BF16 && desc->exclusion == PACK3D_EXCL_NONE &&
@@ -219,7 +226,7 @@ int pack3d_forward(const pack3d_desc *desc, const int32_t *coords, const void *q
   char *base = static_cast<char *>(ws);
   void *geom = base;
   void *ksum = base + gbytes;
-  void *vsum = base + gbytes + sbytes;
+  void *vsum = base + gbytes + kbytes;
   auto mark = [&](int idx) -> int {
     if (!stage_events) return PACK3D_OK;
     return hip_status(hipEventRecord(static_cast<hipEvent_t>(stage_events[idx]), s));

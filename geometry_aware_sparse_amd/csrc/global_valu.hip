@@ -36,7 +36,9 @@ __global__ __launch_bounds__(kNT) void k_global_valu(Geo g, const void *geom,
   const bool active = i < g.N;
   bool cok = false;  // off-grid coordinate: zero query, zero output row
   const float2 *tab = rope_table(geom, g);
-  const int64_t sbase = ((int64_t)b * g.H + h) * g.M * D;
+  const int Mp = (g.M + 31) / 32 * 32;
+  const int64_t kbase = ((int64_t)b * g.H + h) * (Mp / 32);  // k_sum [B,H,Mp/32,D/8,32,8]
+  const int64_t vbase = ((int64_t)b * g.H + h) * (Mp / 8);   // v_sum [B,H,Mp/8,D,8]
 
   float qv[D];
   int c3[3] = {0, 0, 0};
@@ -70,8 +72,9 @@ __global__ __launch_bounds__(kNT) void k_global_valu(Geo g, const void *geom,
     const int nm = min(kTS, g.M - m0);
     __syncthreads();
     for (int e = threadIdx.x; e < nm * D; e += kNT) {
-      sK[e] = to_f32(ks[sbase + (int64_t)m0 * D + e]);
-      sV[e] = to_f32(vs[sbase + (int64_t)m0 * D + e]);
+      const int m = m0 + e / D, d = e % D;
+      sK[e] = to_f32(ks[(((kbase + m / 32) * ((D + 7) / 8) + d / 8) * 32 + m % 32) * 8 + d % 8]);
+      sV[e] = to_f32(vs[((vbase + m / 8) * D + d) * 8 + m % 8]);
     }
     __syncthreads();
     float lg[kTS];

@@ -81,6 +81,52 @@ def pack3d_workspace_bytes(desc):
     return n.value
 
 
+def _mp(M):
+    return (M + 31) // 32 * 32
+
+
+def ksum_shape(desc, M=None):
+    """k_sum: [B, H, Mp/32, Dp/8, 32, 8], Mp = 32*ceil(M/32), Dp = 8*ceil(D/8);
+    key summary (m, d) at [b, h, m // 32, d // 8, m % 32, d % 8]."""
+    M = pack3d_num_summaries(desc) if M is None else M
+    return (desc.B, desc.H, _mp(M) // 32, (desc.D + 7) // 8, 32, 8)
+
+
+def vsum_shape(desc, M=None):
+    """v_sum: [B, H, Mp/8, D, 8]; value summary (m, d) at [b, h, m // 8, d, m % 8]."""
+    M = pack3d_num_summaries(desc) if M is None else M
+    return (desc.B, desc.H, _mp(M) // 8, desc.D, 8)
+
+
+def ksum_to_rows(ks, M, D):
+    """[B, H, Mp/32, Dp/8, 32, 8] -> [B, H, M, D]."""
+    B, H, M32, D8, _, _ = ks.shape
+    return ks.permute(0, 1, 2, 4, 3, 5).reshape(B, H, M32 * 32, D8 * 8)[:, :, :M, :D].contiguous()
+
+
+def ksum_from_rows(k_rows):
+    """[B, H, M, D] -> [B, H, Mp/32, Dp/8, 32, 8], zero padding."""
+    B, H, M, D = k_rows.shape
+    Dp = (D + 7) // 8 * 8
+    pad = k_rows.new_zeros((B, H, _mp(M), Dp))
+    pad[:, :, :M, :D] = k_rows
+    return pad.view(B, H, _mp(M) // 32, 32, Dp // 8, 8).permute(0, 1, 2, 4, 3, 5).contiguous()
+
+
+def vsum_to_rows(vs, M):
+    """[B, H, Mp/8, D, 8] -> [B, H, M, D]."""
+    B, H, M8, D, _ = vs.shape
+    return vs.permute(0, 1, 2, 4, 3).reshape(B, H, M8 * 8, D)[:, :, :M].contiguous()
+
+
+def vsum_from_rows(v_rows):
+    """[B, H, M, D] -> [B, H, Mp/8, D, 8], zero past M."""
+    B, H, M, D = v_rows.shape
+    pad = v_rows.new_zeros((B, H, _mp(M), D))
+    pad[:, :, :M] = v_rows
+    return pad.view(B, H, _mp(M) // 8, 8, D).permute(0, 1, 2, 4, 3).contiguous()
+
+
 def slot_map_view(desc, geom):
     """The int32 slot map inside a geometry buffer, as a tensor view."""
     so, _, _ = pack3d_geometry_layout(desc)
@@ -119,8 +165,8 @@ def pack3d_block_summarize(desc, geom, k, v):
     _need(k, "k", desc, _bnhd(desc))
     _need(v, "v", desc, _bnhd(desc))
     M = pack3d_num_summaries(desc)
-    ks = torch.empty((desc.B, desc.H, M, desc.D), dtype=k.dtype, device=k.device)
-    vs = torch.empty_like(ks)
+    ks = torch.empty(ksum_shape(desc, M), dtype=k.dtype, device=k.device)
+    vs = torch.empty(vsum_shape(desc, M), dtype=k.dtype, device=k.device)
     _check(library().pack3d_block_summarize(C.byref(desc), _ptr(geom), _ptr(k), _ptr(v), _ptr(ks),
                                             _ptr(vs), _stream()), "pack3d_block_summarize")
     return ks, vs
@@ -140,8 +186,8 @@ def pack3d_global_attn(desc, geom, coords, q, ks, vs, out=None):
     _need(coords, "coords", desc, (desc.N, 3), torch.int32)
     _need(q, "q", desc, _bnhd(desc))
     M = pack3d_num_summaries(desc)
-    _need(ks, "k_sum", desc, (desc.B, desc.H, M, desc.D))
-    _need(vs, "v_sum", desc, (desc.B, desc.H, M, desc.D))
+    _need(ks, "k_sum", desc, ksum_shape(desc, M))
+    _need(vs, "v_sum", desc, vsum_shape(desc, M))
     out = torch.empty_like(q) if out is None else out
     _need(out, "out", desc, _bnhd(desc))
     _check(library().pack3d_global_attn(C.byref(desc), _ptr(geom), _ptr(coords), _ptr(q),

@@ -23,8 +23,16 @@
  *      coords                           : int32 [N, 3] = (z, y, x) of the
  *                                         token stored at each position; one
  *                                         packing shared by the whole batch
- *      k_sum, v_sum                     : [B, H, M, D], summaries in block-id
- *                                         order m = (mz*My + my)*Mx + mx
+ *      k_sum, v_sum                     : summaries of blocks in block-id
+ *                                         order m = (mz*My + my)*Mx + mx,
+ *                                         blocked for the matrix-core kernel,
+ *                                         with M padded to Mp = 32*ceil(M/32)
+ *                                         (padding slots are zero):
+ *        k_sum [B, H, Mp/32, Dp/8, 32, 8]: key summary (m, d) at
+ *                                         [b, h, m/32, d/8, m%32, d%8], with
+ *                                         D padded to Dp = 8*ceil(D/8) (zero)
+ *        v_sum [B, H, Mp/8, D, 8]       : value summary (m, d) at
+ *                                         [b, h, m/8, d, m%8]
  *    Element type of q/k/v/gate/o/x/k_sum/v_sum is desc->dtype.
  *  - stream is a hipStream_t passed as void* (NULL = default stream). Every
  *    call only enqueues work on it and returns; results are ready when the
@@ -186,8 +194,8 @@ int pack3d_global_attn(const pack3d_desc *desc, const void *geom, const int32_t 
 int pack3d_mix(const pack3d_desc *desc, const void *gate, const void *o_local,
                const void *o_global, void *o, void *stream);
 
-/* Workspace needed by pack3d_forward: the geometry metadata followed by the
- * two summary tensors, each 256-byte aligned. */
+/* Workspace needed by pack3d_forward: the geometry metadata followed by
+ * k_sum and v_sum, each 256-byte aligned. */
 int pack3d_workspace_bytes(const pack3d_desc *desc, size_t *bytes);
 
 /* The whole forward, stream-ordered: index build, summaries, global branch

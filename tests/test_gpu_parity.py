@@ -79,8 +79,16 @@ def test_block_summarize(w):
     ks, vs = gas.pack3d_block_summarize(d, geom, dev["k"], dev["v"])
     slot, _, _ = oracle.index(od, coords)
     oks, ovs = oracle.summaries(od, slot, oracle.rope_axial(od, coords, k), v)
-    assert_close(w, host(ks), oks, "k_sum")
-    assert_close(w, host(vs), ovs, "v_sum")
+    M = oks.shape[2]
+    assert_close(w, host(gas.ksum_to_rows(ks, M, w.D)), oks, "k_sum")
+    assert_close(w, host(gas.vsum_to_rows(vs, M)), ovs, "v_sum")
+    # padding slots of the blocked layouts are zero
+    Mp, Dp = (M + 31) // 32 * 32, (w.D + 7) // 8 * 8
+    krows = ks.permute(0, 1, 2, 4, 3, 5).reshape(w.B, w.H, Mp, Dp)
+    assert torch.count_nonzero(krows[:, :, :, w.D:]).item() == 0
+    vrows = vs.permute(0, 1, 2, 4, 3).reshape(w.B, w.H, Mp, w.D)
+    assert torch.count_nonzero(krows[:, :, M:]).item() == 0
+    assert torch.count_nonzero(vrows[:, :, M:]).item() == 0
 
 
 @pytest.mark.parametrize("w", CASES, ids=IDS)
@@ -106,7 +114,9 @@ def test_global_attn(w):
     assert_close(w, host(og), ref, "global")
     # ... and from the oracle's summaries rounded to the working dtype
     dt = tdtype(w)
-    og2 = gas.pack3d_global_attn(d, geom, dev["coords"], dev["q"], to_dev(oks, dt), to_dev(ovs, dt))
+    og2 = gas.pack3d_global_attn(d, geom, dev["coords"], dev["q"],
+                                 gas.ksum_from_rows(to_dev(oks, dt)),
+                                 gas.vsum_from_rows(to_dev(ovs, dt)))
     assert_close(w, host(og2), ref, "global(oracle summaries)")
 
 
