@@ -146,27 +146,28 @@ __global__ __launch_bounds__(TZ *TY *TX) void k_local(Geo g, const void *geom, c
   }
 }
 
-// bf16 variant for head dims that are multiples of 16: two lanes per query,
-// each owning half of the channels. Dot products use v_dot2_f32_bf16 on
-// packed pairs (the rotated, scaled query is rounded to bf16), the two halves
-// meet through one lane swap per neighbour, and the value sum pairs
-// neighbours (k, k+1) so that one v_dot2 accumulates two neighbours for one
-// channel. Halves the per-lane registers of the one-lane-per-query kernel, so
-// four waves per SIMD stay resident.
+// bf16 variant for head dims that are multiples of 48: LPQ = D/24 lanes per
+// query, each owning 24 consecutive channels. Dot products use
+// v_dot2_f32_bf16 on packed pairs (the rotated, scaled query is rounded to
+// bf16) and the lanes of a query meet through DPP lane swaps; the value sum
+// pairs neighbours (k, k+1) so that one v_dot2 accumulates two neighbours
+// for one channel, the pairs being formed with v_perm_b32.
 template <int D, int TZ, int TY, int TX>
-__global__ __launch_bounds__(2 * TZ *TY *TX) void k_local_pair(
+__global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_local_pair(
     Geo g, const void *geom, const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const bf16 *__restrict__ v, const bf16 *gate, const bf16 *oglob, bf16 *out, int ntz, int nty,
     int ntx) {
   constexpr int HZ = TZ + 2, HY = TY + 2, HX = TX + 2, NH = HZ * HY * HX, NQ = TZ * TY * TX;
-  constexpr int NT = 2 * NQ;
+  constexpr int LPQ = D / 24;          // lanes per query
+  constexpr int NT = LPQ * NQ;
   constexpr int DA = D / 3;
-  constexpr int DH = D / 2;            // channels per lane
+  constexpr int DH = 24;               // channels per lane
   constexpr int PITCH = D;             // LDS row pitch (elements), 16-byte aligned rows
-  static_assert(D % 16 == 0 && DA % 8 == 0, "head dim must be a multiple of 48");
+  static_assert(D % 48 == 0 && (LPQ == 2 || LPQ == 4), "head dim 48 or 96");
   __shared__ __attribute__((aligned(16))) bf16 sK[NH * PITCH];
   __shared__ __attribute__((aligned(16))) bf16 sV[NH * PITCH];
   __shared__ int sSlot[NH];
+  __shared__ float2 sCS[(HZ + HY + HX) * (D / 6)];  // (cos, sin) of the box's coordinates
 
   const int ntiles = ntz * nty * ntx;
   const int w = xcd_remap(blockIdx.x, gridDim.x);
@@ -177,6 +178,24 @@ __global__ __launch_bounds__(2 * TZ *TY *TX) void k_local_pair(
   const int32_t *slot = slot_map(geom, g);
   const float2 *tab = rope_table(geom, g);
   const int64_t bN = (int64_t)b * g.N;
+  constexpr int P = D / 6;
+  // rotation table rows of the box's coordinate range (clamped at the grid;
+  // off-grid rows are never used)
+  for (int e = threadIdx.x; e < (HZ + HY + HX) * P; e += NT) {
+    const int row = e / P, p = e % P;
+    int a, c;
+    if (row < HZ) { a = 0; c = z0 - 1 + row; }
+    else if (row < HZ + HY) { a = 1; c = y0 - 1 + row - HZ; }
+    else { a = 2; c = x0 - 1 + row - HZ - HY; }
+    const int dim = a == 0 ? g.Z : (a == 1 ? g.Y : g.X);
+    sCS[e] = rope_cs(tab, g, a, min(max(c, 0), dim - 1), p);
+  }
+  // local (cos, sin): axis a at box-relative coordinate rc (0 = one before the box)
+  auto cs_at = [&](int a, int rc, int p) {
+    const int base = a == 0 ? 0 : (a == 1 ? HZ : HZ + HY);
+    return sCS[(base + rc) * P + p];
+  };
+  __syncthreads();
 
   // Stage K~ (rotated, bf16) and V of the halo box, 8 channels per step.
   for (int e = threadIdx.x; e < NH * (D / 8); e += NT) {
@@ -191,12 +210,12 @@ __global__ __launch_bounds__(2 * TZ *TY *TX) void k_local_pair(
       const int64_t off = ((bN + j) * g.H + h) * D + ch * 8;
       const bf16x8 kr = *reinterpret_cast<const bf16x8 *>(k + off);
       vo = *reinterpret_cast<const bf16x8 *>(v + off);
-      const int c3[3] = {z, y, x};
+      const int rc3[3] = {hz, hy, hx};
       const int a = (ch * 8) / DA, p0 = ((ch * 8) % DA) / 2;
 #pragma unroll
       for (int u = 0; u < 4; u++) {
         float k0 = (float)kr[2 * u], k1 = (float)kr[2 * u + 1];
-        rotate(k0, k1, rope_cs(tab, g, a, c3[a], p0 + u));
+        rotate(k0, k1, cs_at(a, rc3[a], p0 + u));
         ko[2 * u] = (bf16)k0;
         ko[2 * u + 1] = (bf16)k1;
       }
@@ -209,28 +228,40 @@ __global__ __launch_bounds__(2 * TZ *TY *TX) void k_local_pair(
   }
   __syncthreads();
 
-  const int qn = threadIdx.x >> 1, hh = threadIdx.x & 1;
+  const int qn = threadIdx.x / LPQ, hh = threadIdx.x % LPQ;
   const int tz = qn / (TY * TX), ty = (qn / TX) % TY, tx = qn % TX;
   const int qs = ((tz + 1) * HY + (ty + 1)) * HX + (tx + 1);
-  const int i = sSlot[qs];  // both lanes of a query see the same value
+  const int i = sSlot[qs];  // all lanes of a query see the same value
   if (i < 0) return;
-  const int c3[3] = {z0 + tz, y0 + ty, x0 + tx};
   const float qscale = g.scale * kLog2e;
   const int64_t off = ((bN + i) * g.H + h) * D + hh * DH;
 
   bf16x2 qp[DH / 2];
+  {
+    const int rc3[3] = {tz + 1, ty + 1, tx + 1};
 #pragma unroll
-  for (int c8 = 0; c8 < DH / 8; c8++) {
-    const bf16x8 raw = *reinterpret_cast<const bf16x8 *>(q + off + 8 * c8);
-    const int d0 = hh * DH + 8 * c8, a = d0 / DA, p0 = (d0 % DA) / 2;
+    for (int c8 = 0; c8 < DH / 8; c8++) {
+      const bf16x8 raw = *reinterpret_cast<const bf16x8 *>(q + off + 8 * c8);
+      const int d0 = hh * DH + 8 * c8, a = d0 / DA, p0 = (d0 % DA) / 2;
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-      float x0v = (float)raw[2 * u], x1v = (float)raw[2 * u + 1];
-      rotate(x0v, x1v, rope_cs(tab, g, a, c3[a], p0 + u));
-      qp[4 * c8 + u][0] = (bf16)(x0v * qscale);
-      qp[4 * c8 + u][1] = (bf16)(x1v * qscale);
+      for (int u = 0; u < 4; u++) {
+        float x0v = (float)raw[2 * u], x1v = (float)raw[2 * u + 1];
+        rotate(x0v, x1v, cs_at(a, rc3[a], p0 + u));
+        qp[4 * c8 + u][0] = (bf16)(x0v * qscale);
+        qp[4 * c8 + u][1] = (bf16)(x1v * qscale);
+      }
     }
   }
+
+  // sum over the LPQ lanes of a query (adjacent lanes) with DPP swaps
+  auto lane_sum = [&](float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xf,
+                                                            0xf, false));  // quad_perm 1,0,3,2
+    if constexpr (LPQ == 4)
+      x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E,
+                                                              0xf, 0xf, false));  // 2,3,0,1
+    return x;
+  };
 
   // logits (log2 units) in canonical offset order k = (dz+1)*9 + (dy+1)*3 + dx+1
   float lg[27];
@@ -242,7 +273,7 @@ __global__ __launch_bounds__(2 * TZ *TY *TX) void k_local_pair(
     float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < DH / 2; j++) acc = __builtin_amdgcn_fdot2_f32_bf16(qp[j], kr[j], acc, false);
-    acc += __shfl_xor(acc, 1);
+    acc = lane_sum(acc);
     lg[kk] = sSlot[hs] >= 0 ? acc : -INFINITY;
     mx = fmaxf(mx, lg[kk]);
   }
@@ -271,7 +302,9 @@ __global__ __launch_bounds__(2 * TZ *TY *TX) void k_local_pair(
 #pragma unroll
     for (int j = 0; j < DH / 2; j++) {
       const uint32_t a = A[j], bb = Bv[j];
-      const uint32_t lo = (a & 0xffffu) | (bb << 16), hi2 = (a >> 16) | (bb & 0xffff0000u);
+      // (a.lo, b.lo) and (a.hi, b.hi)
+      const uint32_t lo = __builtin_amdgcn_perm(bb, a, 0x05040100u);
+      const uint32_t hi2 = __builtin_amdgcn_perm(bb, a, 0x07060302u);
       o[2 * j] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2, lo), o[2 * j], false);
       o[2 * j + 1] =
           __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2, hi2), o[2 * j + 1], false);
@@ -321,7 +354,7 @@ hipError_t run_local_pair(const Geo &g, const void *geom, const void *q, const v
                           hipStream_t s) {
   const int ntz = (g.Z + TZ - 1) / TZ, nty = (g.Y + TY - 1) / TY, ntx = (g.X + TX - 1) / TX;
   const int64_t nwg = (int64_t)g.B * ntz * nty * ntx * g.H;
-  hipLaunchKernelGGL((k_local_pair<D, TZ, TY, TX>), dim3((unsigned)nwg), dim3(2 * TZ * TY * TX), 0,
+  hipLaunchKernelGGL((k_local_pair<D, TZ, TY, TX>), dim3((unsigned)nwg), dim3((D / 24) * TZ * TY * TX), 0,
                      s, g, geom, static_cast<const bf16 *>(q), static_cast<const bf16 *>(k),
                      static_cast<const bf16 *>(v), static_cast<const bf16 *>(gate),
                      static_cast<const bf16 *>(og), static_cast<bf16 *>(out), ntz, nty, ntx);
@@ -340,7 +373,7 @@ hipError_t launch_local(const Geo &g, int dtype, const void *geom, const void *q
       case 12: return run_local<bf16, 12, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
       case 24: return run_local<bf16, 24, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
       case 48: return run_local_pair<48, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
-      case 96: return run_local_pair<96, 2, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
+      case 96: return run_local_pair<96, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
     }
   } else {
     switch (g.D) {

@@ -2,181 +2,160 @@
 // project page Ch. 3 "Rotate first, then pool"; paper summary §3.2, §B.5).
 //
 // One workgroup per (group of 8 consecutive summaries, batch); the summary
-// count is padded to Mp = 32*ceil(M/32) and padding slots are written as 0. For each of
-// its blocks the workgroup stages the members' memory positions (slot map
-// lookups in canonical within-block-slot order) in LDS, then every thread
-// accumulates its channel pair of the members' contiguous [H, D] rows in
-// fp32, in that order -- so the summaries are the same bits under any
-// packing of the tokens. HBM-bound: every K and V element is read once.
+// count is padded to Mp = 32*ceil(M/32) and padding slots are written as 0.
+// The workgroup stages the members' memory positions (slot map lookups in
+// canonical within-block-slot order) in LDS; a thread owns one block of the
+// group and one chunk of CW channels of the token's contiguous [H, D] row,
+// and accumulates the members in fp32 in that order -- so the summaries are
+// the same bits under any packing of the tokens. HBM-bound: every K and V
+// element is read once, with 16-byte loads.
 //
 // Outputs, both blocked so that the matrix-core kernel streams them with
 // contiguous 16-byte-per-lane loads:
 //   k_sum [B, H, Mp/32, Dp/8, 32, 8]: element (m, d) at [b, h, m/32, d/8, m%32, d%8]
 //                                   (Dp = 8*ceil(D/8); padding channels are 0)
 //   v_sum [B, H, Mp/8, D, 8]:        element (m, d) at [b, h, m/8, d, m%8]
-// Holding 8 consecutive summaries per workgroup makes every v_sum write a
-// full 16-byte chunk.
+// The v_sum means pass through LDS so that each (channel, group) is written
+// as one 16-byte chunk.
 #include "launch.hpp"
 
 namespace pk {
 
-constexpr int kMaxVol = 512;  // members staged in LDS per pass
+constexpr int kMaxMembers = 512;  // member slots staged in LDS per pass (8 blocks)
 
-template <typename T>
-__global__ __launch_bounds__(256) void k_summarize(Geo g, const void *geom, const T *k,
+template <typename T, int CW>
+__global__ __launch_bounds__(512) void k_summarize(Geo g, const void *geom, const T *k,
                                                    const T *v, T *ks, T *vsb) {
-  __shared__ int s_slot[kMaxVol];
+  __shared__ int s_slot[kMaxMembers];
+  extern __shared__ float s_vt[];  // [H*D][8] value means for the transposed write
   const int g8 = blockIdx.x, b = blockIdx.y;
   const int Mp = (g.M + 31) / 32 * 32;
   const int Dp = (g.D + 7) / 8 * 8;
   const int32_t *slot = slot_map(geom, g);
   const float2 *tab = rope_table(geom, g);
-  const int half = g.D / 2, da = g.D / 3, npair = g.H * half;
-  // Each thread keeps up to 2 channel pairs (npair <= 2 * blockDim.x) for
-  // the 8 blocks of its group.
-  float ka[2][8][2], va[2][8][2];
-  int cnt[8];
-#pragma unroll
-  for (int u = 0; u < 2; u++)
-#pragma unroll
-    for (int s = 0; s < 8; s++) ka[u][s][0] = ka[u][s][1] = va[u][s][0] = va[u][s][1] = 0.f;
+  const int da = g.D / 3;
+  const int NC = g.H * g.D / CW;        // channel chunks per token row
+  const int CPT = blockDim.x / 8;       // chunk lanes per block
+  const int s = threadIdx.x / CPT;      // block of the group owned by this thread
+  const int c0 = threadIdx.x % CPT;
+  const int m = 8 * g8 + s;
+  const int mz = m / (g.My * g.Mx), my = (m / g.Mx) % g.My, mx = m % g.Mx;
+  const int o3[3] = {mz * g.bz, my * g.by, mx * g.bx};
+  const int64_t bh0 = (int64_t)b * g.H;
 
-  auto origin = [&](int m, int *o) {
-    o[0] = (m / (g.My * g.Mx)) * g.bz;
-    o[1] = ((m / g.Mx) % g.My) * g.by;
-    o[2] = (m % g.Mx) * g.bx;
-  };
-  auto member_slot = [&](int m, int rr) {
-    int o[3];
-    origin(m, o);
-    const int z = o[0] + rr / (g.by * g.bx), y = o[1] + (rr / g.bx) % g.by, x = o[2] + rr % g.bx;
-    return (z < g.Z && y < g.Y && x < g.X) ? slot[site_of(g, z, y, x)] : -1;
-  };
-  // adds member rr (memory position j) of block m into accumulator s
-  auto accumulate = [&](int s, int m, int rr, int j) {
-    int o[3];
-    origin(m, o);
-    const int c3[3] = {o[0] + rr / (g.by * g.bx), o[1] + (rr / g.bx) % g.by, o[2] + rr % g.bx};
-    const int64_t row = ((int64_t)b * g.N + j) * g.H * g.D;
+  // members of all 8 blocks, in passes of kMaxMembers / 8 per block
+  const int per = kMaxMembers / 8;
+  // every thread runs the same number of rounds (the barriers below need it)
+  const int rounds = (NC + CPT - 1) / CPT;  // usually 1
+  for (int rd = 0; rd < rounds; rd++) {
+    const int c = c0 + rd * CPT;
+    const bool act = c < NC;
+    const int h = act ? (c * CW) / g.D : 0, d0 = act ? (c * CW) % g.D : 0;
+    float ka[CW], va[CW];
 #pragma unroll
-    for (int u = 0; u < 2; u++) {
-      const int t = threadIdx.x + u * blockDim.x;
-      if (t < npair) {
-        const int h = t / half, d0 = 2 * (t % half);
-        const int a = d0 / da, p = (d0 % da) / 2;
-        const T *kp = k + row + h * g.D + d0;
-        const T *vp = v + row + h * g.D + d0;
-        float k0 = to_f32(kp[0]), k1 = to_f32(kp[1]);
-        rotate(k0, k1, rope_cs(tab, g, a, c3[a], p));
-#pragma unroll
-        for (int ss = 0; ss < 8; ss++)
-          if (ss == s) {
-            ka[u][ss][0] += k0;
-            ka[u][ss][1] += k1;
-            va[u][ss][0] += to_f32(vp[0]);
-            va[u][ss][1] += to_f32(vp[1]);
-          }
+    for (int u = 0; u < CW; u++) ka[u] = va[u] = 0.f;
+    int cnt = 0;
+    for (int r0 = 0; r0 < g.vol; r0 += per) {
+      const int nr = min(per, g.vol - r0);
+      __syncthreads();
+      for (int e = threadIdx.x; e < 8 * nr; e += blockDim.x) {
+        const int ss = e / nr, rr = r0 + e % nr, mm = 8 * g8 + ss;
+        int j = -1;
+        if (mm < g.M) {
+          const int z = (mm / (g.My * g.Mx)) * g.bz + rr / (g.by * g.bx);
+          const int y = ((mm / g.Mx) % g.My) * g.by + (rr / g.bx) % g.by;
+          const int x = (mm % g.Mx) * g.bx + rr % g.bx;
+          if (z < g.Z && y < g.Y && x < g.X) j = slot[site_of(g, z, y, x)];
+        }
+        s_slot[e] = j;
       }
-    }
-  };
-
-#pragma unroll
-  for (int s = 0; s < 8; s++) cnt[s] = 0;
-  if (8 * g.vol <= kMaxVol) {
-    // stage the members of all 8 blocks at once
-    for (int idx = threadIdx.x; idx < 8 * g.vol; idx += blockDim.x) {
-      const int m = 8 * g8 + idx / g.vol;
-      s_slot[idx] = m < g.M ? member_slot(m, idx % g.vol) : -1;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 8; s++) {
-      const int m = 8 * g8 + s;
+      __syncthreads();
 #pragma unroll 4
-      for (int r = 0; r < g.vol; r++) {
-        const int j = s_slot[s * g.vol + r];
-        if (j < 0) continue;
-        cnt[s]++;
-        accumulate(s, m, r, j);
-      }
-    }
-  } else {
-    // large blocks: one block at a time, members in chunks
+      for (int r = 0; r < nr; r++) {
+        const int j = s_slot[s * nr + r];
+        if (j < 0 || !act) continue;
+        cnt++;
+        const int rr = r0 + r;
+        const int c3[3] = {o3[0] + rr / (g.by * g.bx), o3[1] + (rr / g.bx) % g.by, o3[2] + rr % g.bx};
+        const int64_t off = (((int64_t)b * g.N + j) * g.H + h) * g.D + d0;
+        float kx[CW], vx[CW];
+        if constexpr (CW == 8 && sizeof(T) == 2) {
+          const bf16x8 kr = *reinterpret_cast<const bf16x8 *>(k + off);
+          const bf16x8 vr = *reinterpret_cast<const bf16x8 *>(v + off);
 #pragma unroll
-    for (int s = 0; s < 8; s++) {
-      const int m = 8 * g8 + s;
-      if (m >= g.M) continue;  // uniform
-      for (int r0 = 0; r0 < g.vol; r0 += kMaxVol) {
-        const int nr = min(kMaxVol, g.vol - r0);
-        __syncthreads();
-        for (int r = threadIdx.x; r < nr; r += blockDim.x) s_slot[r] = member_slot(m, r0 + r);
-        __syncthreads();
-        for (int r = 0; r < nr; r++) {
-          const int j = s_slot[r];
-          if (j < 0) continue;
-          cnt[s]++;
-          accumulate(s, m, r0 + r, j);
+          for (int u = 0; u < 8; u++) {
+            kx[u] = (float)kr[u];
+            vx[u] = (float)vr[u];
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < CW; u++) {
+            kx[u] = to_f32(k[off + u]);
+            vx[u] = to_f32(v[off + u]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < CW; u += 2) {
+          const int dd = d0 + u, a = dd / da;
+          rotate(kx[u], kx[u + 1], rope_cs(tab, g, a, c3[a], (dd % da) / 2));
+        }
+#pragma unroll
+        for (int u = 0; u < CW; u++) {
+          ka[u] += kx[u];
+          va[u] += vx[u];
         }
       }
     }
-  }
-
-#pragma unroll
-  for (int u = 0; u < 2; u++) {
-    const int t = threadIdx.x + u * blockDim.x;
-    if (t >= npair) continue;
-    const int h = t / half, d0 = 2 * (t % half);
+    if (!act) continue;
     // mean = sum / count (a division, as in the definition); empty -> 0
-    float km[8][2], vm[8][2];
+    const int64_t ko = ((((bh0 + h) * (Mp / 32) + m / 32) * (Dp / 8) + d0 / 8) * 32 + m % 32) * 8;
 #pragma unroll
-    for (int s = 0; s < 8; s++)
-#pragma unroll
-      for (int c = 0; c < 2; c++) {
-        km[s][c] = cnt[s] > 0 ? ka[u][s][c] / (float)cnt[s] : 0.0f;
-        vm[s][c] = cnt[s] > 0 ? va[u][s][c] / (float)cnt[s] : 0.0f;
-      }
-#pragma unroll
-    for (int s = 0; s < 8; s++) {
-      const int m = 8 * g8 + s;
-      const int64_t o =
-          (((((int64_t)b * g.H + h) * (Mp / 32) + m / 32) * (Dp / 8) + d0 / 8) * 32 + m % 32) * 8 +
-          d0 % 8;
-      ks[o] = from_f32<T>(km[s][0]);
-      ks[o + 1] = from_f32<T>(km[s][1]);
+    for (int u = 0; u < CW; u++) {
+      ks[ko + (d0 + u) % 8] = from_f32<T>(cnt > 0 ? ka[u] / (float)cnt : 0.0f);
+      s_vt[(h * g.D + d0 + u) * 8 + s] = cnt > 0 ? va[u] / (float)cnt : 0.0f;
     }
-    const int64_t vo = ((((int64_t)b * g.H + h) * (Mp / 8) + g8) * g.D + d0) * 8;
+  }
+  __syncthreads();
+  // v_sum: one 16-byte (bf16) chunk per (head, channel)
+  for (int e = threadIdx.x; e < g.H * g.D; e += blockDim.x) {
+    const int h = e / g.D, d = e % g.D;
+    T *dst = vsb + (((bh0 + h) * (Mp / 8) + g8) * g.D + d) * 8;
 #pragma unroll
-    for (int c = 0; c < 2; c++)
-#pragma unroll
-      for (int s = 0; s < 8; s++) vsb[vo + 8 * c + s] = from_f32<T>(vm[s][c]);
+    for (int u = 0; u < 8; u++) dst[u] = from_f32<T>(s_vt[e * 8 + u]);
   }
   // padding channels D..Dp of k_sum are zero
-  for (int t = threadIdx.x; t < g.H * (Dp - g.D); t += blockDim.x) {
-    const int h = t / (Dp - g.D), d = g.D + t % (Dp - g.D);
-#pragma unroll
-    for (int s = 0; s < 8; s++) {
-      const int m = 8 * g8 + s;
-      ks[(((((int64_t)b * g.H + h) * (Mp / 32) + m / 32) * (Dp / 8) + d / 8) * 32 + m % 32) * 8 +
-         d % 8] = from_f32<T>(0.0f);
-    }
+  for (int e = threadIdx.x; e < 8 * g.H * (Dp - g.D); e += blockDim.x) {
+    const int ss = e / (g.H * (Dp - g.D)), rem = e % (g.H * (Dp - g.D));
+    const int h = rem / (Dp - g.D), d = g.D + rem % (Dp - g.D), mm = 8 * g8 + ss;
+    ks[((((bh0 + h) * (Mp / 32) + mm / 32) * (Dp / 8) + d / 8) * 32 + mm % 32) * 8 + d % 8] =
+        from_f32<T>(0.0f);
   }
 }
 
+namespace {
+template <typename T, int CW>
+hipError_t run_summarize(const Geo &g, const void *geom, const void *k, const void *v, void *ks,
+                         void *vs, hipStream_t s) {
+  const int NC = g.H * g.D / CW;
+  const int cpt = NC < 64 ? NC : 64;  // chunk lanes per block
+  const size_t lds = (size_t)g.H * g.D * 8 * sizeof(float);
+  dim3 grid((unsigned)((g.M + 31) / 32 * 4), (unsigned)g.B);
+  hipLaunchKernelGGL((k_summarize<T, CW>), grid, dim3(8 * cpt), lds, s, g, geom,
+                     static_cast<const T *>(k), static_cast<const T *>(v), static_cast<T *>(ks),
+                     static_cast<T *>(vs));
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_summarize(const Geo &g, int dtype, const void *geom, const void *k,
                             const void *v, void *ks, void *vs, hipStream_t s) {
-  const int npair = g.H * g.D / 2;
-  const int threads = npair <= 256 ? ((npair + 63) / 64) * 64 : 256;
-  if (npair > 2 * threads) return hipErrorInvalidValue;  // host checks H*D <= 1024
-  dim3 grid((unsigned)((g.M + 31) / 32 * 4), (unsigned)g.B);
+  // host checks H*D <= 1024, so the transposition buffer stays within 32 KiB
+  const bool c8 = g.D % 8 == 0;
   if (dtype == PACK3D_BF16)
-    hipLaunchKernelGGL(k_summarize<bf16>, grid, dim3(threads), 0, s, g, geom,
-                       static_cast<const bf16 *>(k), static_cast<const bf16 *>(v),
-                       static_cast<bf16 *>(ks), static_cast<bf16 *>(vs));
-  else
-    hipLaunchKernelGGL(k_summarize<float>, grid, dim3(threads), 0, s, g, geom,
-                       static_cast<const float *>(k), static_cast<const float *>(v),
-                       static_cast<float *>(ks), static_cast<float *>(vs));
-  return hipGetLastError();
+    return c8 ? run_summarize<bf16, 8>(g, geom, k, v, ks, vs, s)
+              : run_summarize<bf16, 2>(g, geom, k, v, ks, vs, s);
+  return c8 ? run_summarize<float, 8>(g, geom, k, v, ks, vs, s)
+            : run_summarize<float, 2>(g, geom, k, v, ks, vs, s);
 }
 
 }  // namespace pk
