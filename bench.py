@@ -179,7 +179,9 @@ def main():
     gflops = work["global"]["flops"]
     g_s = stage_ms["global"] * 1e-3
     achieved = gflops / g_s / 1e12
-    roofline = {"bound": "mfma", "kernel": "k_global_mfma<48>", "achieved": round(achieved, 1),
+    kname = (f"k_global_mfma<{w.D}>" if w.dtype == "bf16" and w.D in (48, 96)
+             else "k_global_valu")
+    roofline = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 1),
                 "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4), "traffic": measured_traffic(),
                 "traffic_unit": "bytes/launch"}

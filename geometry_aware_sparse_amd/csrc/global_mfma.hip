@@ -8,11 +8,11 @@
 //
 // Layout of the work. A workgroup of 4 waves owns 64*G*4 consecutive tokens
 // (packed order) of one (batch, head); a wave owns 32*G of them as G groups
-// of 32 that share every LDS fragment read. Summary tiles of TS rows stream
-// through double-buffered LDS by direct global->LDS loads (16 bytes per
-// lane, no staging registers): the next tile is in flight while the current
-// one is used, one barrier per tile. Both tiles are stored chunk-major -- a
-// 16-byte chunk is 8 channels of one k_sum row, or one channel of 8
+// of 32 that share every LDS fragment read. Summary tiles stream through
+// double-buffered LDS by direct global->LDS loads (16 bytes per lane, no
+// staging registers, no branches), one barrier per tile, the next tile in
+// flight while the current one is used. Both tiles are stored chunk-major --
+// a 16-byte chunk is 8 channels of one k_sum row, or one channel of 8
 // consecutive v_sum rows -- laid out so that every fragment read of a
 // half-wave is one contiguous 512-byte run (no bank conflicts). Per
 // 32-summary sub-tile a wave computes the TRANSPOSED scores
@@ -21,9 +21,10 @@
 // are placed so that row r lands where the matrix core wants row r with bits
 // 2 and 3 swapped, which makes the score registers come out exactly in the
 // operand order of the next product O^T += Vsum^T * P^T: probabilities go
-// from registers straight into the matrix core. The products of sub-tile
-// n+1 are issued before the exponentials of sub-tile n so that the matrix
-// core and the vector unit overlap within one wave.
+// from registers straight into the matrix core. The sub-tiles run as a
+// three-stage software pipeline -- value products of sub-tile j, exp2 of
+// j+1, score products of j+2 in one step -- so that within a step no matrix
+// instruction waits on a vector one and the two units overlap.
 //
 // Softmax details. Scores are in log2 units (the query is pre-multiplied by
 // scale*log2(e)). Subtracting a running maximum only guards exp against
@@ -41,6 +42,8 @@
 // query's arithmetic depends only on its own row and the summaries, never on
 // which tokens share its tile, so a repack of the tokens permutes the output
 // bit for bit.
+#include <type_traits>
+
 #include "launch.hpp"
 
 namespace pk {
@@ -49,22 +52,33 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = 4;
 
+// 16 bytes of bf16 ones: the source of the value-tile row that makes the
+// matrix core return the softmax denominator. Read-only.
+__device__ __attribute__((aligned(16))) uint32_t g_ones[4] = {0x3F803F80u, 0x3F803F80u,
+                                                                 0x3F803F80u, 0x3F803F80u};
+
 __device__ __forceinline__ int swap23(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 typedef __attribute__((address_space(3))) void *lds_ptr;
 
-// Scheduling hint for one sub-tile body: alternate one matrix instruction
-// with four vector instructions so that a wave keeps issuing exp2/convert
-// work while its own products run (a wave issues in order; a run of matrix
-// instructions would otherwise stall it on the busy matrix pipe).
-#define SCHED_INTERLEAVE()                                        \
-  do {                                                            \
-    _Pragma("unroll") for (int _i = 0; _i < 14; _i++) {           \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          \
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);          \
-    }                                                             \
-  } while (0)
+// Scheduling hint for one pipeline step: the LDS fragment reads first, a
+// few vector instructions while they land, then one matrix instruction
+// followed by PER vector instructions (exp2 and bf16 packs), so that a wave
+// keeps issuing vector work while its own products run (a wave issues in
+// order; a run of matrix instructions would otherwise stall it on the busy
+// matrix pipe).
+template <int NDS, int NMF, int NVA>
+__device__ __forceinline__ void sched_step() {
+  constexpr int PER = NVA / NMF, LEAD = NVA - NMF * PER;
+  __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+  if constexpr (LEAD > 0) __builtin_amdgcn_sched_group_barrier(0x002, LEAD, 0);
+#pragma unroll
+  for (int i = 0; i < NMF; i++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);
+  }
+}
 }  // namespace
 
 // G = 32-query groups per wave; TS = summaries per LDS tile.
@@ -84,35 +98,27 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
   constexpr int NSUB = TS / 32;
   constexpr int KPARTS = TS / 64;        // 64-lane loads per k_sum chunk row
   constexpr int VPARTS = (DPAD + 63) / 64;
+  constexpr int VROWS = 64 * VPARTS;     // LDS rows per 8-summary group of a value tile
   constexpr int NKI = NCH * KPARTS, NVI = NJ8 * VPARTS;  // loads per tile
-  static_assert(D % 16 == 0 && DA % 8 == 0 && TS % 64 == 0, "shape");
+  static_assert(D % 16 == 0 && DA % 8 == 0 && (NSUB == 2 || NSUB == 4), "shape");
+  static_assert(NKI % kWaves == 0 && NVI % kWaves == 0, "loads split evenly over the waves");
   // Two LDS buffers per operand, as distinct objects: the compiler can then
   // tell the in-flight global->LDS loads into one buffer from the reads of
   // the other and does not wait for the loads before every read.
   __shared__ bf16x8 sK0[NCH * TS], sK1[NCH * TS];    // chunk (ch, pos): channels 8ch.., row at pos
-  __shared__ bf16x8 sV0[NJ8 * DPAD], sV1[NJ8 * DPAD];  // chunk (j8, d): channel d of rows 8j8..+7
+  __shared__ bf16x8 sV0[NJ8 * VROWS], sV1[NJ8 * VROWS];  // chunk (j8, d): channel d of rows 8j8..+7
 
   const int w = xcd_remap(blockIdx.x, gridDim.x);
   const int tile = w % ntiles;
   const int bh = w / ntiles;
   const int h = bh % g.H, b = bh / g.H;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int hi = lane >> 5;  // which half of the wave
   const int l32 = lane & 31;
   const int M32 = (g.M + 31) / 32;                       // summaries padded to Mp = 32*M32
   const int64_t kbase = ((int64_t)b * g.H + h) * M32;      // k_sum [B,H,M32,D/8,32,8]
   const int64_t vbase = ((int64_t)b * g.H + h) * M32 * 4;  // v_sum [B,H,Mp/8,D,8]
-
-  // value tiles start as zeros (rows past M are never loaded and must stay
-  // finite), with the all-ones spare row that yields the denominator
-  for (int e = threadIdx.x; e < NJ8 * DPAD; e += 256) {
-    const int d = e % DPAD;
-    bf16x8 c;
-#pragma unroll
-    for (int x = 0; x < 8; x++) c[x] = (bf16)((ONES && d == D) ? 1.0f : 0.0f);
-    sV0[e] = c;
-    sV1[e] = c;
-  }
 
   // Query fragments: lane holds channels 16c + 8*hi .. +7 of its query,
   // rotated at the token's own coordinate, scaled, rounded to bf16. A token
@@ -162,32 +168,6 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
     }
   }
 
-  // Direct global->LDS loads of tile ts into buffer bb: each 64-lane load
-  // writes 64 consecutive chunks; lanes whose row lies past M stay idle.
-  auto issue_tile = [&](int ts, bf16x8 *dK, bf16x8 *dV) {
-    const int m0 = ts * TS;
-    for (int i = wv; i < NKI + NVI; i += kWaves) {
-      if (i < NKI) {
-        // 64 lanes = two 32-summary groups; within a group the lane for LDS
-        // position p reads summary swap23(p): 512 contiguous bytes per half
-        const int ch = i / KPARTS, part = i % KPARTS;
-        const int g32 = m0 / 32 + 2 * part + hi;
-        if (g32 < M32)
-          __builtin_amdgcn_global_load_lds(
-              ks + (((kbase + g32) * NCH + ch) * 32 + swap23(l32)) * 8,
-              (lds_ptr)&dK[ch * TS + part * 64], 16, 0, 0);
-      } else {
-        const int iv = i - NKI;
-        const int j8 = iv / VPARTS, part = iv % VPARTS;
-        const int d = part * 64 + lane;
-        const int g8 = m0 / 8 + j8;
-        if (d < D && g8 < 4 * M32)
-          __builtin_amdgcn_global_load_lds(vsb + ((vbase + g8) * D + d) * 8,
-                                           (lds_ptr)&dV[j8 * DPAD + part * 64], 16, 0, 0);
-      }
-    }
-  };
-
   f32x16 acc[G][DT];
   float lsum[G];
 #pragma unroll
@@ -199,10 +179,12 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
     lsum[gi] = 0.f;
   }
   const f32x16 zero16 = {};
-  const int ntile_s = (g.M + TS - 1) / TS;
 
-  // S^T = Ksum * Q~^T from the k_sum fragments of one sub-tile
-  auto scores_from = [&](const bf16x8 *kf, f32x16 *s) {
+  // S^T = Ksum * Q~^T for the 32 summaries at row offset 32*pos of a k_sum tile
+  auto scores_from = [&](const bf16x8 *K, int pos, f32x16 *s) {
+    bf16x8 kf[KD];
+#pragma unroll
+    for (int c = 0; c < KD; c++) kf[c] = K[(2 * c + hi) * TS + 32 * pos + l32];
 #pragma unroll
     for (int c = 0; c < KD; c++)
 #pragma unroll
@@ -211,9 +193,8 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
                                                         0, 0);
   };
 
-  // Scores of summaries past M take no part (-inf). Applied when a sub-tile's
-  // scores are handed over, outside the block that overlaps the next
-  // products with this sub-tile's exp2, so that block has no branch in it.
+  // Scores of summaries at or past M take no part (-inf); a select, so
+  // whatever a stale LDS row held is discarded.
   auto mask_tail = [&](f32x16 *s, int mbase) {
     if (mbase + 32 > g.M) {
 #pragma unroll
@@ -226,89 +207,168 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
     }
   };
 
+  // Without a spare output row the denominator is summed on the vector unit,
+  // from the same bf16-rounded probabilities the value product uses (one
+  // v_dot2 per pair), so the weights applied sum to one.
+  bf16x2 ones2;
+  ones2[0] = ones2[1] = (bf16)1.0f;
+  auto sum_bf16 = [&](const bf16x8 (*pfr)[2], float *ls) {
+#pragma unroll
+    for (int gi = 0; gi < G; gi++)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; c2++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          bf16x2 pr2;
+          pr2[0] = pfr[gi][c2][2 * e];
+          pr2[1] = pfr[gi][c2][2 * e + 1];
+          ls[gi] = __builtin_amdgcn_fdot2_f32_bf16(pr2, ones2, ls[gi], false);
+        }
+  };
+
   // ---- fast path: p = exp2(s), no running maximum ----
   const bool force_exact = (g.flags & PACK3D_EXACT_SOFTMAX) != 0;  // uniform
   if (!force_exact) {
-    __syncthreads();  // value tiles initialised before any load lands
-    issue_tile(0, sK0, sV0);
+    // Three-stage software pipeline over 32-summary sub-tiles: step j issues
+    // the value products of sub-tile j, the exp2 of sub-tile j+1 and the
+    // score products of sub-tile j+2. The 14 (D = 48) matrix instructions of
+    // a step depend on none of its vector instructions, so the two streams
+    // interleave freely within one wave.
+    //
+    // Summaries reach LDS by direct global->LDS loads (16 bytes per lane, no
+    // staging registers), double-buffered: key tile k in buffer k&1, value
+    // tile v in buffer (v+1)&1. A key tile holds the NSUB
+    // sub-tiles [NSUB*k, NSUB*k + NSUB); a value tile is shifted two
+    // sub-tiles back, [NSUB*v - 2, NSUB*v + NSUB - 2), so that both switch
+    // tiles at the same step: the step j with (j + 2) % NSUB == 0 first reads
+    // key tile (j+2)/NSUB and value tile (j+2)/NSUB. One barrier at that
+    // step makes both visible, and at that point no wave reads the key and
+    // value tiles before them any more, so the loads of the following tiles
+    // go into those buffers right after it (NSUB steps ahead of their use).
+    const int S = (g.M + 31) / 32;                 // sub-tiles with summaries
+    const int IT = (S + 2 * NSUB - 1) / (2 * NSUB);  // iterations of 2*NSUB steps
+    // Every lane of every load is active, so the loads need no branches:
+    // lanes that would read past the summaries read the last group instead
+    // (those rows are masked to -inf, or multiplied by p = 0).
+    //
+    // k_sum tile kt: each 64-lane load covers two 32-summary groups; within a
+    // group the lane for LDS position p reads summary swap23(p), so every
+    // fragment read is one contiguous 512-byte run per half-wave.
+    auto issue_k = [&](int kt, bf16x8 *dK) {
+#pragma unroll
+      for (int r = 0; r < NKI / kWaves; r++) {
+        const int i = wv + kWaves * r;
+        const int ch = i / KPARTS, part = i % KPARTS;
+        const int g32 = min(kt * NSUB + 2 * part + hi, M32 - 1);
+        __builtin_amdgcn_global_load_lds(ks + (((kbase + g32) * NCH + ch) * 32 + swap23(l32)) * 8,
+                                         (lds_ptr)&dK[ch * TS + part * 64], 16, 0, 0);
+      }
+    };
+    // v_sum tile vt: LDS chunk (j8, d) = channel d of summaries 8*j8.. of the
+    // tile. Row D is all ones when it carries the denominator (from a 16-byte
+    // constant); the other rows past D repeat channel D-1 and only feed
+    // output rows that are dropped.
+    // The lane that loads row D takes the ones instead; the choice is a bit
+    // mask built once and kept opaque to the compiler, which would otherwise
+    // turn it into a branch around the loads.
+    static_assert(!ONES || VPARTS == 1, "the denominator row is in the first part");
+    uint32_t keep = (ONES && lane == D) ? 0u : ~0u;
+    asm volatile("" : "+v"(keep));
+    const uint64_t keep64 = ((uint64_t)keep << 32) | keep;
+    const uint64_t ones_bits = reinterpret_cast<uint64_t>(g_ones) & ~keep64;
+    auto issue_v = [&](int vt, bf16x8 *dV) {
+      const int g8base = 4 * (vt * NSUB - 2);
+#pragma unroll
+      for (int r = 0; r < NVI / kWaves; r++) {
+        const int i = wv + kWaves * r;
+        const int j8 = i / VPARTS, part = i % VPARTS;
+        const int d = part * 64 + lane;
+        const int g8 = min(max(g8base + j8, 0), 4 * M32 - 1);
+        const bf16 *src = vsb + ((vbase + g8) * D + min(d, D - 1)) * 8;
+        if constexpr (ONES)
+          src = reinterpret_cast<const bf16 *>((reinterpret_cast<uint64_t>(src) & keep64) | ones_bits);
+        __builtin_amdgcn_global_load_lds(src, (lds_ptr)&dV[j8 * VROWS + part * 64], 16, 0, 0);
+      }
+    };
+
+    issue_k(0, sK0);
+    issue_v(0, sV1);  // sub-tiles -2 .. NSUB-3 (only 0, 1 exist for NSUB = 4)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // Software pipeline over 32-summary sub-tiles: at sub-tile n the
-    // products of n+1 (fragments read one step ahead) and the value
-    // fragments of n are issued first, then the exp2 of n runs while the
-    // matrix core works, then the value products of n. At the last sub-tile
-    // of an LDS tile the barrier comes before the exp2, so the first products
-    // of the next tile overlap it too; every read of the old buffer has
-    // landed in registers before that barrier, after which the other waves
-    // may refill it.
-    bf16x8 kf[2][KD];
-    f32x16 s_cur[G], s_nxt[G];
+    issue_k(1, sK1);
+    issue_v(1, sV0);
+
+    f32x16 s[2][G];        // scores of sub-tiles j+1, j+2 (by parity)
+    bf16x8 pf[2][G][2];    // probabilities of sub-tiles j, j+1 (by parity)
+    scores_from(sK0, 0, s[0]);
+    mask_tail(s[0], 0);
+    scores_from(sK0, 1, s[1]);
 #pragma unroll
-    for (int c = 0; c < KD; c++) kf[0][c] = sK0[(2 * c + hi) * TS + l32];
-    scores_from(kf[0], s_cur);
-    mask_tail(s_cur, 0);
-    if (NSUB > 1) {
+    for (int gi = 0; gi < G; gi++)
 #pragma unroll
-      for (int c = 0; c < KD; c++) kf[1][c] = sK0[(2 * c + hi) * TS + 32 + l32];
-    }
-    auto run_tile = [&](int ts, const bf16x8 *cK, const bf16x8 *cV, bf16x8 *nK, bf16x8 *nV) {
-      const int m0 = ts * TS;
-      const bool more = ts + 1 < ntile_s;  // uniform; then this tile is full
-      if (more) issue_tile(ts + 1, nK, nV);
+      for (int j = 0; j < 16; j++) pf[0][gi][j >> 3][j & 7] = (bf16)__builtin_amdgcn_exp2f(s[0][gi][j]);
+    if constexpr (!ONES) sum_bf16(pf[0], lsum);
+
+    // one step; JJ = position in the 2*NSUB-step iteration (compile time)
+    auto step = [&](int it, auto jc, auto mc) {
+      constexpr int JJ = decltype(jc)::value;
+      constexpr bool MASK = decltype(mc)::value;  // some summary of sub-tile j+1 may be past M
+      constexpr int KT = (JJ + 2) / NSUB;  // key tile of sub-tile j+2, from 2*it
+      constexpr int KB = KT & 1;
+      constexpr int VB = (KT + 1) & 1;     // value tile of sub-tile j: 2*it + KT
+      constexpr int POS = (JJ + 2) % NSUB;
+      constexpr int P = JJ & 1;
+      const bf16x8 *cK = KB ? sK1 : sK0;
+      const bf16x8 *cV = VB ? sV1 : sV0;
+      const int j = 2 * NSUB * it + JJ;
+      if constexpr (POS == 0) {
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads landed, LDS reads done
+        __syncthreads();
+        issue_k(2 * it + KT + 1, KB ? sK0 : sK1);
+        issue_v(2 * it + KT + 1, KB ? sV1 : sV0);
+      }
+      if constexpr (MASK) mask_tail(s[P ^ 1], 32 * (j + 1));
+      bf16x8 vf[DT][2];
 #pragma unroll
-      for (int sub = 0; sub < NSUB; sub++) {
-        if (m0 + 32 * sub >= g.M) break;
-        const bool last = sub == NSUB - 1;
-        bf16x8 vf[DT][2];
+      for (int t = 0; t < DT; t++)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; c2++) vf[t][c2] = cV[(4 * POS + 2 * c2 + hi) * VROWS + 32 * t + l32];
+      scores_from(cK, POS, s[P]);
+#pragma unroll
+      for (int gi = 0; gi < G; gi++)
+#pragma unroll
+        for (int jr = 0; jr < 16; jr++)
+          pf[P ^ 1][gi][jr >> 3][jr & 7] = (bf16)__builtin_amdgcn_exp2f(s[P ^ 1][gi][jr]);
+      if constexpr (!ONES) sum_bf16(pf[P ^ 1], lsum);
+#pragma unroll
+      for (int gi = 0; gi < G; gi++)
 #pragma unroll
         for (int t = 0; t < DT; t++)
 #pragma unroll
-          for (int c2 = 0; c2 < 2; c2++) vf[t][c2] = cV[(4 * sub + 2 * c2 + hi) * DPAD + 32 * t + l32];
-        if (!last) {
-          scores_from(kf[(sub + 1) & 1], s_nxt);
-          if (sub + 2 < NSUB) {
-#pragma unroll
-            for (int c = 0; c < KD; c++) kf[sub & 1][c] = cK[(2 * c + hi) * TS + 32 * (sub + 2) + l32];
-          }
-        } else if (more) {
-          __builtin_amdgcn_s_waitcnt(0);  // next tile landed, old-buffer reads done
-          __syncthreads();
-#pragma unroll
-          for (int c = 0; c < KD; c++) kf[0][c] = nK[(2 * c + hi) * TS + l32];
-          scores_from(kf[0], s_nxt);
-          if (NSUB > 1) {
-#pragma unroll
-            for (int c = 0; c < KD; c++) kf[1][c] = nK[(2 * c + hi) * TS + 32 + l32];
-          }
-        }
-        bf16x8 pf[G][2];
-#pragma unroll
-        for (int gi = 0; gi < G; gi++) {
-#pragma unroll
-          for (int j = 0; j < 16; j++) {
-            const float p = __builtin_amdgcn_exp2f(s_cur[gi][j]);
-            if (!ONES) lsum[gi] += p;
-            pf[gi][j >> 3][j & 7] = (bf16)p;
-          }
-        }
-#pragma unroll
-        for (int gi = 0; gi < G; gi++)
-#pragma unroll
-          for (int t = 0; t < DT; t++)
-#pragma unroll
-            for (int c2 = 0; c2 < 2; c2++)
-              acc[gi][t] =
-                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t][c2], pf[gi][c2], acc[gi][t], 0, 0, 0);
-        SCHED_INTERLEAVE();
-#pragma unroll
-        for (int gi = 0; gi < G; gi++) s_cur[gi] = s_nxt[gi];
-        mask_tail(s_cur, last ? m0 + TS : m0 + 32 * (sub + 1));
+          for (int c2 = 0; c2 < 2; c2++)
+            acc[gi][t] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t][c2], pf[P][gi][c2], acc[gi][t], 0, 0, 0);
+      sched_step<KD + 2 * DT, G * (KD + 2 * DT), G * (ONES ? 24 : 32)>();
+    };
+    // Iterations before IT_CLEAN only see sub-tiles that lie wholly below M,
+    // so their steps carry no mask (and no branch that would split a step's
+    // matrix and vector streams); the last iteration(s) mask.
+    const int IT_CLEAN = min(IT, max(0, (g.M / 32 - 1) / (2 * NSUB)));
+    auto iteration = [&](int it, auto mc) {
+      step(it, std::integral_constant<int, 0>{}, mc);
+      step(it, std::integral_constant<int, 1>{}, mc);
+      step(it, std::integral_constant<int, 2>{}, mc);
+      step(it, std::integral_constant<int, 3>{}, mc);
+      if constexpr (NSUB == 4) {
+        step(it, std::integral_constant<int, 4>{}, mc);
+        step(it, std::integral_constant<int, 5>{}, mc);
+        step(it, std::integral_constant<int, 6>{}, mc);
+        step(it, std::integral_constant<int, 7>{}, mc);
       }
     };
-    for (int ts = 0; ts < ntile_s; ts += 2) {
-      run_tile(ts, sK0, sV0, sK1, sV1);
-      if (ts + 1 < ntile_s) run_tile(ts + 1, sK1, sV1, sK0, sV0);
-    }
+    int it = 0;
+    for (; it < IT_CLEAN; it++) iteration(it, std::false_type{});
+    for (; it < IT; it++) iteration(it, std::true_type{});
   }
 
   // denominator: spare row D (lanes 0..31, register 8 of the last tile), or
@@ -415,10 +475,10 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
       for (int j = 0; j < 16; j++) {
         const int r = (j >> 2) * 8 + hi * 4 + (j & 3);
         const float p = (m0 + swap23(r) < g.M) ? __builtin_amdgcn_exp2f(s[gi][j]) : 0.f;
-        if (!ONES) lsum[gi] += p;
         pf[gi][j >> 3][j & 7] = (bf16)p;
       }
     }
+    if constexpr (!ONES) sum_bf16(pf, lsum);
 #pragma unroll
     for (int t = 0; t < DT; t++) {
       const int d = 32 * t + l32;

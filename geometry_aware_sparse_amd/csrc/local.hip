@@ -278,13 +278,15 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_local_pair(
     mx = fmaxf(mx, lg[kk]);
   }
   float pr[28];
-  float den = 0.f;
 #pragma unroll
-  for (int kk = 0; kk < 27; kk++) {
+  for (int kk = 0; kk < 27; kk++)
     pr[kk] = __builtin_amdgcn_exp2f(lg[kk] - mx);  // exactly 0 for an invalid neighbour
-    den += pr[kk];
-  }
   pr[27] = 0.f;
+  // the weights are rounded to bf16 for the value products; the denominator
+  // sums the same rounded weights, so the weights used sum to one
+  float den = 0.f;
+  bf16x2 ones2;
+  ones2[0] = ones2[1] = (bf16)1.0f;
   float o[DH];
 #pragma unroll
   for (int d = 0; d < DH; d++) o[d] = 0.f;
@@ -297,6 +299,7 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_local_pair(
     bf16x2 pp;
     pp[0] = (bf16)pr[2 * kp];
     pp[1] = (bf16)pr[2 * kp + 1];
+    den = __builtin_amdgcn_fdot2_f32_bf16(pp, ones2, den, false);
     const uint32_t *A = reinterpret_cast<const uint32_t *>(sV + hs0 * PITCH + hh * DH);
     const uint32_t *Bv = reinterpret_cast<const uint32_t *>(sV + hs1 * PITCH + hh * DH);
 #pragma unroll
