@@ -12,6 +12,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// LDS destination of a direct global->LDS load
+typedef __attribute__((address_space(3))) void *lds_ptr;
 
 // Problem geometry, derived once on the host from pack3d_desc and passed to
 // kernels by value.

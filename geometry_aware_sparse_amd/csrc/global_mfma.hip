@@ -60,7 +60,6 @@ __device__ __attribute__((aligned(16))) uint32_t g_ones[4] = {0x3F803F80u, 0x3F8
 __device__ __forceinline__ int swap23(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
-typedef __attribute__((address_space(3))) void *lds_ptr;
 
 // Scheduling hint for one pipeline step: the LDS fragment reads first, a
 // few vector instructions while they land, then one matrix instruction

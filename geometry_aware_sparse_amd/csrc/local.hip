@@ -164,8 +164,14 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_local_pair(
   constexpr int DH = 24;               // channels per lane
   constexpr int PITCH = D;             // LDS row pitch (elements), 16-byte aligned rows
   static_assert(D % 48 == 0 && (LPQ == 2 || LPQ == 4), "head dim 48 or 96");
-  __shared__ __attribute__((aligned(16))) bf16 sK[NH * PITCH];
-  __shared__ __attribute__((aligned(16))) bf16 sV[NH * PITCH];
+  constexpr int CPS = D / 8;                // 16-byte chunks per staged row
+  constexpr int NCK = NH * CPS;             // chunks per staged tensor
+  constexpr int RS = (NCK + NT - 1) / NT;   // staging rounds per thread
+  // rows are PITCH = D apart, so chunk e of the halo is at element 8e; the
+  // arrays are padded to whole rounds so that every lane of every round has
+  // a place to write
+  __shared__ __attribute__((aligned(16))) bf16 sK[RS * NT * 8];
+  __shared__ __attribute__((aligned(16))) bf16 sV[RS * NT * 8];
   __shared__ int sSlot[NH];
   __shared__ float2 sCS[(HZ + HY + HX) * (D / 6)];  // (cos, sin) of the box's coordinates
 
@@ -179,69 +185,108 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_local_pair(
   const float2 *tab = rope_table(geom, g);
   const int64_t bN = (int64_t)b * g.N;
   constexpr int P = D / 6;
-  // rotation table rows of the box's coordinate range (clamped at the grid;
-  // off-grid rows are never used)
-  for (int e = threadIdx.x; e < (HZ + HY + HX) * P; e += NT) {
-    const int row = e / P, p = e % P;
-    int a, c;
-    if (row < HZ) { a = 0; c = z0 - 1 + row; }
-    else if (row < HZ + HY) { a = 1; c = y0 - 1 + row - HZ; }
-    else { a = 2; c = x0 - 1 + row - HZ - HY; }
-    const int dim = a == 0 ? g.Z : (a == 1 ? g.Y : g.X);
-    sCS[e] = rope_cs(tab, g, a, min(max(c, 0), dim - 1), p);
-  }
   // local (cos, sin): axis a at box-relative coordinate rc (0 = one before the box)
   auto cs_at = [&](int a, int rc, int p) {
     const int base = a == 0 ? 0 : (a == 1 ? HZ : HZ + HY);
     return sCS[(base + rc) * P + p];
   };
-  __syncthreads();
-
-  // Stage K~ (rotated, bf16) and V of the halo box, 8 channels per step.
-  for (int e = threadIdx.x; e < NH * (D / 8); e += NT) {
-    const int hs = e / (D / 8), ch = e % (D / 8);
-    const int hz = hs / (HY * HX), hy = (hs / HX) % HY, hx = hs % HX;
-    const int z = z0 - 1 + hz, y = y0 - 1 + hy, x = x0 - 1 + hx;
-    int j = -1;
-    if (z >= 0 && y >= 0 && x >= 0 && z < g.Z && y < g.Y && x < g.X) j = slot[site_of(g, z, y, x)];
-    if (ch == 0) sSlot[hs] = j;
-    bf16x8 ko, vo;
-    if (j >= 0) {
-      const int64_t off = ((bN + j) * g.H + h) * D + ch * 8;
-      const bf16x8 kr = *reinterpret_cast<const bf16x8 *>(k + off);
-      vo = *reinterpret_cast<const bf16x8 *>(v + off);
-      const int rc3[3] = {hz, hy, hx};
-      const int a = (ch * 8) / DA, p0 = ((ch * 8) % DA) / 2;
+  // Rotation table rows of the box's coordinate range (clamped at the grid;
+  // off-grid rows are never used) and the slots of the halo sites (-1 off
+  // the grid): all loads first, then the LDS writes, one barrier.
+  {
+    constexpr int NTAB = (HZ + HY + HX) * P;
+    constexpr int RT = (NTAB + NT - 1) / NT, RSL = (NH + NT - 1) / NT;
+    float2 tv[RT];
+    int sv[RSL];
 #pragma unroll
-      for (int u = 0; u < 4; u++) {
-        float k0 = (float)kr[2 * u], k1 = (float)kr[2 * u + 1];
-        rotate(k0, k1, cs_at(a, rc3[a], p0 + u));
-        ko[2 * u] = (bf16)k0;
-        ko[2 * u + 1] = (bf16)k1;
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < 8; u++) ko[u] = vo[u] = (bf16)0.0f;
+    for (int r = 0; r < RT; r++) {
+      const int e = (int)threadIdx.x + r * NT;
+      const int row = min(e, NTAB - 1) / P, p = min(e, NTAB - 1) % P;
+      int a, c;
+      if (row < HZ) { a = 0; c = z0 - 1 + row; }
+      else if (row < HZ + HY) { a = 1; c = y0 - 1 + row - HZ; }
+      else { a = 2; c = x0 - 1 + row - HZ - HY; }
+      const int dim = a == 0 ? g.Z : (a == 1 ? g.Y : g.X);
+      tv[r] = rope_cs(tab, g, a, min(max(c, 0), dim - 1), p);
     }
-    *reinterpret_cast<bf16x8 *>(&sK[hs * PITCH + ch * 8]) = ko;
-    *reinterpret_cast<bf16x8 *>(&sV[hs * PITCH + ch * 8]) = vo;
+#pragma unroll
+    for (int r = 0; r < RSL; r++) {
+      const int hs = min((int)threadIdx.x + r * NT, NH - 1);
+      const int hz = hs / (HY * HX), hy = (hs / HX) % HY, hx = hs % HX;
+      const int z = z0 - 1 + hz, y = y0 - 1 + hy, x = x0 - 1 + hx;
+      const bool on = z >= 0 && y >= 0 && x >= 0 && z < g.Z && y < g.Y && x < g.X;
+      const int j = slot[on ? site_of(g, z, y, x) : 0];
+      sv[r] = on ? j : -1;
+    }
+#pragma unroll
+    for (int r = 0; r < RT; r++)
+      if ((int)threadIdx.x + r * NT < NTAB) sCS[threadIdx.x + r * NT] = tv[r];
+#pragma unroll
+    for (int r = 0; r < RSL; r++)
+      if ((int)threadIdx.x + r * NT < NH) sSlot[threadIdx.x + r * NT] = sv[r];
   }
   __syncthreads();
 
+  // Every global load of the workgroup goes out before any is waited for:
+  // the raw K chunks into registers, the V chunks straight into LDS (16
+  // bytes per lane), this lane's query slice, and for the fused mix its
+  // slice of O_glob and the gate. A site off the grid reads token 0 instead:
+  // its logit is replaced by -inf and its weight is exactly 0, so only
+  // finiteness matters.
   const int qn = threadIdx.x / LPQ, hh = threadIdx.x % LPQ;
   const int tz = qn / (TY * TX), ty = (qn / TX) % TY, tx = qn % TX;
   const int qs = ((tz + 1) * HY + (ty + 1)) * HX + (tx + 1);
   const int i = sSlot[qs];  // all lanes of a query see the same value
+  const int wbase = __builtin_amdgcn_readfirstlane(threadIdx.x & ~63);
+  bf16x8 kraw[RS];
+#pragma unroll
+  for (int r = 0; r < RS; r++) {
+    const int e = min((int)threadIdx.x + r * NT, NCK - 1);
+    const int hs = e / CPS, ch = e % CPS;
+    const int64_t off = ((bN + max(sSlot[hs], 0)) * g.H + h) * D + ch * 8;
+    kraw[r] = *reinterpret_cast<const bf16x8 *>(k + off);
+    __builtin_amdgcn_global_load_lds(v + off, (lds_ptr)&sV[(wbase + r * NT) * 8], 16, 0, 0);
+  }
+  const int64_t off = ((bN + max(i, 0)) * g.H + h) * D + hh * DH;
+  bf16x8 qraw[DH / 8], ograw[DH / 8];
+  float gl = 0.f;
+#pragma unroll
+  for (int c8 = 0; c8 < DH / 8; c8++) qraw[c8] = *reinterpret_cast<const bf16x8 *>(q + off + 8 * c8);
+  if (gate) {
+#pragma unroll
+    for (int c8 = 0; c8 < DH / 8; c8++)
+      ograw[c8] = *reinterpret_cast<const bf16x8 *>(oglob + off + 8 * c8);
+    gl = (float)gate[(bN + max(i, 0)) * g.H + h];
+  }
+  // rotate the staged keys at their own coordinates
+#pragma unroll
+  for (int r = 0; r < RS; r++) {
+    const int e = (int)threadIdx.x + r * NT;
+    const int ec = min(e, NCK - 1);
+    const int hs = ec / CPS, ch = ec % CPS;
+    const int rc3[3] = {hs / (HY * HX), (hs / HX) % HY, hs % HX};
+    const int a = (ch * 8) / DA, p0 = ((ch * 8) % DA) / 2;
+    bf16x8 ko;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      float k0 = (float)kraw[r][2 * u], k1 = (float)kraw[r][2 * u + 1];
+      rotate(k0, k1, cs_at(a, rc3[a], p0 + u));
+      ko[2 * u] = (bf16)k0;
+      ko[2 * u + 1] = (bf16)k1;
+    }
+    *reinterpret_cast<bf16x8 *>(&sK[e * 8]) = ko;
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
+  __syncthreads();
   if (i < 0) return;
   const float qscale = g.scale * kLog2e;
-  const int64_t off = ((bN + i) * g.H + h) * D + hh * DH;
 
   bf16x2 qp[DH / 2];
   {
     const int rc3[3] = {tz + 1, ty + 1, tx + 1};
 #pragma unroll
     for (int c8 = 0; c8 < DH / 8; c8++) {
-      const bf16x8 raw = *reinterpret_cast<const bf16x8 *>(q + off + 8 * c8);
+      const bf16x8 raw = qraw[c8];
       const int d0 = hh * DH + 8 * c8, a = d0 / DA, p0 = (d0 % DA) / 2;
 #pragma unroll
       for (int u = 0; u < 4; u++) {
@@ -315,11 +360,10 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_local_pair(
   }
   const float inv = 1.0f / den;
   if (gate) {
-    const float gl = (float)gate[(bN + i) * g.H + h];
     const float gg = 1.0f / (1.0f + expf(-gl));
 #pragma unroll
     for (int c8 = 0; c8 < DH / 8; c8++) {
-      const bf16x8 og = *reinterpret_cast<const bf16x8 *>(oglob + off + 8 * c8);
+      const bf16x8 og = ograw[c8];
       bf16x8 r;
 #pragma unroll
       for (int u = 0; u < 8; u++)
