@@ -132,6 +132,158 @@ __global__ __launch_bounds__(512) void k_summarize(Geo g, const void *geom, cons
   }
 }
 
+// bf16 rows whose head dim is a multiple of 8: the same summaries (same
+// members, same order, same fp32 arithmetic), arranged so that memory
+// latency is paid a few times per workgroup instead of once per member.
+//   1. The members' slots and the RoPE rows of the 8 blocks' coordinate
+//      ranges are staged in LDS (one round of loads, one barrier).
+//   2. A thread owns one block and one 16-byte chunk of the token row; it
+//      issues the K and V loads of up to 8 members at once, then adds them
+//      up in within-block-slot order. A member that is absent reads token 0
+//      and contributes +0 through a select, which leaves the sum unchanged
+//      bit for bit.
+//   3. The value means are transposed through LDS with an odd row pitch, so
+//      the writes of a wave fall in distinct banks.
+constexpr int kBatch = 8;  // members whose loads are in flight together
+
+__global__ __launch_bounds__(512) void k_summarize_b8(Geo g, const void *geom, const bf16 *k,
+                                                       const bf16 *v, bf16 *ks, bf16 *vsb,
+                                                       int nrow) {
+  extern __shared__ float s_dyn[];
+  const int NC = g.H * g.D / 8;          // 16-byte chunks per token row
+  const int NT = 8 * NC;
+  const int per = min(g.vol, kMaxMembers / 8);  // members staged per pass and block
+  const int P = g.P;
+  int *s_slot = reinterpret_cast<int *>(s_dyn);                  // [8][per]
+  int *s_lc = s_slot + 8 * per;                                  // [per] packed (lz, ly, lx)
+  float2 *s_cs = reinterpret_cast<float2 *>(s_dyn + 8 * per + per + ((9 * per) & 1));  // [8][nrow][P]
+  float *s_vt = reinterpret_cast<float *>(s_cs + 8 * nrow * P);  // [8][NC][9]
+  const int g8 = blockIdx.x, b = blockIdx.y;
+  const int Mp = (g.M + 31) / 32 * 32;
+  const int32_t *slot = slot_map(geom, g);
+  const float2 *tab = rope_table(geom, g);
+  const int s = threadIdx.x / NC;        // block of the group owned by this thread
+  const int c = threadIdx.x - s * NC;    // chunk of the token row
+  const int h = (c * 8) / g.D, d0 = c * 8 - h * g.D;
+  const int DA = g.D / 3;
+  const int a = d0 / DA, p0 = (d0 - a * DA) / 2;
+  const int m = 8 * g8 + s;
+  // origin of block 8*g8 + ss (block-raster order), for every ss, computed
+  // from the group's first block once (wave-uniform)
+  const int m0 = 8 * g8;
+  const int MyMx = g.My * g.Mx;
+  int oz[8], oy[8], ox[8];
+  {
+    int mz = m0 / MyMx, rem = m0 - mz * MyMx;
+    int my = rem / g.Mx, mx = rem - my * g.Mx;
+#pragma unroll
+    for (int ss = 0; ss < 8; ss++) {
+      oz[ss] = mz * g.bz;
+      oy[ss] = my * g.by;
+      ox[ss] = mx * g.bx;
+      const bool wx = mx + 1 == g.Mx;  // carry into y, then z (selects, no branches)
+      const bool wy = wx && my + 1 == g.My;
+      mx = wx ? 0 : mx + 1;
+      my = wy ? 0 : (wx ? my + 1 : my);
+      mz = wy ? mz + 1 : mz;
+    }
+  }
+  // RoPE rows of every block of the group: row (ss, axis, local coordinate)
+  for (int t = threadIdx.x; t < nrow * P; t += NT) {
+    const int row = t / P, pp = t - row * P;
+    const int aa = row < g.bz ? 0 : (row < g.bz + g.by ? 1 : 2);
+    const int lc = row - (aa == 0 ? 0 : (aa == 1 ? g.bz : g.bz + g.by));
+    const int dim = aa == 0 ? g.Z : (aa == 1 ? g.Y : g.X);
+    float2 cs[8];
+#pragma unroll
+    for (int ss = 0; ss < 8; ss++) {
+      const int o = aa == 0 ? oz[ss] : (aa == 1 ? oy[ss] : ox[ss]);
+      cs[ss] = rope_cs(tab, g, aa, min(o + lc, dim - 1), pp);
+    }
+#pragma unroll
+    for (int ss = 0; ss < 8; ss++) s_cs[(ss * nrow + row) * P + pp] = cs[ss];
+  }
+  const int rowbase = a == 0 ? 0 : (a == 1 ? g.bz : g.bz + g.by);
+  float ka[8], va[8];
+#pragma unroll
+  for (int u = 0; u < 8; u++) ka[u] = va[u] = 0.f;
+  int cnt = 0;
+  const int64_t rowoff = (int64_t)b * g.N;
+  for (int r0 = 0; r0 < g.vol; r0 += per) {
+    const int nr = min(per, g.vol - r0);
+    if (r0 > 0) __syncthreads();  // previous pass done with s_slot, s_lc
+    // slots of member rr of every block, and rr's local coordinates
+    for (int t = threadIdx.x; t < nr; t += NT) {
+      const int rr = r0 + t;
+      const int lz = rr / (g.by * g.bx), rem = rr - lz * (g.by * g.bx);
+      const int ly = rem / g.bx, lx = rem - ly * g.bx;
+      s_lc[t] = lz | (ly << 10) | (lx << 20);
+      int j[8];
+#pragma unroll
+      for (int ss = 0; ss < 8; ss++) {
+        const int z = oz[ss] + lz, y = oy[ss] + ly, x = ox[ss] + lx;
+        const bool on = m0 + ss < g.M && z < g.Z && y < g.Y && x < g.X;
+        j[ss] = slot[on ? site_of(g, z, y, x) : 0];
+        j[ss] = on ? j[ss] : -1;
+      }
+#pragma unroll
+      for (int ss = 0; ss < 8; ss++) s_slot[ss * nr + t] = j[ss];
+    }
+    __syncthreads();
+    for (int q0 = 0; q0 < nr; q0 += kBatch) {
+      bf16x8 kr[kBatch], vr[kBatch];
+      int jj[kBatch];
+#pragma unroll
+      for (int t = 0; t < kBatch; t++) {
+        jj[t] = q0 + t < nr ? s_slot[s * nr + q0 + t] : -1;
+        const int64_t off = ((rowoff + max(jj[t], 0)) * g.H + h) * g.D + d0;
+        kr[t] = *reinterpret_cast<const bf16x8 *>(k + off);
+        vr[t] = *reinterpret_cast<const bf16x8 *>(v + off);
+      }
+#pragma unroll
+      for (int t = 0; t < kBatch; t++) {
+        const bool on = jj[t] >= 0;
+        cnt += on ? 1 : 0;
+        const int lcp = s_lc[min(q0 + t, nr - 1)];
+        const int lc = (lcp >> (10 * a)) & 1023;
+        const float2 *cs = s_cs + ((s * nrow) + rowbase + lc) * P + p0;
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          float x0 = (float)kr[t][2 * u], x1 = (float)kr[t][2 * u + 1];
+          rotate(x0, x1, cs[u]);
+          ka[2 * u] += on ? x0 : 0.0f;
+          ka[2 * u + 1] += on ? x1 : 0.0f;
+          va[2 * u] += on ? (float)vr[t][2 * u] : 0.0f;
+          va[2 * u + 1] += on ? (float)vr[t][2 * u + 1] : 0.0f;
+        }
+      }
+    }
+  }
+  // mean = sum / count (a division, as in the definition); empty -> 0
+  bf16x8 ko;
+#pragma unroll
+  for (int u = 0; u < 8; u++) {
+    ko[u] = (bf16)(cnt > 0 ? ka[u] / (float)cnt : 0.0f);
+    s_vt[(u * NC + c) * 9 + s] = cnt > 0 ? va[u] / (float)cnt : 0.0f;
+  }
+  {  // m < Mp always: the grid covers Mp / 8 groups
+    const int64_t bh = (int64_t)b * g.H + h;
+    *reinterpret_cast<bf16x8 *>(ks + ((bh * (Mp / 32) + m / 32) * (g.D / 8) + d0 / 8) * 256 +
+                                (m % 32) * 8) = ko;
+  }
+  __syncthreads();
+  // v_sum: one 16-byte chunk per (head, channel) of the group; thread t
+  // takes channel 8*(t / 8)... of the row in chunk-major order
+  for (int t = threadIdx.x; t < NT; t += NT) {
+    const int cc = t >> 3, u = t & 7;          // chunk, channel within it
+    const int hh = (cc * 8) / g.D, d = cc * 8 - hh * g.D + u;
+    bf16x8 o;
+#pragma unroll
+    for (int q = 0; q < 8; q++) o[q] = (bf16)s_vt[(u * NC + cc) * 9 + q];
+    *reinterpret_cast<bf16x8 *>(vsb + ((((int64_t)b * g.H + hh) * (Mp / 8) + g8) * g.D + d) * 8) = o;
+  }
+}
+
 namespace {
 template <typename T, int CW>
 hipError_t run_summarize(const Geo &g, const void *geom, const void *k, const void *v, void *ks,
@@ -151,6 +303,19 @@ hipError_t launch_summarize(const Geo &g, int dtype, const void *geom, const voi
                             const void *v, void *ks, void *vs, hipStream_t s) {
   // host checks H*D <= 1024, so the transposition buffer stays within 32 KiB
   const bool c8 = g.D % 8 == 0;
+  if (dtype == PACK3D_BF16 && c8) {
+    const int nrow = g.bz + g.by + g.bx;
+    const int per = g.vol < kMaxMembers / 8 ? g.vol : kMaxMembers / 8;
+    const size_t lds = (size_t)9 * per * 4 + 8 + (size_t)8 * nrow * g.P * 8 +
+                       (size_t)8 * (g.H * g.D / 8) * 9 * 4;
+    if (lds <= 48 * 1024 && g.H * g.D <= 512 && g.bz < 1024 && g.by < 1024 && g.bx < 1024) {
+      dim3 grid((unsigned)((g.M + 31) / 32 * 4), (unsigned)g.B);
+      hipLaunchKernelGGL(k_summarize_b8, grid, dim3(g.H * g.D), lds, s, g, geom,
+                         static_cast<const bf16 *>(k), static_cast<const bf16 *>(v),
+                         static_cast<bf16 *>(ks), static_cast<bf16 *>(vs), nrow);
+      return hipGetLastError();
+    }
+  }
   if (dtype == PACK3D_BF16)
     return c8 ? run_summarize<bf16, 8>(g, geom, k, v, ks, vs, s)
               : run_summarize<bf16, 2>(g, geom, k, v, ks, vs, s);
