@@ -1,4 +1,5 @@
-"""The five synthetic workloads, one-to-one with the measured configurations.
+"""The synthetic workloads: five measured configurations, then two volumes of
+2^20 and 2^22 tokens for the million-token reach.
 
 Grid is (Z, Y, X) with x fastest in raster order; block is (bz, by, bx).
 """
@@ -49,6 +50,10 @@ WORKLOADS = {
     3: Workload(3, "grid32x32x64_bf16", (32, 32, 64), 1, 8, 48, (2, 2, 2), "bf16", "iid", "block", "group"),
     4: Workload(4, "grid64_bf16_random", (64, 64, 64), 1, 8, 48, (4, 4, 4), "bf16", "iid", "random", "random2"),
     5: Workload(5, "grid16x64x64_bf16_smooth", (16, 64, 64), 4, 4, 96, (2, 2, 4), "bf16", "smooth", "block", "raster"),
+    # million-token reach: 2^20 tokens with 4,096 summaries per head (256
+    # tokens per 4x8x8 block), and 2^22 tokens at the same block volume
+    6: Workload(6, "grid64x128x128_bf16_1m", (64, 128, 128), 1, 8, 48, (4, 8, 8), "bf16", "iid", "block", "random"),
+    7: Workload(7, "grid128x128x256_bf16_4m", (128, 128, 256), 1, 8, 48, (4, 8, 8), "bf16", "iid", "block", "random"),
 }
 
 

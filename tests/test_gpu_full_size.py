@@ -78,3 +78,14 @@ def test_full_size_repack_bitwise(w):
                                        to_dev(v, dt), to_dev(g, dt)))
     p = torch.from_numpy(pi.order_between(ca, cb, w.grid)).to("cuda")
     assert torch.equal(outs[0], outs[1][:, p])
+
+
+# Million-token reach: 2^20 tokens, 4,096 summaries per head, one forward in
+# the launch configuration the benchmark times, checked at sampled rows; and
+# the same volume under a random repack, bit for bit.
+MILLION = pi.workload(6)
+
+
+def test_million_tokens_sampled_rows_and_repack():
+    test_full_size_sampled_rows(MILLION)
+    test_full_size_repack_bitwise(MILLION)
