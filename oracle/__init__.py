@@ -39,7 +39,7 @@ def _load(path):
     L.ork_index.restype = C.c_int
     L.ork_index.argtypes = [P, P, P, P, P]
     for name, n in [("ork_neighbours", 4), ("ork_rope_axial", 4), ("ork_rope_sequence", 3),
-                    ("ork_summaries", 6)]:
+                    ("ork_summaries", 6), ("ork_summaries_centre", 6)]:
         getattr(L, name).restype = None
         getattr(L, name).argtypes = [P] * n
     L.ork_local.restype = None
@@ -157,6 +157,18 @@ def summaries(desc, slot, kr, v):
     return ks, vs
 
 
+def summaries_centre(desc, slot, k, v):
+    """Summary-centre variant: mean of the UNROTATED keys k, rotated once at
+    the block centre; values as in summaries()."""
+    k, v = _f64(k), _f64(v)
+    M = num_blocks(desc)
+    ks = np.empty((desc.B, desc.H, M, desc.D))
+    vs = np.empty_like(ks)
+    lib().ork_summaries_centre(C.byref(desc), _ptr(_i32(slot)), _ptr(k), _ptr(v), _ptr(ks),
+                               _ptr(vs))
+    return ks, vs
+
+
 def _rows(rows, N):
     if rows is None:
         return None, N
@@ -188,9 +200,12 @@ def mix(desc, gate, oloc, oglob, rows=None):
     return out
 
 
-def forward(desc, coords, q, k, v, gate, rows=None, rope="axial", return_parts=False):
+def forward(desc, coords, q, k, v, gate, rows=None, rope="axial", return_parts=False,
+            summary_rope="token"):
     """The whole operator, steps 0-5 in order. rope: "axial" (grid
-    coordinates), "sequence" (packed-index control) or "none"."""
+    coordinates), "sequence" (packed-index control) or "none". summary_rope:
+    "token" (rotate every key, then pool) or "centre" (pool unrotated keys,
+    rotate the mean at the block centre; axial RoPE only)."""
     slot, _, _ = index(desc, coords)
     if rope == "axial":
         qr, kr = rope_axial(desc, coords, q), rope_axial(desc, coords, k)
@@ -200,7 +215,12 @@ def forward(desc, coords, q, k, v, gate, rows=None, rope="axial", return_parts=F
         qr, kr = _f64(q), _f64(k)
     else:
         raise ValueError(rope)
-    ks, vs = summaries(desc, slot, kr, v)
+    if summary_rope == "token":
+        ks, vs = summaries(desc, slot, kr, v)
+    elif summary_rope == "centre" and rope == "axial":
+        ks, vs = summaries_centre(desc, slot, k, v)
+    else:
+        raise ValueError(summary_rope)
     ol = local(desc, coords, slot, qr, kr, v, rows)
     og = global_(desc, coords, qr, ks, vs, rows)
     o = mix(desc, gate, ol, og, rows)

@@ -21,7 +21,9 @@
  *                     (project page Ch. 3, Contract 3; paper summary §B.2)
  *   2. summaries      keys are rotated first, then mean-pooled per contiguous
  *                     3D block; values are pooled unrotated (project page
- *                     Ch. 3 "Rotate first, then pool"; paper summary §3.2, §B.5)
+ *                     Ch. 3 "Rotate first, then pool"; paper summary §3.2, §B.5).
+ *                     Variant: pool unrotated keys, rotate the mean once at
+ *                     the block centre (paper summary §B.7, §B.8)
  *   3. local          exact softmax attention over the <=27 tokens of the
  *                     3x3x3 coordinate neighbourhood (project page Ch. 3,
  *                     Contract 1; paper summary §3.2, §3.5)
@@ -229,6 +231,45 @@ void ork_summaries(const ork_desc *d, const int32_t *slot, const double *kr, con
             ko[c] /= count;
             vo[c] /= count;
           }
+      }
+    }
+  }
+}
+
+/* Summary-centre variant (paper summary §B.7, §B.8; project page Ch. 3, the
+ * cheaper summary that pools unrotated keys and rotates the result once at a
+ * representative coordinate). The keys k are the unrotated inputs; each
+ * block's mean key is rotated at the block centre, origin + (extent - 1) / 2
+ * along each axis, the extent clipped at the grid edge (a half-integer
+ * coordinate for an even extent). Values are pooled as in ork_summaries. */
+void ork_summaries_centre(const ork_desc *d, const int32_t *slot, const double *k,
+                          const double *v, double *ks, double *vs) {
+  ork_summaries(d, slot, k, v, ks, vs); /* plain means of the unrotated keys */
+  const int D = d->D, H = d->H, M = ork_num_blocks(d), da = D / 3, P = da / 2;
+  const int My = blocks_along(d, 1), Mx = blocks_along(d, 2);
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int b = 0; b < d->B; b++) {
+    for (int m = 0; m < M; m++) {
+      const int o[3] = {(m / (My * Mx)) * d->block[0], ((m / Mx) % My) * d->block[1],
+                        (m % Mx) * d->block[2]};
+      double centre[3];
+      for (int a = 0; a < 3; a++) {
+        int extent = d->grid[a] - o[a] < d->block[a] ? d->grid[a] - o[a] : d->block[a];
+        centre[a] = o[a] + 0.5 * (extent - 1);
+      }
+      for (int h = 0; h < H; h++) {
+        double *ko = ks + (((int64_t)b * H + h) * M + m) * D;
+        for (int a = 0; a < 3; a++) {
+          for (int p = 0; p < P; p++) {
+            double theta = pow(d->rope_base, -2.0 * (double)p / (double)da);
+            double phi = centre[a] * theta;
+            double cs = cos(phi), sn = sin(phi);
+            const int first = a * da + 2 * p; /* channels (first, first + 1) */
+            double x0 = ko[first], x1 = ko[first + 1];
+            ko[first] = x0 * cs - x1 * sn;
+            ko[first + 1] = x0 * sn + x1 * cs;
+          }
+        }
       }
     }
   }

@@ -86,6 +86,23 @@ def pin_mix():
     return np.allclose(o, (1 - sig) * parts["local"] + sig * parts["glob"], atol=1e-14)
 
 
+def pin_summary_centre():
+    d, c, q, k, v, _ = _setup(grid=(5, 4, 6), block=(2, 2, 4))
+    slot, _, _ = oracle.index(d, c)
+    ks, vs = oracle.summaries_centre(d, slot, k, v)
+    bid = block_ids(c, d.grid, d.block)
+    My, Mx = -(-d.grid[1] // d.block[1]), -(-d.grid[2] // d.block[2])
+    for m in range(ks.shape[2]):
+        o = np.array([(m // (My * Mx)) * d.block[0], ((m // Mx) % My) * d.block[1],
+                      (m % Mx) * d.block[2]])
+        centre = o + 0.5 * (np.minimum(np.array(d.block), np.array(d.grid) - o) - 1)
+        mem = np.flatnonzero(bid == m)
+        if not np.allclose(ks[0, 1, m], rotation(centre, d.D) @ k[0, mem, 1].mean(axis=0),
+                           atol=1e-12):
+            return False
+    return True
+
+
 MUTANTS = [
     ("rope_sin_sign", "yr[c0 + 1] = x0 * sn + x1 * cs;", "yr[c0 + 1] = -x0 * sn + x1 * cs;", pin_rope),
     ("rope_frequency", "pow(d->rope_base, -2.0 * p / (double)da)", "pow(d->rope_base, -2.0 * p / (double)D)", pin_rope),
@@ -99,12 +116,15 @@ MUTANTS = [
     ("summary_block_origin", "int oz = (m / (My * Mx)) * bz, oy = ((m / Mx) % My) * by, ox = (m % Mx) * bx;", "int oz = (m / (My * Mx)) * bz, oy = (m % My) * by, ox = ((m / My) % Mx) * bx;", pin_summaries),
     ("global_summary_stride", "logit[m] = s * dot(q, ks + (((int64_t)b * H + h) * M + m) * D, D);", "logit[m] = s * dot(q, ks + (((int64_t)b * M + m) * H + h) * D, D);", pin_global),
     ("global_value_head", "const double *vm = vs + (((int64_t)b * H + h) * M + m) * D;", "const double *vm = vs + (((int64_t)b * H + 0) * M + m) * D;", pin_global),
+    ("centre_extent", "centre[a] = o[a] + 0.5 * (extent - 1);", "centre[a] = o[a] + 0.5 * extent;", pin_summary_centre),
+    ("centre_unclipped", "int extent = d->grid[a] - o[a] < d->block[a] ? d->grid[a] - o[a] : d->block[a];", "int extent = d->block[a];", pin_summary_centre),
     ("mix_swapped", "out[base + c] = (1.0 - g) * oloc[base + c] + g * oglob[base + c];", "out[base + c] = g * oloc[base + c] + (1.0 - g) * oglob[base + c];", pin_mix),
 ]
 
 
 def test_unmodified_oracle_passes_every_pin():
-    for f in (pin_rope, pin_neighbours, pin_local, pin_summaries, pin_global, pin_mix):
+    for f in (pin_rope, pin_neighbours, pin_local, pin_summaries, pin_global, pin_mix,
+              pin_summary_centre):
         assert f(), f.__name__
 
 
