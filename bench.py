@@ -122,6 +122,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summary-centre", action="store_true",
+                    help="summary-centre variant: pool unrotated keys, rotate at the block centre")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the PACK3D "
@@ -147,7 +149,8 @@ def main():
     dev = torch.device("cuda:0")
     dc = torch.from_numpy(coords).to(dev)
     dq, dk, dv, dg = (torch.from_numpy(a).to(dev).to(dt).contiguous() for a in (q, k, v, g))
-    d = gas.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block, dtype=dt, rope_base=w.rope_base)
+    d = gas.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block, dtype=dt, rope_base=w.rope_base,
+                      summary_centre=args.summary_centre)
     ws = torch.empty(gas.pack3d_workspace_bytes(d), dtype=torch.uint8, device=dev)
     out = torch.empty_like(dq)
     nev = 2 * gas.PACK3D_NUM_STAGES
@@ -198,7 +201,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "grid_zyx": list(w.grid), "batch": w.B, "heads": w.H,
                    "head_dim": w.D, "block": list(w.block), "summaries": w.M,
-                   "tokens": w.tokens, "packing": w.packing, "values": w.values},
+                   "tokens": w.tokens, "packing": w.packing, "values": w.values,
+                   "summary_rope": "centre" if args.summary_centre else "token"},
         "roofline": roofline,
         "stages": stage_roof,
         "wall_s_timed_region": round(wall, 4),

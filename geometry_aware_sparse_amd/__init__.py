@@ -9,7 +9,7 @@ this package loads the library and fails loudly when it has not been built
 """
 from ._lib import (PACK3D_BF16, PACK3D_EXCL_NEIGHBOURHOOD_BLOCKS, PACK3D_EXCL_NONE,
                    PACK3D_EXCL_OWN_BLOCK, PACK3D_F32, PACK3D_NUM_STAGES, PACK3D_VALIDATE,
-                   PACK3D_EXACT_SOFTMAX,
+                   PACK3D_EXACT_SOFTMAX, PACK3D_SUMMARY_CENTRE,
                    EXPORTED_SYMBOLS, LIB_PATH, Desc, Pack3DError, library)
 from .ops import (make_desc, pack3d_block_summarize, pack3d_forward, pack3d_geometry_bytes,
                   pack3d_geometry_layout, pack3d_global_attn, pack3d_index_build,
@@ -21,7 +21,7 @@ library()  # load now: no silent fallback when the HIP library is absent
 
 __all__ = [
     "PACK3D_BF16", "PACK3D_F32", "PACK3D_EXCL_NONE", "PACK3D_EXCL_OWN_BLOCK",
-    "PACK3D_EXCL_NEIGHBOURHOOD_BLOCKS", "PACK3D_VALIDATE", "PACK3D_EXACT_SOFTMAX", "PACK3D_NUM_STAGES",
+    "PACK3D_EXCL_NEIGHBOURHOOD_BLOCKS", "PACK3D_VALIDATE", "PACK3D_EXACT_SOFTMAX", "PACK3D_SUMMARY_CENTRE", "PACK3D_NUM_STAGES",
     "EXPORTED_SYMBOLS", "LIB_PATH", "Desc", "Pack3DError", "library", "make_desc",
     "pack3d_block_summarize", "pack3d_forward", "pack3d_geometry_bytes", "pack3d_geometry_layout",
     "pack3d_global_attn", "pack3d_index_build", "pack3d_local_attn", "pack3d_mix",

@@ -11,6 +11,7 @@ PACK3D_EXCL_OWN_BLOCK = 1
 PACK3D_EXCL_NEIGHBOURHOOD_BLOCKS = 2
 PACK3D_VALIDATE = 0x1
 PACK3D_EXACT_SOFTMAX = 0x2
+PACK3D_SUMMARY_CENTRE = 0x4
 PACK3D_NUM_STAGES = 4
 
 STATUS = {0: "PACK3D_OK", -1: "PACK3D_ERR_INVALID_ARG", -2: "PACK3D_ERR_SHAPE",

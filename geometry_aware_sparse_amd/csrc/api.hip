@@ -23,6 +23,8 @@ int make_geo(const pack3d_desc *d, Geo *g) {
     return PACK3D_ERR_INVALID_ARG;
   if (!(d->rope_base > 0.0f) || !isfinite(d->rope_base)) return PACK3D_ERR_INVALID_ARG;
   if (!isfinite(d->scale)) return PACK3D_ERR_INVALID_ARG;
+  if (d->flags & ~(PACK3D_VALIDATE | PACK3D_EXACT_SOFTMAX | PACK3D_SUMMARY_CENTRE))
+    return PACK3D_ERR_INVALID_ARG;
   for (int a = 0; a < 3; a++)
     if (d->grid[a] <= 0 || d->block[a] <= 0) return PACK3D_ERR_SHAPE;
   if (d->D % 6 != 0) return PACK3D_ERR_SHAPE;
@@ -62,7 +64,7 @@ int make_geo(const pack3d_desc *d, Geo *g) {
 }
 
 size_t geometry_bytes(const Geo &g) {
-  return align_up((size_t)g.table_off + (size_t)(g.Z + g.Y + g.X) * g.P * 8);
+  return align_up((size_t)g.table_off + (size_t)(g.Z + g.Y + g.X + 1) * g.P * 8);
 }
 
 // k_sum [B, H, Mp/32, Dp/8, 32, 8] and v_sum [B, H, Mp/8, D, 8],

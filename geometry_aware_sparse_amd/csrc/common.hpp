@@ -50,6 +50,10 @@ __device__ __forceinline__ float2 rope_cs(const float2 *tab, const Geo &g, int a
   int start = a == 0 ? 0 : (a == 1 ? g.Z : g.Z + g.Y);
   return tab[(int64_t)(start + c) * g.P + p];
 }
+// (cos, sin) of half of plane p's angle per unit step: the table's last row.
+__device__ __forceinline__ float2 rope_half(const float2 *tab, const Geo &g, int p) {
+  return tab[(int64_t)(g.Z + g.Y + g.X) * g.P + p];
+}
 // The same value computed directly: angle c * base^(-2p/(D/3)) in double,
 // cos and sin in double, rounded to fp32.
 __device__ __forceinline__ float2 rope_cs_direct(float base, int D, int c, int p) {
@@ -57,6 +61,14 @@ __device__ __forceinline__ float2 rope_cs_direct(float base, int D, int c, int p
   double phi = (double)c * theta;
   double s, co;
   sincos(phi, &s, &co);
+  return make_float2((float)co, (float)s);
+}
+// (cos, sin) at a real coordinate (a block centre may be a half-integer):
+// angle c * base^(-2p/(D/3)) in double, cos and sin in double, rounded to fp32.
+__device__ __forceinline__ float2 rope_cs_real(float base, int D, double c, int p) {
+  double theta = pow((double)base, -2.0 * (double)p / (double)(D / 3));
+  double s, co;
+  sincos(c * theta, &s, &co);
   return make_float2((float)co, (float)s);
 }
 // Rotate the channel pair (x0, x1) by (cos, sin).

@@ -6,17 +6,21 @@
 
 namespace pk {
 
-// Clears the status word and slot map and fills the RoPE table.
+// Clears the status word and slot map and fills the RoPE table: one row per
+// grid coordinate of each axis, then one row of half-angles theta_p / 2 (a
+// block centre of even extent sits half-way between two coordinates).
 __global__ void k_geom_init(Geo g, int32_t *status, int32_t *slot, float2 *tab) {
   int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int64_t S = (int64_t)g.Z * g.Y * g.X;
   if (t == 0) status[0] = 0;
   if (t < S) slot[t] = -1;
-  int64_t T = (int64_t)(g.Z + g.Y + g.X) * g.P;
+  const int rows = g.Z + g.Y + g.X;
+  int64_t T = (int64_t)(rows + 1) * g.P;
   if (t < T) {
     int row = (int)(t / g.P), p = (int)(t % g.P);
     int c = row < g.Z ? row : (row < g.Z + g.Y ? row - g.Z : row - g.Z - g.Y);
-    tab[t] = rope_cs_direct(g.rope_base, g.D, c, p);
+    tab[t] = row < rows ? rope_cs_direct(g.rope_base, g.D, c, p)
+                        : rope_cs_real(g.rope_base, g.D, 0.5, p);
   }
 }
 
@@ -58,7 +62,7 @@ hipError_t launch_index(const Geo &g, const int32_t *coords, void *geom, int32_t
   int32_t *slot = reinterpret_cast<int32_t *>(base + g.slot_off);
   float2 *tab = reinterpret_cast<float2 *>(base + g.table_off);
   int64_t S = (int64_t)g.Z * g.Y * g.X;
-  int64_t T = (int64_t)(g.Z + g.Y + g.X) * g.P;
+  int64_t T = (int64_t)(g.Z + g.Y + g.X + 1) * g.P;
   int64_t n = S > T ? S : T;
   const int TB = 256;
   hipLaunchKernelGGL(k_geom_init, dim3((unsigned)((n + TB - 1) / TB)), dim3(TB), 0, s, g, status,

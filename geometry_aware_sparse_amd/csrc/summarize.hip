@@ -1,5 +1,8 @@
 // Rotate-then-pool block summaries (Geometry Matters in Packed 3D Attention,
-// project page Ch. 3 "Rotate first, then pool"; paper summary §3.2, §B.5).
+// project page Ch. 3 "Rotate first, then pool"; paper summary §3.2, §B.5),
+// and the summary-centre variant under PACK3D_SUMMARY_CENTRE (paper summary
+// §B.7, §B.8): the mean of the unrotated keys, rotated once at the block
+// centre.
 //
 // One workgroup per (group of 8 consecutive summaries, batch); the summary
 // count is padded to Mp = 32*ceil(M/32) and padding slots are written as 0.
@@ -23,7 +26,34 @@ namespace pk {
 
 constexpr int kMaxMembers = 512;  // member slots staged in LDS per pass (8 blocks)
 
-template <typename T, int CW>
+// Summary-centre variant: rotate the (unrotated) mean key of block m, a chunk
+// of CW channels of axis a starting at plane p0, at the block centre
+// origin + (extent - 1) / 2, the extent clipped at the grid edge. An odd
+// extent puts the centre on a grid coordinate, origin + l, whose (cos, sin)
+// is a table row; an even one puts it at origin + l + 1/2, whose (cos, sin)
+// follow from row l and the table's half-angle row by the angle-addition
+// formulas. cs_at(l, p) gives plane p's (cos, sin) at local coordinate l.
+template <int CW, typename CsAt>
+__device__ __forceinline__ void rotate_at_centre(const Geo &g, int m, int a, int p0,
+                                                 const float2 *tab, CsAt cs_at, float *x) {
+  const int mz = m / (g.My * g.Mx), my = (m / g.Mx) % g.My, mx = m % g.Mx;
+  const int o = a == 0 ? mz * g.bz : (a == 1 ? my * g.by : mx * g.bx);
+  const int ext = min(a == 0 ? g.bz : (a == 1 ? g.by : g.bx), (a == 0 ? g.Z : (a == 1 ? g.Y : g.X)) - o);
+  const int l = (ext - 1) / 2;
+  const bool odd = (ext & 1) != 0;
+#pragma unroll
+  for (int u = 0; u < CW; u += 2) {
+    const int p = p0 + u / 2;
+    float2 t = cs_at(l, p);
+    if (!odd) {
+      const float2 hh = rope_half(tab, g, p);
+      t = make_float2(t.x * hh.x - t.y * hh.y, t.y * hh.x + t.x * hh.y);
+    }
+    rotate(x[u], x[u + 1], t);
+  }
+}
+
+template <typename T, int CW, bool CENTRE>
 __global__ __launch_bounds__(512) void k_summarize(Geo g, const void *geom, const T *k,
                                                    const T *v, T *ks, T *vsb) {
   __shared__ int s_slot[kMaxMembers];
@@ -94,10 +124,12 @@ __global__ __launch_bounds__(512) void k_summarize(Geo g, const void *geom, cons
             vx[u] = to_f32(v[off + u]);
           }
         }
+        if constexpr (!CENTRE) {
 #pragma unroll
-        for (int u = 0; u < CW; u += 2) {
-          const int dd = d0 + u, a = dd / da;
-          rotate(kx[u], kx[u + 1], rope_cs(tab, g, a, c3[a], (dd % da) / 2));
+          for (int u = 0; u < CW; u += 2) {
+            const int dd = d0 + u, a = dd / da;
+            rotate(kx[u], kx[u + 1], rope_cs(tab, g, a, c3[a], (dd % da) / 2));
+          }
         }
 #pragma unroll
         for (int u = 0; u < CW; u++) {
@@ -108,10 +140,18 @@ __global__ __launch_bounds__(512) void k_summarize(Geo g, const void *geom, cons
     }
     if (!act) continue;
     // mean = sum / count (a division, as in the definition); empty -> 0
+    float km[CW];
+#pragma unroll
+    for (int u = 0; u < CW; u++) km[u] = cnt > 0 ? ka[u] / (float)cnt : 0.0f;
+    if (CENTRE && m < g.M) {  // padding slots stay 0 (and have no extent)
+      const int a = d0 / da;  // a chunk lies within one axis
+      rotate_at_centre<CW>(g, m, a, (d0 % da) / 2, tab,
+                           [&](int l, int p) { return rope_cs(tab, g, a, o3[a] + l, p); }, km);
+    }
     const int64_t ko = ((((bh0 + h) * (Mp / 32) + m / 32) * (Dp / 8) + d0 / 8) * 32 + m % 32) * 8;
 #pragma unroll
     for (int u = 0; u < CW; u++) {
-      ks[ko + (d0 + u) % 8] = from_f32<T>(cnt > 0 ? ka[u] / (float)cnt : 0.0f);
+      ks[ko + (d0 + u) % 8] = from_f32<T>(km[u]);
       s_vt[(h * g.D + d0 + u) * 8 + s] = cnt > 0 ? va[u] / (float)cnt : 0.0f;
     }
   }
@@ -146,6 +186,7 @@ __global__ __launch_bounds__(512) void k_summarize(Geo g, const void *geom, cons
 //      the writes of a wave fall in distinct banks.
 constexpr int kBatch = 8;  // members whose loads are in flight together
 
+template <bool CENTRE>
 __global__ __launch_bounds__(512) void k_summarize_b8(Geo g, const void *geom, const bf16 *k,
                                                        const bf16 *v, bf16 *ks, bf16 *vsb,
                                                        int nrow) {
@@ -250,7 +291,7 @@ __global__ __launch_bounds__(512) void k_summarize_b8(Geo g, const void *geom, c
 #pragma unroll
         for (int u = 0; u < 4; u++) {
           float x0 = (float)kr[t][2 * u], x1 = (float)kr[t][2 * u + 1];
-          rotate(x0, x1, cs[u]);
+          if constexpr (!CENTRE) rotate(x0, x1, cs[u]);
           ka[2 * u] += on ? x0 : 0.0f;
           ka[2 * u + 1] += on ? x1 : 0.0f;
           va[2 * u] += on ? (float)vr[t][2 * u] : 0.0f;
@@ -260,10 +301,16 @@ __global__ __launch_bounds__(512) void k_summarize_b8(Geo g, const void *geom, c
     }
   }
   // mean = sum / count (a division, as in the definition); empty -> 0
+  float km[8];
+#pragma unroll
+  for (int u = 0; u < 8; u++) km[u] = cnt > 0 ? ka[u] / (float)cnt : 0.0f;
+  if (CENTRE && m < g.M)  // padding slots stay 0 (and have no extent)
+    rotate_at_centre<8>(g, m, a, p0, tab,
+                        [&](int l, int p) { return s_cs[(s * nrow + rowbase + l) * P + p]; }, km);
   bf16x8 ko;
 #pragma unroll
   for (int u = 0; u < 8; u++) {
-    ko[u] = (bf16)(cnt > 0 ? ka[u] / (float)cnt : 0.0f);
+    ko[u] = (bf16)km[u];
     s_vt[(u * NC + c) * 9 + s] = cnt > 0 ? va[u] / (float)cnt : 0.0f;
   }
   {  // m < Mp always: the grid covers Mp / 8 groups
@@ -292,9 +339,9 @@ hipError_t run_summarize(const Geo &g, const void *geom, const void *k, const vo
   const int cpt = NC < 64 ? NC : 64;  // chunk lanes per block
   const size_t lds = (size_t)g.H * g.D * 8 * sizeof(float);
   dim3 grid((unsigned)((g.M + 31) / 32 * 4), (unsigned)g.B);
-  hipLaunchKernelGGL((k_summarize<T, CW>), grid, dim3(8 * cpt), lds, s, g, geom,
-                     static_cast<const T *>(k), static_cast<const T *>(v), static_cast<T *>(ks),
-                     static_cast<T *>(vs));
+  auto kern = (g.flags & PACK3D_SUMMARY_CENTRE) ? k_summarize<T, CW, true> : k_summarize<T, CW, false>;
+  hipLaunchKernelGGL(kern, grid, dim3(8 * cpt), lds, s, g, geom, static_cast<const T *>(k),
+                     static_cast<const T *>(v), static_cast<T *>(ks), static_cast<T *>(vs));
   return hipGetLastError();
 }
 }  // namespace
@@ -310,7 +357,8 @@ hipError_t launch_summarize(const Geo &g, int dtype, const void *geom, const voi
                        (size_t)8 * (g.H * g.D / 8) * 9 * 4;
     if (lds <= 48 * 1024 && g.H * g.D <= 512 && g.bz < 1024 && g.by < 1024 && g.bx < 1024) {
       dim3 grid((unsigned)((g.M + 31) / 32 * 4), (unsigned)g.B);
-      hipLaunchKernelGGL(k_summarize_b8, grid, dim3(g.H * g.D), lds, s, g, geom,
+      auto kern = (g.flags & PACK3D_SUMMARY_CENTRE) ? k_summarize_b8<true> : k_summarize_b8<false>;
+      hipLaunchKernelGGL(kern, grid, dim3(g.H * g.D), lds, s, g, geom,
                          static_cast<const bf16 *>(k), static_cast<const bf16 *>(v),
                          static_cast<bf16 *>(ks), static_cast<bf16 *>(vs), nrow);
       return hipGetLastError();

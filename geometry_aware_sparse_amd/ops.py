@@ -4,13 +4,14 @@ import ctypes as C
 import torch
 
 from ._lib import (PACK3D_BF16, PACK3D_EXACT_SOFTMAX, PACK3D_F32, PACK3D_NUM_STAGES,
+                   PACK3D_SUMMARY_CENTRE,
                    PACK3D_VALIDATE, Desc, Pack3DError, library)
 
 _DTYPES = {PACK3D_F32: torch.float32, PACK3D_BF16: torch.bfloat16}
 
 
 def make_desc(B, N, H, D, grid, block, dtype=PACK3D_BF16, rope_base=10000.0, scale=0.0,
-              exclusion=0, validate=False, exact_softmax=False):
+              exclusion=0, validate=False, exact_softmax=False, summary_centre=False):
     if isinstance(dtype, torch.dtype):
         dtype = {torch.float32: PACK3D_F32, torch.bfloat16: PACK3D_BF16}[dtype]
     d = Desc()
@@ -21,7 +22,8 @@ def make_desc(B, N, H, D, grid, block, dtype=PACK3D_BF16, rope_base=10000.0, sca
     d.scale = float(scale)
     d.dtype = int(dtype)
     d.exclusion = int(exclusion)
-    d.flags = (PACK3D_VALIDATE if validate else 0) | (PACK3D_EXACT_SOFTMAX if exact_softmax else 0)
+    d.flags = ((PACK3D_VALIDATE if validate else 0) | (PACK3D_EXACT_SOFTMAX if exact_softmax else 0)
+               | (PACK3D_SUMMARY_CENTRE if summary_centre else 0))
     return d
 
 

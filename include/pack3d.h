@@ -96,6 +96,14 @@ typedef enum pack3d_exclusion {
  * is redone by an exact two-pass softmax. This flag sends every query
  * through the two-pass softmax (maximum first, then the sums). */
 #define PACK3D_EXACT_SOFTMAX 0x2u
+/* Summary-centre variant of the compressed branch (paper summary §B.7, §B.8;
+ * project page Ch. 3): the key summary is the mean of the UNROTATED member
+ * keys, rotated once at the block centre (origin + (extent - 1) / 2 along
+ * each axis, the extent clipped at the grid edge; a half-integer coordinate
+ * for an even extent). Without it every key is rotated at its own coordinate
+ * before pooling, which keeps each member's displacement from the query
+ * exactly (the default). Values are pooled the same way in both. */
+#define PACK3D_SUMMARY_CENTRE 0x4u
 
 typedef struct pack3d_desc {
   int32_t B, N, H, D;  /* batch, tokens, heads, head dim (D % 6 == 0)         */
@@ -127,10 +135,12 @@ int64_t pack3d_num_summaries(const pack3d_desc *desc);
  *                          bit 1: coordinate duplicated), then padding
  *   [slot_offset, ...)     int32 slot map [Z*Y*X]: slot[(z*Y + y)*X + x] =
  *                          memory position of the token at (z,y,x), -1 if none
- *   [table_offset, ...)    float32 RoPE table [(Z+Y+X) * (D/6)][2]: entry
+ *   [table_offset, ...)    float32 RoPE table [(Z+Y+X+1) * (D/6)][2]: entry
  *                          (axis_start + c)*(D/6) + p holds (cos, sin) of
  *                          c * base^(-2p/(D/3)), evaluated in double and
- *                          rounded; axis_start is 0, Z, Z+Y for z, y, x
+ *                          rounded; axis_start is 0, Z, Z+Y for z, y, x;
+ *                          the last row (Z+Y+X)*(D/6) + p holds the same at
+ *                          c = 1/2 (block centres of even extent)
  * Offsets are reported by pack3d_geometry_layout. */
 int pack3d_geometry_bytes(const pack3d_desc *desc, size_t *bytes);
 int pack3d_geometry_layout(const pack3d_desc *desc, size_t *slot_offset, size_t *table_offset,

@@ -32,7 +32,7 @@ def _gpu():
         pytest.skip("no GPU")
 
 
-def _forward_in(w, kind, fields, base=None):
+def _forward_in(w, kind, fields, base=None, centre=False):
     import geometry_aware_sparse_amd as gas
     if kind == "group":
         coords = pi.group_permuted_coords(base, w.block, w.seed("perm2"))
@@ -41,16 +41,18 @@ def _forward_in(w, kind, fields, base=None):
         coords = pi.packing_coords(w.grid, kind, block=w.block, seed=seed)
     q, k, v, g = pi.pack_fields(fields, coords, w.grid)
     d, _ = desc_pair(w)
+    if centre:
+        d.flags |= gas.PACK3D_SUMMARY_CENTRE
     dt = tdtype(w)
     o = gas.pack3d_forward(d, to_dev(coords, torch.int32), to_dev(q, dt), to_dev(k, dt),
                            to_dev(v, dt), to_dev(g, dt))
     return coords, o
 
 
-def _check(w, a, b):
+def _check(w, a, b, centre=False):
     fields = pi.make_fields(w)
-    ca, oa = _forward_in(w, a, fields)
-    cb, ob = _forward_in(w, b, fields, base=ca)
+    ca, oa = _forward_in(w, a, fields, centre=centre)
+    cb, ob = _forward_in(w, b, fields, base=ca, centre=centre)
     p = torch.from_numpy(pi.order_between(ca, cb, w.grid)).to("cuda")
     assert torch.equal(oa, ob[:, p]), f"{w.name}: {a} vs {b} differ"
     assert torch.isfinite(oa.float()).all()
@@ -73,3 +75,8 @@ def test_deterministic_replay():
     o1 = gas.pack3d_forward(d, *args)
     o2 = gas.pack3d_forward(d, *args)
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("w,a,b", [SMALL[1], SMALL[4]], ids=["grid8-centre", "ragged-centre"])
+def test_repack_permutes_output_bitwise_summary_centre(w, a, b):
+    _check(w, a, b, centre=True)

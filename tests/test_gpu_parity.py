@@ -63,6 +63,25 @@ def test_index_build_bit_exact(w):
 
 
 @pytest.mark.parametrize("w", CASES, ids=IDS)
+def test_rope_table(w):
+    # rows (axis_start + c) * P + p hold (cos, sin) of c * base^(-2p/(D/3))
+    # rounded from double to fp32; the last row holds the same at c = 1/2
+    # (paper summary §3.1; the half row serves block centres of even extent)
+    gas, w, d, od, coords, _, dev, geom, _ = _setup(w)
+    _, to, nb = gas.pack3d_geometry_layout(d)
+    Z, Y, X = w.grid
+    P = w.D // 6
+    rows = Z + Y + X + 1
+    assert nb >= to + rows * P * 8
+    tab = geom[to:to + rows * P * 8].view(torch.float32).cpu().numpy().reshape(rows, P, 2)
+    c = np.concatenate([np.arange(Z), np.arange(Y), np.arange(X), [0.5]]).astype(np.float64)
+    theta = float(w.rope_base) ** (-2.0 * np.arange(P) / (w.D // 3))
+    ang = c[:, None] * theta[None, :]
+    want = np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+    assert np.abs(tab.astype(np.float64) - want.astype(np.float64)).max() <= 2.0 ** -23
+
+
+@pytest.mark.parametrize("w", CASES, ids=IDS)
 def test_rope_coords(w):
     gas, w, d, od, coords, (q, k, v, g), dev, geom, _ = _setup(w)
     got = host(gas.pack3d_rope_coords(d, dev["coords"], dev["q"]))
@@ -236,3 +255,50 @@ def test_global_overflowing_scores_fall_back_per_query():
     assert torch.equal(f[must], e[must])
     ordinary = torch.from_numpy(np.broadcast_to(~big[None, :, None], smax.shape).copy()).to("cuda")
     assert (f[ordinary] - e[ordinary]).abs().max().item() < 2e-2
+
+
+# Summary-centre variant (paper summary §B.7, §B.8): keys pooled unrotated,
+# the mean rotated once at the block centre. Cases with even, odd and clipped
+# block extents, fp32 and bf16 (both pooling kernels).
+CENTRE_CASES = [CASES[0], CASES[1], CASES[2], CASES[3], CASES[4], CASES[5]]
+
+
+def _centre_pair(w):
+    import geometry_aware_sparse_amd as gas
+    d = gas.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block,
+                      dtype=gas.PACK3D_BF16 if w.dtype == "bf16" else gas.PACK3D_F32,
+                      rope_base=w.rope_base, summary_centre=True)
+    od = oracle.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block, rope_base=w.rope_base)
+    return d, od
+
+
+@pytest.mark.parametrize("w", CENTRE_CASES, ids=[c.name for c in CENTRE_CASES])
+def test_block_summarize_centre(w):
+    import geometry_aware_sparse_amd as gas
+    coords, q, k, v, g = inputs(w)
+    d, od = _centre_pair(w)
+    dt = tdtype(w)
+    dc = to_dev(coords, torch.int32)
+    geom, _, _, _ = gas.pack3d_index_build(d, dc)
+    ks, vs = gas.pack3d_block_summarize(d, geom, to_dev(k, dt), to_dev(v, dt))
+    slot, _, _ = oracle.index(od, coords)
+    oks, ovs = oracle.summaries_centre(od, slot, k, v)
+    M = oks.shape[2]
+    assert_close(w, host(gas.ksum_to_rows(ks, M, w.D)), oks, "centre k_sum")
+    assert_close(w, host(gas.vsum_to_rows(vs, M)), ovs, "centre v_sum")
+    # and the summaries differ from rotate-then-pool unless every block is one site
+    ks_t, _ = gas.pack3d_block_summarize(desc_pair(w)[0], geom, to_dev(k, dt), to_dev(v, dt))
+    if w.block != (1, 1, 1):
+        assert not torch.equal(ks, ks_t)
+
+
+@pytest.mark.parametrize("w", CENTRE_CASES, ids=[c.name for c in CENTRE_CASES])
+def test_forward_centre(w):
+    import geometry_aware_sparse_amd as gas
+    coords, q, k, v, g = inputs(w)
+    d, od = _centre_pair(w)
+    dt = tdtype(w)
+    o = gas.pack3d_forward(d, to_dev(coords, torch.int32), to_dev(q, dt), to_dev(k, dt),
+                           to_dev(v, dt), to_dev(g, dt))
+    ref = oracle.forward(od, coords, q, k, v, g, summary_rope="centre")
+    assert_close(w, host(o), ref, "centre forward")
