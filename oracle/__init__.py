@@ -6,9 +6,10 @@ this package; the GPU library never does, and this package never imports the
 GPU library.
 
 All float inputs are converted to float64 (bf16 inputs are exactly
-representable), outputs are float64 numpy arrays. Layouts: Q/K/V [B,N,H,D] in
-packed (memory) order, coords int32 [N,3] as (z,y,x), gate [B,N,H],
-summaries [B,H,M,D].
+representable), outputs are float64 numpy arrays. Layouts: Q [B,N,H,D] and
+K/V [B,N,Hkv,D] in packed (memory) order, coords int32 [N,3] as (z,y,x), gate
+[B,N,H], summaries [B,Hkv,M,D]; Hkv (key/value heads) equals H unless the
+descriptor sets fewer, query head h reading KV head h // (H // Hkv).
 """
 import contextlib
 import ctypes as C
@@ -24,7 +25,8 @@ _lib = None
 class _Desc(C.Structure):
     _fields_ = [("B", C.c_int32), ("N", C.c_int32), ("H", C.c_int32), ("D", C.c_int32),
                 ("grid", C.c_int32 * 3), ("block", C.c_int32 * 3),
-                ("rope_base", C.c_double), ("scale", C.c_double), ("exclusion", C.c_int32)]
+                ("rope_base", C.c_double), ("scale", C.c_double), ("exclusion", C.c_int32),
+                ("Hkv", C.c_int32)]
 
 
 EXCLUSION = {"none": 0, "own_block": 1, "neighbourhood_blocks": 2}
@@ -94,9 +96,13 @@ def _i32(a):
     return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
 
 
-def make_desc(B, N, H, D, grid, block, rope_base=10000.0, scale=0.0, exclusion="none"):
+def make_desc(B, N, H, D, grid, block, rope_base=10000.0, scale=0.0, exclusion="none",
+              kv_heads=None):
+    if kv_heads is not None and (kv_heads < 1 or H % kv_heads):
+        raise ValueError("kv_heads must divide H")
     d = _Desc()
     d.B, d.N, d.H, d.D = B, N, H, D
+    d.Hkv = H if kv_heads is None else int(kv_heads)
     d.grid[:] = list(grid)
     d.block[:] = list(block)
     d.rope_base = float(rope_base)
@@ -134,24 +140,40 @@ def neighbours(desc, coords, slot):
     return nbr
 
 
+def kv_heads(desc) -> int:
+    return desc.Hkv if desc.Hkv > 0 else desc.H
+
+
+def _with_heads(desc, heads):
+    # the rotations act on each [D] row alone; a K/V tensor has Hkv rows per token
+    if heads == desc.H:
+        return desc
+    d = _Desc.from_buffer_copy(desc)
+    d.H = d.Hkv = heads
+    return d
+
+
 def rope_axial(desc, coords, x):
+    """x: [B, N, heads, D] with heads H (queries) or Hkv (keys)."""
     x = _f64(x)
     y = np.empty_like(x)
-    lib().ork_rope_axial(C.byref(desc), _ptr(_i32(coords)), _ptr(x), _ptr(y))
+    lib().ork_rope_axial(C.byref(_with_heads(desc, x.shape[2])), _ptr(_i32(coords)), _ptr(x),
+                         _ptr(y))
     return y
 
 
 def rope_sequence(desc, x):
     x = _f64(x)
     y = np.empty_like(x)
-    lib().ork_rope_sequence(C.byref(desc), _ptr(x), _ptr(y))
+    lib().ork_rope_sequence(C.byref(_with_heads(desc, x.shape[2])), _ptr(x), _ptr(y))
     return y
 
 
 def summaries(desc, slot, kr, v):
     kr, v = _f64(kr), _f64(v)
+    _check_kv(desc, kr, v)
     M = num_blocks(desc)
-    ks = np.empty((desc.B, desc.H, M, desc.D))
+    ks = np.empty((desc.B, kv_heads(desc), M, desc.D))
     vs = np.empty_like(ks)
     lib().ork_summaries(C.byref(desc), _ptr(_i32(slot)), _ptr(kr), _ptr(v), _ptr(ks), _ptr(vs))
     return ks, vs
@@ -161,12 +183,19 @@ def summaries_centre(desc, slot, k, v):
     """Summary-centre variant: mean of the UNROTATED keys k, rotated once at
     the block centre; values as in summaries()."""
     k, v = _f64(k), _f64(v)
+    _check_kv(desc, k, v)
     M = num_blocks(desc)
-    ks = np.empty((desc.B, desc.H, M, desc.D))
+    ks = np.empty((desc.B, kv_heads(desc), M, desc.D))
     vs = np.empty_like(ks)
     lib().ork_summaries_centre(C.byref(desc), _ptr(_i32(slot)), _ptr(k), _ptr(v), _ptr(ks),
                                _ptr(vs))
     return ks, vs
+
+
+def _check_kv(desc, *xs):
+    for x in xs:
+        if x.shape != (desc.B, desc.N, kv_heads(desc), desc.D):
+            raise ValueError(f"K/V shape {x.shape}: expected [B, N, Hkv, D]")
 
 
 def _rows(rows, N):
@@ -178,17 +207,24 @@ def _rows(rows, N):
 
 def local(desc, coords, slot, qr, kr, v, rows=None):
     r, n = _rows(rows, desc.N)
+    kr, v = _f64(kr), _f64(v)
+    _check_kv(desc, kr, v)
     out = np.empty((desc.B, n, desc.H, desc.D))
     lib().ork_local(C.byref(desc), _ptr(_i32(coords)), _ptr(_i32(slot)), _ptr(_f64(qr)),
-                    _ptr(_f64(kr)), _ptr(_f64(v)), _ptr(r), n, _ptr(out))
+                    _ptr(kr), _ptr(v), _ptr(r), n, _ptr(out))
     return out
 
 
 def global_(desc, coords, qr, ks, vs, rows=None):
     r, n = _rows(rows, desc.N)
+    ks, vs = _f64(ks), _f64(vs)
+    M = num_blocks(desc)
+    for x in (ks, vs):
+        if x.shape != (desc.B, kv_heads(desc), M, desc.D):
+            raise ValueError(f"summary shape {x.shape}: expected [B, Hkv, M, D]")
     out = np.empty((desc.B, n, desc.H, desc.D))
-    lib().ork_global(C.byref(desc), _ptr(_i32(coords)), _ptr(_f64(qr)), _ptr(_f64(ks)),
-                     _ptr(_f64(vs)), _ptr(r), n, _ptr(out))
+    lib().ork_global(C.byref(desc), _ptr(_i32(coords)), _ptr(_f64(qr)), _ptr(ks),
+                     _ptr(vs), _ptr(r), n, _ptr(out))
     return out
 
 

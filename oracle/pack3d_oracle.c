@@ -32,6 +32,13 @@
  *   5. mix            a tokenwise gate combines the two branches (paper
  *                     summary §3.3, §4.4)
  *
+ * Grouped key/value heads (GQA/MQA): keys, values and therefore the block
+ * summaries exist per KV head (project page Ch. 3, Contract 2, which counts
+ * summaries per KV head; paper summary §D.1, KV groups). With Hkv KV heads
+ * and H query heads (H a multiple of Hkv), query head h reads KV head
+ * floor(h / (H / Hkv)): consecutive query heads form a group. Hkv == H is
+ * ordinary multi-head attention, Hkv == 1 multi-query attention.
+ *
  * Readings taken where the pages are silent or garbled (the displayed
  * formulas did not survive): contiguous z|y|x channel chunks of D/3 per axis,
  * interleaved (2p, 2p+1) planes, theta_p = base^(-2p/(D/3)), integer 0-based
@@ -67,6 +74,7 @@ typedef struct {
   double rope_base;  /* 10000 in every workload */
   double scale;      /* <= 0 selects 1/sqrt(D) */
   int32_t exclusion; /* 0 none, 1 own block, 2 blocks meeting the neighbourhood */
+  int32_t Hkv;       /* key/value heads; 0 means H */
 } ork_desc;
 
 enum { ORK_OK = 0, ORK_ERR_ARG = -1, ORK_ERR_RANGE = -2, ORK_ERR_DUP = -3 };
@@ -78,6 +86,10 @@ int ork_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Number of key/value heads, and the KV head that query head h reads. */
+static int kv_heads(const ork_desc *d) { return d->Hkv > 0 ? d->Hkv : d->H; }
+static int kv_of(const ork_desc *d, int h) { return h / (d->H / kv_heads(d)); }
 
 static double scale_of(const ork_desc *d) {
   return d->scale > 0 ? d->scale : 1.0 / sqrt((double)d->D);
@@ -198,10 +210,11 @@ void ork_rope_sequence(const ork_desc *d, const double *x, double *y) {
  * in canonical within-block slot order r = ((z%bz)*by + y%by)*bx + x%bx; the
  * summary key is the mean of the members' ROTATED keys, the summary value the
  * mean of their values. Sites that are off-grid (partial edge blocks) or
- * empty do not count. kr, v: [B, N, H, D]; ks, vs: [B, H, M, D]. */
+ * empty do not count. Summaries exist per KV head. kr, v: [B, N, Hkv, D];
+ * ks, vs: [B, Hkv, M, D]. */
 void ork_summaries(const ork_desc *d, const int32_t *slot, const double *kr, const double *v,
                    double *ks, double *vs) {
-  const int D = d->D, H = d->H, M = ork_num_blocks(d);
+  const int D = d->D, H = kv_heads(d), M = ork_num_blocks(d);
   const int My = blocks_along(d, 1), Mx = blocks_along(d, 2);
   const int bz = d->block[0], by = d->block[1], bx = d->block[2];
 #pragma omp parallel for collapse(2) schedule(static)
@@ -245,7 +258,7 @@ void ork_summaries(const ork_desc *d, const int32_t *slot, const double *kr, con
 void ork_summaries_centre(const ork_desc *d, const int32_t *slot, const double *k,
                           const double *v, double *ks, double *vs) {
   ork_summaries(d, slot, k, v, ks, vs); /* plain means of the unrotated keys */
-  const int D = d->D, H = d->H, M = ork_num_blocks(d), da = D / 3, P = da / 2;
+  const int D = d->D, H = kv_heads(d), M = ork_num_blocks(d), da = D / 3, P = da / 2;
   const int My = blocks_along(d, 1), Mx = blocks_along(d, 2);
 #pragma omp parallel for collapse(2) schedule(static)
   for (int b = 0; b < d->B; b++) {
@@ -285,10 +298,11 @@ static double dot(const double *a, const double *b, int n) {
  * (rows == NULL: all N). Logits s*<q~_i, k~_j> over the valid neighbours in
  * offset order, softmax with the maximum subtracted, then the weighted sum of
  * the neighbours' (unrotated) values. Self is always valid, so the set is
- * never empty. out: [B, nrows, H, D]. */
+ * never empty. Query head h reads KV head kv_of(h). qr: [B, N, H, D];
+ * kr, v: [B, N, Hkv, D]; out: [B, nrows, H, D]. */
 void ork_local(const ork_desc *d, const int32_t *coords, const int32_t *slot, const double *qr,
                const double *kr, const double *v, const int32_t *rows, int nrows, double *out) {
-  const int D = d->D, H = d->H;
+  const int D = d->D, H = d->H, Hk = kv_heads(d);
   const double s = scale_of(d);
   if (!rows) nrows = d->N;
 #pragma omp parallel for collapse(2) schedule(static)
@@ -302,7 +316,7 @@ void ork_local(const ork_desc *d, const int32_t *coords, const int32_t *slot, co
         double logit[27], mx = -INFINITY;
         for (int k = 0; k < 27; k++) {
           if (nb[k] < 0) continue;
-          logit[k] = s * dot(q, kr + (((int64_t)b * d->N + nb[k]) * H + h) * D, D);
+          logit[k] = s * dot(q, kr + (((int64_t)b * d->N + nb[k]) * Hk + kv_of(d, h)) * D, D);
           if (logit[k] > mx) mx = logit[k];
         }
         double den = 0.0;
@@ -313,7 +327,7 @@ void ork_local(const ork_desc *d, const int32_t *coords, const int32_t *slot, co
         for (int k = 0; k < 27; k++) {
           if (nb[k] < 0) continue;
           double p = exp(logit[k] - mx) / den;
-          const double *vj = v + (((int64_t)b * d->N + nb[k]) * H + h) * D;
+          const double *vj = v + (((int64_t)b * d->N + nb[k]) * Hk + kv_of(d, h)) * D;
           for (int c = 0; c < D; c++) o[c] += p * vj[c];
         }
       }
@@ -340,10 +354,11 @@ static int excluded(const ork_desc *d, const int32_t *c, int m) {
 /* Step 4. Query-to-summary attention: logits s*<q~_i, ks_m> over every
  * summary m (minus the excluded ones) in block-id order, softmax with the
  * maximum subtracted, weighted sum of the summary values. If every summary is
- * excluded the branch output is zero. out: [B, nrows, H, D]. */
+ * excluded the branch output is zero. Query head h reads the summaries of KV
+ * head kv_of(h). qr: [B, N, H, D]; ks, vs: [B, Hkv, M, D]; out: [B, nrows, H, D]. */
 void ork_global(const ork_desc *d, const int32_t *coords, const double *qr, const double *ks,
                 const double *vs, const int32_t *rows, int nrows, double *out) {
-  const int D = d->D, H = d->H, M = ork_num_blocks(d);
+  const int D = d->D, H = d->H, Hk = kv_heads(d), M = ork_num_blocks(d);
   const double s = scale_of(d);
   if (!rows) nrows = d->N;
 #pragma omp parallel
@@ -361,7 +376,7 @@ void ork_global(const ork_desc *d, const int32_t *coords, const double *qr, cons
               logit[m] = -INFINITY;
               continue;
             }
-            logit[m] = s * dot(q, ks + (((int64_t)b * H + h) * M + m) * D, D);
+            logit[m] = s * dot(q, ks + (((int64_t)b * Hk + kv_of(d, h)) * M + m) * D, D);
             if (logit[m] > mx) mx = logit[m];
           }
           double *o = out + (((int64_t)b * nrows + t) * H + h) * D;
@@ -373,7 +388,7 @@ void ork_global(const ork_desc *d, const int32_t *coords, const double *qr, cons
           for (int m = 0; m < M; m++) {
             if (logit[m] == -INFINITY) continue;
             double p = exp(logit[m] - mx) / den;
-            const double *vm = vs + (((int64_t)b * H + h) * M + m) * D;
+            const double *vm = vs + (((int64_t)b * Hk + kv_of(d, h)) * M + m) * D;
             for (int c = 0; c < D; c++) o[c] += p * vm[c];
           }
         }

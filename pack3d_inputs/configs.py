@@ -21,6 +21,11 @@ class Workload:
     packing: str             # packing of the primary run
     repack: str              # packing of the equivariance check
     rope_base: float = 10000.0
+    Hkv: int = 0             # key/value heads (grouped-query attention); 0 means H
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv if self.Hkv > 0 else self.H
 
     @property
     def N(self) -> int:

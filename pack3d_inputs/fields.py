@@ -54,16 +54,17 @@ def _draw(rng, shape, values, grid):
 
 
 def make_fields(w, values=None, shape_override=None):
-    """Q, K, V [B, sites, H, D] and gate logits G [B, sites, H], fp32 arrays
-    in raster site order (bf16-representable when the workload is bf16).
-    Gate logits are iid N(0,1) for every workload."""
+    """Q [B, sites, H, D], K and V [B, sites, Hkv, D] and gate logits G
+    [B, sites, H], fp32 arrays in raster site order (bf16-representable when
+    the workload is bf16). Gate logits are iid N(0,1) for every workload."""
     values = values or w.values
     B, H, D = w.B, w.H, w.D
     N = w.N
     out = []
     for name in ("q", "k", "v"):
         rng = np.random.Generator(np.random.PCG64(w.seed(name)))
-        out.append(_draw(rng, (B, N, H, D), values, w.grid))
+        heads = H if name == "q" else w.kv_heads
+        out.append(_draw(rng, (B, N, heads, D), values, w.grid))
     rng = np.random.Generator(np.random.PCG64(w.seed("g")))
     out.append(rng.standard_normal((B, N, H), dtype=np.float32))
     if w.dtype == "bf16":

@@ -62,12 +62,14 @@ def dense_masked_attention(qr, kr, v, mask, scale):
 
 
 def torch_sdpa(qr, ks, vs, scale, mask=None):
-    """qr [B,N,H,D], ks/vs [B,H,M,D] -> [B,N,H,D] via torch SDPA in float64."""
+    """qr [B,N,H,D], ks/vs [B,Hkv,M,D] -> [B,N,H,D] via torch SDPA in float64
+    (with Hkv < H, torch's own grouped-query head mapping)."""
     q = torch.from_numpy(np.ascontiguousarray(qr.transpose(0, 2, 1, 3)))
     k = torch.from_numpy(np.ascontiguousarray(ks))
     v = torch.from_numpy(np.ascontiguousarray(vs))
     am = None if mask is None else torch.from_numpy(mask)
-    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=am, scale=scale)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=am, scale=scale,
+                                                         enable_gqa=k.shape[1] != q.shape[1])
     return o.numpy().transpose(0, 2, 1, 3)
 
 

@@ -103,6 +103,24 @@ def pin_summary_centre():
     return True
 
 
+def pin_gqa():
+    # H = 4 query heads over 2 KV heads: torch SDPA's grouped mapping for the
+    # global branch, dense attention over K/V repeated per group for the local one
+    d0, c, q, _, _, _ = _setup(H=4)
+    rng = np.random.default_rng(3)
+    k, v = (rng.standard_normal((1, d0.N, 2, d0.D)) for _ in range(2))
+    d = oracle.make_desc(1, d0.N, 4, d0.D, tuple(d0.grid), tuple(d0.block), kv_heads=2)
+    slot, _, _ = oracle.index(d, c)
+    qr, kr = oracle.rope_axial(d, c, q), oracle.rope_axial(d, c, k)
+    ks, vs = oracle.summaries(d, slot, kr, v)
+    s = 1 / np.sqrt(d.D)
+    if not np.allclose(oracle.global_(d, c, qr, ks, vs), torch_sdpa(qr, ks, vs, s), atol=1e-12):
+        return False
+    ref = dense_masked_attention(rotate_all(c, q), rotate_all(c, np.repeat(k, 2, axis=2)),
+                                 np.repeat(v, 2, axis=2), chebyshev_mask(c), s)
+    return np.allclose(oracle.local(d, c, slot, qr, kr, v), ref, atol=1e-12)
+
+
 MUTANTS = [
     ("rope_sin_sign", "yr[c0 + 1] = x0 * sn + x1 * cs;", "yr[c0 + 1] = -x0 * sn + x1 * cs;", pin_rope),
     ("rope_frequency", "pow(d->rope_base, -2.0 * p / (double)da)", "pow(d->rope_base, -2.0 * p / (double)D)", pin_rope),
@@ -114,8 +132,10 @@ MUTANTS = [
     ("local_drop_self", "if (nb[k] < 0) continue;\n          logit[k]", "if (nb[k] < 0 || k == 13) continue;\n          logit[k]", pin_local),
     ("summary_count", "ko[c] /= count;", "ko[c] /= (count + 1);", pin_summaries),
     ("summary_block_origin", "int oz = (m / (My * Mx)) * bz, oy = ((m / Mx) % My) * by, ox = (m % Mx) * bx;", "int oz = (m / (My * Mx)) * bz, oy = (m % My) * by, ox = ((m / My) % Mx) * bx;", pin_summaries),
-    ("global_summary_stride", "logit[m] = s * dot(q, ks + (((int64_t)b * H + h) * M + m) * D, D);", "logit[m] = s * dot(q, ks + (((int64_t)b * M + m) * H + h) * D, D);", pin_global),
-    ("global_value_head", "const double *vm = vs + (((int64_t)b * H + h) * M + m) * D;", "const double *vm = vs + (((int64_t)b * H + 0) * M + m) * D;", pin_global),
+    ("global_summary_stride", "logit[m] = s * dot(q, ks + (((int64_t)b * Hk + kv_of(d, h)) * M + m) * D, D);", "logit[m] = s * dot(q, ks + (((int64_t)b * M + m) * Hk + kv_of(d, h)) * D, D);", pin_global),
+    ("global_value_head", "const double *vm = vs + (((int64_t)b * Hk + kv_of(d, h)) * M + m) * D;", "const double *vm = vs + (((int64_t)b * Hk + 0) * M + m) * D;", pin_global),
+    ("kv_group_modulo", "static int kv_of(const ork_desc *d, int h) { return h / (d->H / kv_heads(d)); }", "static int kv_of(const ork_desc *d, int h) { return h % kv_heads(d); }", pin_gqa),
+    ("local_kv_head_ignored", "logit[k] = s * dot(q, kr + (((int64_t)b * d->N + nb[k]) * Hk + kv_of(d, h)) * D, D);", "logit[k] = s * dot(q, kr + (((int64_t)b * d->N + nb[k]) * Hk + 0) * D, D);", pin_gqa),
     ("centre_extent", "centre[a] = o[a] + 0.5 * (extent - 1);", "centre[a] = o[a] + 0.5 * extent;", pin_summary_centre),
     ("centre_unclipped", "int extent = d->grid[a] - o[a] < d->block[a] ? d->grid[a] - o[a] : d->block[a];", "int extent = d->block[a];", pin_summary_centre),
     ("mix_swapped", "out[base + c] = (1.0 - g) * oloc[base + c] + g * oglob[base + c];", "out[base + c] = g * oloc[base + c] + (1.0 - g) * oglob[base + c];", pin_mix),
@@ -124,7 +144,7 @@ MUTANTS = [
 
 def test_unmodified_oracle_passes_every_pin():
     for f in (pin_rope, pin_neighbours, pin_local, pin_summaries, pin_global, pin_mix,
-              pin_summary_centre):
+              pin_summary_centre, pin_gqa):
         assert f(), f.__name__
 
 
