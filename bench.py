@@ -17,6 +17,7 @@ timed on a bounded sample of the same workload on this host's cores.
   python bench.py --copy-calibration    # plain device copy, for counter scaling
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -38,18 +39,19 @@ def algorithmic(w, es=2):
     """Algorithmic work per launch of each stage: what the method must read,
     write or compute once (bytes / flops), not what a kernel happens to move."""
     B, N, H, D, M = w.B, w.N, w.H, w.D, w.M
-    row = H * D * es
+    row = H * D * es              # a token's query (or output) row
+    kvrow = w.kv_heads * D * es   # a token's key (or value) row
     return {
         # coords (12 B/token) read, slot map (4 B/site) written, RoPE table
         "index": {"bytes": N * 12 + N * 4},
-        # K and V read once, slot map read, summaries written
-        "summarize": {"bytes": B * N * 2 * row + N * 4 + B * M * 2 * row},
+        # K and V read once, slot map read, summaries (per KV head) written
+        "summarize": {"bytes": B * N * 2 * kvrow + N * 4 + B * M * 2 * kvrow},
         # Q read, O_glob written, coords read, summaries read once; 4*D flops
-        # per (token, head, summary) pair (QK^T and PV)
-        "global": {"bytes": B * N * 2 * row + N * 12 + B * M * 2 * row,
+        # per (token, query head, summary) pair (QK^T and PV)
+        "global": {"bytes": B * N * 2 * row + N * 12 + B * M * 2 * kvrow,
                    "flops": 4.0 * B * H * N * M * D},
         # Q, K, V read, O_glob and gate read (fused mix), O written, slot map
-        "local_mix": {"bytes": B * N * (5 * row + H * es) + N * 4},
+        "local_mix": {"bytes": B * N * (3 * row + 2 * kvrow + H * es) + N * 4},
     }
 
 
@@ -76,7 +78,8 @@ def cpu_baseline(w, coords, q, k, v, g, target_s=15.0):
     import numpy as np
 
     import oracle
-    od = oracle.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block, rope_base=w.rope_base)
+    od = oracle.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block, rope_base=w.rope_base,
+                          kv_heads=w.kv_heads)
     rng = np.random.default_rng(0)
     # two short probes separate the fixed cost (rotations, summaries) from the
     # per-token cost, to size the sample for ~target_s of work
@@ -124,6 +127,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summary-centre", action="store_true",
                     help="summary-centre variant: pool unrotated keys, rotate at the block centre")
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="grouped key/value heads (GQA/MQA) for the workload; 0 keeps H")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the PACK3D "
@@ -142,6 +147,8 @@ def main():
     import pack3d_inputs as pi
 
     w = pi.workload(args.workload)
+    if args.kv_heads:
+        w = dataclasses.replace(w, Hkv=args.kv_heads)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     es = 2 if w.dtype == "bf16" else 4
     coords = pi.packing_coords(w.grid, w.packing, block=w.block, seed=w.seed("perm"))
@@ -150,7 +157,7 @@ def main():
     dc = torch.from_numpy(coords).to(dev)
     dq, dk, dv, dg = (torch.from_numpy(a).to(dev).to(dt).contiguous() for a in (q, k, v, g))
     d = gas.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block, dtype=dt, rope_base=w.rope_base,
-                      summary_centre=args.summary_centre)
+                      summary_centre=args.summary_centre, kv_heads=w.kv_heads)
     ws = torch.empty(gas.pack3d_workspace_bytes(d), dtype=torch.uint8, device=dev)
     out = torch.empty_like(dq)
     nev = 2 * gas.PACK3D_NUM_STAGES
@@ -200,6 +207,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "grid_zyx": list(w.grid), "batch": w.B, "heads": w.H,
+                   "kv_heads": w.kv_heads,
                    "head_dim": w.D, "block": list(w.block), "summaries": w.M,
                    "tokens": w.tokens, "packing": w.packing, "values": w.values,
                    "summary_rope": "centre" if args.summary_centre else "token"},

@@ -11,7 +11,7 @@ from ._lib import (PACK3D_BF16, PACK3D_EXCL_NEIGHBOURHOOD_BLOCKS, PACK3D_EXCL_NO
                    PACK3D_EXCL_OWN_BLOCK, PACK3D_F32, PACK3D_NUM_STAGES, PACK3D_VALIDATE,
                    PACK3D_EXACT_SOFTMAX, PACK3D_SUMMARY_CENTRE,
                    EXPORTED_SYMBOLS, LIB_PATH, Desc, Pack3DError, library)
-from .ops import (make_desc, pack3d_block_summarize, pack3d_forward, pack3d_geometry_bytes,
+from .ops import (kv_heads, make_desc, pack3d_block_summarize, pack3d_forward, pack3d_geometry_bytes,
                   pack3d_geometry_layout, pack3d_global_attn, pack3d_index_build,
                   pack3d_local_attn, pack3d_mix, pack3d_num_summaries, pack3d_rope_coords,
                   pack3d_workspace_bytes, slot_map_view, ksum_from_rows, ksum_shape,
@@ -22,7 +22,7 @@ library()  # load now: no silent fallback when the HIP library is absent
 __all__ = [
     "PACK3D_BF16", "PACK3D_F32", "PACK3D_EXCL_NONE", "PACK3D_EXCL_OWN_BLOCK",
     "PACK3D_EXCL_NEIGHBOURHOOD_BLOCKS", "PACK3D_VALIDATE", "PACK3D_EXACT_SOFTMAX", "PACK3D_SUMMARY_CENTRE", "PACK3D_NUM_STAGES",
-    "EXPORTED_SYMBOLS", "LIB_PATH", "Desc", "Pack3DError", "library", "make_desc",
+    "EXPORTED_SYMBOLS", "LIB_PATH", "Desc", "Pack3DError", "library", "kv_heads", "make_desc",
     "pack3d_block_summarize", "pack3d_forward", "pack3d_geometry_bytes", "pack3d_geometry_layout",
     "pack3d_global_attn", "pack3d_index_build", "pack3d_local_attn", "pack3d_mix",
     "pack3d_num_summaries", "pack3d_rope_coords", "pack3d_workspace_bytes", "slot_map_view",

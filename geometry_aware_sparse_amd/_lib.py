@@ -4,6 +4,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libpack3d.so")
 
+ABI_VERSION = 2  # layout of Desc below; the library must report the same
 PACK3D_F32 = 0
 PACK3D_BF16 = 1
 PACK3D_EXCL_NONE = 0
@@ -35,7 +36,7 @@ class Desc(C.Structure):
     _fields_ = [("B", C.c_int32), ("N", C.c_int32), ("H", C.c_int32), ("D", C.c_int32),
                 ("grid", C.c_int32 * 3), ("block", C.c_int32 * 3), ("rope_base", C.c_float),
                 ("scale", C.c_float), ("dtype", C.c_int32), ("exclusion", C.c_int32),
-                ("flags", C.c_uint32)]
+                ("flags", C.c_uint32), ("kv_heads", C.c_int32)]
 
 
 _P = C.c_void_p
@@ -72,5 +73,8 @@ def library():
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
+        if L.pack3d_abi_version() != ABI_VERSION:
+            raise ImportError(f"{LIB_PATH} reports ABI {L.pack3d_abi_version()}, the binding "
+                              f"expects {ABI_VERSION}: rebuild the library")
         _lib = L
     return _lib

@@ -25,6 +25,9 @@ int make_geo(const pack3d_desc *d, Geo *g) {
   if (!isfinite(d->scale)) return PACK3D_ERR_INVALID_ARG;
   if (d->flags & ~(PACK3D_VALIDATE | PACK3D_EXACT_SOFTMAX | PACK3D_SUMMARY_CENTRE))
     return PACK3D_ERR_INVALID_ARG;
+  if (d->kv_heads < 0) return PACK3D_ERR_INVALID_ARG;
+  const int hkv = d->kv_heads > 0 ? d->kv_heads : d->H;
+  if (d->H % hkv != 0) return PACK3D_ERR_SHAPE;
   for (int a = 0; a < 3; a++)
     if (d->grid[a] <= 0 || d->block[a] <= 0) return PACK3D_ERR_SHAPE;
   if (d->D % 6 != 0) return PACK3D_ERR_SHAPE;
@@ -39,6 +42,8 @@ int make_geo(const pack3d_desc *d, Geo *g) {
   g->N = d->N;
   g->H = d->H;
   g->D = d->D;
+  g->Hkv = hkv;
+  g->G = d->H / hkv;
   g->Z = d->grid[0];
   g->Y = d->grid[1];
   g->X = d->grid[2];
@@ -67,14 +72,14 @@ size_t geometry_bytes(const Geo &g) {
   return align_up((size_t)g.table_off + (size_t)(g.Z + g.Y + g.X + 1) * g.P * 8);
 }
 
-// k_sum [B, H, Mp/32, Dp/8, 32, 8] and v_sum [B, H, Mp/8, D, 8],
+// k_sum [B, Hkv, Mp/32, Dp/8, 32, 8] and v_sum [B, Hkv, Mp/8, D, 8],
 // Mp = 32*ceil(M/32), Dp = 8*ceil(D/8)
 size_t ksum_bytes(const Geo &g, int dtype) {
-  return align_up((size_t)g.B * g.H * ((g.M + 31) / 32 * 32) * ((g.D + 7) / 8 * 8) *
+  return align_up((size_t)g.B * g.Hkv * ((g.M + 31) / 32 * 32) * ((g.D + 7) / 8 * 8) *
                   elem_size(dtype));
 }
 size_t vsum_bytes(const Geo &g, int dtype) {
-  return align_up((size_t)g.B * g.H * ((g.M + 31) / 32 * 32) * g.D * elem_size(dtype));
+  return align_up((size_t)g.B * g.Hkv * ((g.M + 31) / 32 * 32) * g.D * elem_size(dtype));
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PACK3D_OK : PACK3D_ERR_HIP; }
@@ -99,7 +104,7 @@ const char *pack3d_strerror(int status) {
   switch (status) {
     case PACK3D_OK: return "success";
     case PACK3D_ERR_INVALID_ARG: return "invalid argument (null pointer, non-positive size or bad enum)";
-    case PACK3D_ERR_SHAPE: return "invalid shape (N != Z*Y*X, D not a multiple of 6, block < 1, or size limits)";
+    case PACK3D_ERR_SHAPE: return "invalid shape (N != Z*Y*X, D not a multiple of 6, block < 1, H not a multiple of kv_heads, or size limits)";
     case PACK3D_ERR_WORKSPACE: return "workspace too small";
     case PACK3D_ERR_UNSUPPORTED: return "dtype / head-dim / exclusion combination not built";
     case PACK3D_ERR_HIP: return "HIP runtime or launch failure";

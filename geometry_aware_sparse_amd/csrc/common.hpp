@@ -19,6 +19,8 @@ typedef __attribute__((address_space(3))) void *lds_ptr;
 // kernels by value.
 struct Geo {
   int B, N, H, D;
+  int Hkv;        // key/value heads; query head h reads KV head h / G
+  int G;          // query heads per KV head, H / Hkv
   int Z, Y, X;
   int bz, by, bx;
   int Mz, My, Mx;

@@ -116,8 +116,9 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
   const int hi = lane >> 5;  // which half of the wave
   const int l32 = lane & 31;
   const int M32 = (g.M + 31) / 32;                       // summaries padded to Mp = 32*M32
-  const int64_t kbase = ((int64_t)b * g.H + h) * M32;      // k_sum [B,H,M32,D/8,32,8]
-  const int64_t vbase = ((int64_t)b * g.H + h) * M32 * 4;  // v_sum [B,H,Mp/8,D,8]
+  const int64_t bk = (int64_t)b * g.Hkv + h / g.G;         // the KV head query head h reads
+  const int64_t kbase = bk * M32;                          // k_sum [B,Hkv,M32,D/8,32,8]
+  const int64_t vbase = bk * M32 * 4;                      // v_sum [B,Hkv,Mp/8,D,8]
 
   // Query fragments: lane holds channels 16c + 8*hi .. +7 of its query,
   // rotated at the token's own coordinate, scaled, rounded to bf16. A token

@@ -37,8 +37,9 @@ __global__ __launch_bounds__(kNT) void k_global_valu(Geo g, const void *geom,
   bool cok = false;  // off-grid coordinate: zero query, zero output row
   const float2 *tab = rope_table(geom, g);
   const int Mp = (g.M + 31) / 32 * 32;
-  const int64_t kbase = ((int64_t)b * g.H + h) * (Mp / 32);  // k_sum [B,H,Mp/32,D/8,32,8]
-  const int64_t vbase = ((int64_t)b * g.H + h) * (Mp / 8);   // v_sum [B,H,Mp/8,D,8]
+  const int64_t bk = (int64_t)b * g.Hkv + h / g.G;           // the KV head query head h reads
+  const int64_t kbase = bk * (Mp / 32);  // k_sum [B,Hkv,Mp/32,D/8,32,8]
+  const int64_t vbase = bk * (Mp / 8);   // v_sum [B,Hkv,Mp/8,D,8]
 
   float qv[D];
   int c3[3] = {0, 0, 0};

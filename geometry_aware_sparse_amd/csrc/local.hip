@@ -3,8 +3,8 @@
 // optionally fused with the tokenwise mix (paper summary §3.3).
 //
 // Queries are tiled in grid space: a workgroup owns a TZ x TY x TX box of
-// sites for one (batch, head) and stages the box plus a one-site halo of
-// RoPE-rotated keys and raw values in LDS, gathering each site's token
+// sites for one (batch, query head) and stages the box plus a one-site halo
+// of RoPE-rotated keys and raw values of that head's KV head in LDS, gathering each site's token
 // through the coordinate-to-slot map (so any packing is legal input). One
 // thread per query then takes the 27 offsets in canonical order: logits,
 // maximum, exp2, weighted sum, all in fp32 -- no neighbour tensor is ever
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(TZ *TY *TX) void k_local(Geo g, const void *geom, c
     if (ch == 0) sSlot[hs] = j;
     float kv[CW], vv[CW];
     if (j >= 0) {
-      const int64_t off = ((bN + j) * g.H + h) * D + ch * CW;
+      const int64_t off = ((bN + j) * g.Hkv + h / g.G) * D + ch * CW;  // KV head of query head h
       load_n<T, CW>(k + off, kv);
       load_n<T, CW>(v + off, vv);
       const int c3[3] = {z, y, x};
@@ -243,7 +243,7 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_local_pair(
   for (int r = 0; r < RS; r++) {
     const int e = min((int)threadIdx.x + r * NT, NCK - 1);
     const int hs = e / CPS, ch = e % CPS;
-    const int64_t off = ((bN + max(sSlot[hs], 0)) * g.H + h) * D + ch * 8;
+    const int64_t off = ((bN + max(sSlot[hs], 0)) * g.Hkv + h / g.G) * D + ch * 8;  // KV head of h
     kraw[r] = *reinterpret_cast<const bf16x8 *>(k + off);
     __builtin_amdgcn_global_load_lds(v + off, (lds_ptr)&sV[(wbase + r * NT) * 8], 16, 0, 0);
   }

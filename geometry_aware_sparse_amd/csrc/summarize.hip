@@ -64,14 +64,14 @@ __global__ __launch_bounds__(512) void k_summarize(Geo g, const void *geom, cons
   const int32_t *slot = slot_map(geom, g);
   const float2 *tab = rope_table(geom, g);
   const int da = g.D / 3;
-  const int NC = g.H * g.D / CW;        // channel chunks per token row
+  const int NC = g.Hkv * g.D / CW;        // channel chunks per token row
   const int CPT = blockDim.x / 8;       // chunk lanes per block
   const int s = threadIdx.x / CPT;      // block of the group owned by this thread
   const int c0 = threadIdx.x % CPT;
   const int m = 8 * g8 + s;
   const int mz = m / (g.My * g.Mx), my = (m / g.Mx) % g.My, mx = m % g.Mx;
   const int o3[3] = {mz * g.bz, my * g.by, mx * g.bx};
-  const int64_t bh0 = (int64_t)b * g.H;
+  const int64_t bh0 = (int64_t)b * g.Hkv;
 
   // members of all 8 blocks, in passes of kMaxMembers / 8 per block
   const int per = kMaxMembers / 8;
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(512) void k_summarize(Geo g, const void *geom, cons
         cnt++;
         const int rr = r0 + r;
         const int c3[3] = {o3[0] + rr / (g.by * g.bx), o3[1] + (rr / g.bx) % g.by, o3[2] + rr % g.bx};
-        const int64_t off = (((int64_t)b * g.N + j) * g.H + h) * g.D + d0;
+        const int64_t off = (((int64_t)b * g.N + j) * g.Hkv + h) * g.D + d0;
         float kx[CW], vx[CW];
         if constexpr (CW == 8 && sizeof(T) == 2) {
           const bf16x8 kr = *reinterpret_cast<const bf16x8 *>(k + off);
@@ -157,15 +157,15 @@ __global__ __launch_bounds__(512) void k_summarize(Geo g, const void *geom, cons
   }
   __syncthreads();
   // v_sum: one 16-byte (bf16) chunk per (head, channel)
-  for (int e = threadIdx.x; e < g.H * g.D; e += blockDim.x) {
+  for (int e = threadIdx.x; e < g.Hkv * g.D; e += blockDim.x) {
     const int h = e / g.D, d = e % g.D;
     T *dst = vsb + (((bh0 + h) * (Mp / 8) + g8) * g.D + d) * 8;
 #pragma unroll
     for (int u = 0; u < 8; u++) dst[u] = from_f32<T>(s_vt[e * 8 + u]);
   }
   // padding channels D..Dp of k_sum are zero
-  for (int e = threadIdx.x; e < 8 * g.H * (Dp - g.D); e += blockDim.x) {
-    const int ss = e / (g.H * (Dp - g.D)), rem = e % (g.H * (Dp - g.D));
+  for (int e = threadIdx.x; e < 8 * g.Hkv * (Dp - g.D); e += blockDim.x) {
+    const int ss = e / (g.Hkv * (Dp - g.D)), rem = e % (g.Hkv * (Dp - g.D));
     const int h = rem / (Dp - g.D), d = g.D + rem % (Dp - g.D), mm = 8 * g8 + ss;
     ks[((((bh0 + h) * (Mp / 32) + mm / 32) * (Dp / 8) + d / 8) * 32 + mm % 32) * 8 + d % 8] =
         from_f32<T>(0.0f);
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(512) void k_summarize_b8(Geo g, const void *geom, c
                                                        const bf16 *v, bf16 *ks, bf16 *vsb,
                                                        int nrow) {
   extern __shared__ float s_dyn[];
-  const int NC = g.H * g.D / 8;          // 16-byte chunks per token row
+  const int NC = g.Hkv * g.D / 8;          // 16-byte chunks per token row
   const int NT = 8 * NC;
   const int per = min(g.vol, kMaxMembers / 8);  // members staged per pass and block
   const int P = g.P;
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(512) void k_summarize_b8(Geo g, const void *geom, c
 #pragma unroll
       for (int t = 0; t < kBatch; t++) {
         jj[t] = q0 + t < nr ? s_slot[s * nr + q0 + t] : -1;
-        const int64_t off = ((rowoff + max(jj[t], 0)) * g.H + h) * g.D + d0;
+        const int64_t off = ((rowoff + max(jj[t], 0)) * g.Hkv + h) * g.D + d0;
         kr[t] = *reinterpret_cast<const bf16x8 *>(k + off);
         vr[t] = *reinterpret_cast<const bf16x8 *>(v + off);
       }
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(512) void k_summarize_b8(Geo g, const void *geom, c
     s_vt[(u * NC + c) * 9 + s] = cnt > 0 ? va[u] / (float)cnt : 0.0f;
   }
   {  // m < Mp always: the grid covers Mp / 8 groups
-    const int64_t bh = (int64_t)b * g.H + h;
+    const int64_t bh = (int64_t)b * g.Hkv + h;
     *reinterpret_cast<bf16x8 *>(ks + ((bh * (Mp / 32) + m / 32) * (g.D / 8) + d0 / 8) * 256 +
                                 (m % 32) * 8) = ko;
   }
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(512) void k_summarize_b8(Geo g, const void *geom, c
     bf16x8 o;
 #pragma unroll
     for (int q = 0; q < 8; q++) o[q] = (bf16)s_vt[(u * NC + cc) * 9 + q];
-    *reinterpret_cast<bf16x8 *>(vsb + ((((int64_t)b * g.H + hh) * (Mp / 8) + g8) * g.D + d) * 8) = o;
+    *reinterpret_cast<bf16x8 *>(vsb + ((((int64_t)b * g.Hkv + hh) * (Mp / 8) + g8) * g.D + d) * 8) = o;
   }
 }
 
@@ -335,9 +335,9 @@ namespace {
 template <typename T, int CW>
 hipError_t run_summarize(const Geo &g, const void *geom, const void *k, const void *v, void *ks,
                          void *vs, hipStream_t s) {
-  const int NC = g.H * g.D / CW;
+  const int NC = g.Hkv * g.D / CW;
   const int cpt = NC < 64 ? NC : 64;  // chunk lanes per block
-  const size_t lds = (size_t)g.H * g.D * 8 * sizeof(float);
+  const size_t lds = (size_t)g.Hkv * g.D * 8 * sizeof(float);
   dim3 grid((unsigned)((g.M + 31) / 32 * 4), (unsigned)g.B);
   auto kern = (g.flags & PACK3D_SUMMARY_CENTRE) ? k_summarize<T, CW, true> : k_summarize<T, CW, false>;
   hipLaunchKernelGGL(kern, grid, dim3(8 * cpt), lds, s, g, geom, static_cast<const T *>(k),
@@ -354,11 +354,11 @@ hipError_t launch_summarize(const Geo &g, int dtype, const void *geom, const voi
     const int nrow = g.bz + g.by + g.bx;
     const int per = g.vol < kMaxMembers / 8 ? g.vol : kMaxMembers / 8;
     const size_t lds = (size_t)9 * per * 4 + 8 + (size_t)8 * nrow * g.P * 8 +
-                       (size_t)8 * (g.H * g.D / 8) * 9 * 4;
-    if (lds <= 48 * 1024 && g.H * g.D <= 512 && g.bz < 1024 && g.by < 1024 && g.bx < 1024) {
+                       (size_t)8 * (g.Hkv * g.D / 8) * 9 * 4;
+    if (lds <= 48 * 1024 && g.Hkv * g.D <= 512 && g.bz < 1024 && g.by < 1024 && g.bx < 1024) {
       dim3 grid((unsigned)((g.M + 31) / 32 * 4), (unsigned)g.B);
       auto kern = (g.flags & PACK3D_SUMMARY_CENTRE) ? k_summarize_b8<true> : k_summarize_b8<false>;
-      hipLaunchKernelGGL(kern, grid, dim3(g.H * g.D), lds, s, g, geom,
+      hipLaunchKernelGGL(kern, grid, dim3(g.Hkv * g.D), lds, s, g, geom,
                          static_cast<const bf16 *>(k), static_cast<const bf16 *>(v),
                          static_cast<bf16 *>(ks), static_cast<bf16 *>(vs), nrow);
       return hipGetLastError();

@@ -11,7 +11,10 @@ _DTYPES = {PACK3D_F32: torch.float32, PACK3D_BF16: torch.bfloat16}
 
 
 def make_desc(B, N, H, D, grid, block, dtype=PACK3D_BF16, rope_base=10000.0, scale=0.0,
-              exclusion=0, validate=False, exact_softmax=False, summary_centre=False):
+              exclusion=0, validate=False, exact_softmax=False, summary_centre=False,
+              kv_heads=None):
+    """kv_heads: key/value heads (grouped-query attention); None means H.
+    Query head h reads KV head h // (H // kv_heads)."""
     if isinstance(dtype, torch.dtype):
         dtype = {torch.float32: PACK3D_F32, torch.bfloat16: PACK3D_BF16}[dtype]
     d = Desc()
@@ -24,7 +27,12 @@ def make_desc(B, N, H, D, grid, block, dtype=PACK3D_BF16, rope_base=10000.0, sca
     d.exclusion = int(exclusion)
     d.flags = ((PACK3D_VALIDATE if validate else 0) | (PACK3D_EXACT_SOFTMAX if exact_softmax else 0)
                | (PACK3D_SUMMARY_CENTRE if summary_centre else 0))
+    d.kv_heads = 0 if kv_heads is None else int(kv_heads)
     return d
+
+
+def kv_heads(desc):
+    return desc.kv_heads if desc.kv_heads > 0 else desc.H
 
 
 def _check(rc, what):
@@ -58,6 +66,10 @@ def _bnhd(desc):
     return (desc.B, desc.N, desc.H, desc.D)
 
 
+def _bnkd(desc):
+    return (desc.B, desc.N, kv_heads(desc), desc.D)
+
+
 def pack3d_num_summaries(desc):
     m = library().pack3d_num_summaries(C.byref(desc))
     _check(0 if m >= 0 else int(m), "pack3d_num_summaries")
@@ -88,16 +100,16 @@ def _mp(M):
 
 
 def ksum_shape(desc, M=None):
-    """k_sum: [B, H, Mp/32, Dp/8, 32, 8], Mp = 32*ceil(M/32), Dp = 8*ceil(D/8);
-    key summary (m, d) at [b, h, m // 32, d // 8, m % 32, d % 8]."""
+    """k_sum: [B, Hkv, Mp/32, Dp/8, 32, 8], Mp = 32*ceil(M/32), Dp = 8*ceil(D/8);
+    key summary (m, d) of KV head h at [b, h, m // 32, d // 8, m % 32, d % 8]."""
     M = pack3d_num_summaries(desc) if M is None else M
-    return (desc.B, desc.H, _mp(M) // 32, (desc.D + 7) // 8, 32, 8)
+    return (desc.B, kv_heads(desc), _mp(M) // 32, (desc.D + 7) // 8, 32, 8)
 
 
 def vsum_shape(desc, M=None):
-    """v_sum: [B, H, Mp/8, D, 8]; value summary (m, d) at [b, h, m // 8, d, m % 8]."""
+    """v_sum: [B, Hkv, Mp/8, D, 8]; value summary (m, d) at [b, h, m // 8, d, m % 8]."""
     M = pack3d_num_summaries(desc) if M is None else M
-    return (desc.B, desc.H, _mp(M) // 8, desc.D, 8)
+    return (desc.B, kv_heads(desc), _mp(M) // 8, desc.D, 8)
 
 
 def ksum_to_rows(ks, M, D):
@@ -154,7 +166,13 @@ def pack3d_index_build(desc, coords, geom=None, neighbours=False, blocks=False, 
 
 
 def pack3d_rope_coords(desc, coords, x, out=None):
+    """x: [B, N, H, D], or [B, N, Hkv, D] (keys; rotated through a descriptor
+    whose head count is Hkv)."""
     _need(coords, "coords", desc, (desc.N, 3), torch.int32)
+    if x.dim() == 4 and x.shape[2] == kv_heads(desc) and x.shape[2] != desc.H:
+        d = Desc.from_buffer_copy(desc)
+        d.H, d.kv_heads = kv_heads(desc), 0
+        desc = d
     _need(x, "x", desc, _bnhd(desc))
     out = torch.empty_like(x) if out is None else out
     _need(out, "out", desc, _bnhd(desc))
@@ -164,8 +182,8 @@ def pack3d_rope_coords(desc, coords, x, out=None):
 
 
 def pack3d_block_summarize(desc, geom, k, v):
-    _need(k, "k", desc, _bnhd(desc))
-    _need(v, "v", desc, _bnhd(desc))
+    _need(k, "k", desc, _bnkd(desc))
+    _need(v, "v", desc, _bnkd(desc))
     M = pack3d_num_summaries(desc)
     ks = torch.empty(ksum_shape(desc, M), dtype=k.dtype, device=k.device)
     vs = torch.empty(vsum_shape(desc, M), dtype=k.dtype, device=k.device)
@@ -175,8 +193,9 @@ def pack3d_block_summarize(desc, geom, k, v):
 
 
 def pack3d_local_attn(desc, geom, q, k, v, out=None):
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, desc, _bnhd(desc))
+    _need(q, "q", desc, _bnhd(desc))
+    _need(k, "k", desc, _bnkd(desc))
+    _need(v, "v", desc, _bnkd(desc))
     out = torch.empty_like(q) if out is None else out
     _need(out, "out", desc, _bnhd(desc))
     _check(library().pack3d_local_attn(C.byref(desc), _ptr(geom), _ptr(q), _ptr(k), _ptr(v),
@@ -213,8 +232,9 @@ def pack3d_forward(desc, coords, q, k, v, gate, out=None, workspace=None, stage_
     """The whole operator. stage_events: None or a list of
     2*PACK3D_NUM_STAGES torch.cuda.Event(enable_timing=True) objects."""
     _need(coords, "coords", desc, (desc.N, 3), torch.int32)
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, desc, _bnhd(desc))
+    _need(q, "q", desc, _bnhd(desc))
+    _need(k, "k", desc, _bnkd(desc))
+    _need(v, "v", desc, _bnkd(desc))
     _need(gate, "gate", desc, (desc.B, desc.N, desc.H))
     out = torch.empty_like(q) if out is None else out
     _need(out, "out", desc, _bnhd(desc))

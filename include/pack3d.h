@@ -17,8 +17,9 @@
  *  - Pointers named q, k, v, gate, o, x, k_sum, v_sum, geom, coords, ws and
  *    the *_out arrays are DEVICE pointers owned by the caller; the library
  *    never allocates, frees or retains device memory.
- *  - Layouts (row-major, C order):
- *      q, k, v, o, o_local, o_global, x : [B, N, H, D] in packed memory order
+ *  - Layouts (row-major, C order), with Hkv = desc->kv_heads (H when 0):
+ *      q, o, o_local, o_global, x       : [B, N, H, D] in packed memory order
+ *      k, v                             : [B, N, Hkv, D], same packing
  *      gate                             : [B, N, H] (gate logits G)
  *      coords                           : int32 [N, 3] = (z, y, x) of the
  *                                         token stored at each position; one
@@ -28,11 +29,17 @@
  *                                         blocked for the matrix-core kernel,
  *                                         with M padded to Mp = 32*ceil(M/32)
  *                                         (padding slots are zero):
- *        k_sum [B, H, Mp/32, Dp/8, 32, 8]: key summary (m, d) at
- *                                         [b, h, m/32, d/8, m%32, d%8], with
- *                                         D padded to Dp = 8*ceil(D/8) (zero)
- *        v_sum [B, H, Mp/8, D, 8]       : value summary (m, d) at
+ *        k_sum [B, Hkv, Mp/32, Dp/8, 32, 8]: key summary (m, d) of KV
+ *                                         head h at [b, h, m/32, d/8, m%32,
+ *                                         d%8], with D padded to
+ *                                         Dp = 8*ceil(D/8) (zero)
+ *        v_sum [B, Hkv, Mp/8, D, 8]     : value summary (m, d) at
  *                                         [b, h, m/8, d, m%8]
+ *  - Grouped key/value heads (GQA, MQA): keys, values and the summaries
+ *    exist per KV head (project page Ch. 3, Contract 2 counts summaries per
+ *    KV head; paper summary §D.1 shares work within KV groups). Query head h
+ *    reads KV head h / (H / Hkv): consecutive query heads form a group.
+ *    Hkv == H is multi-head attention, Hkv == 1 multi-query attention.
  *    Element type of q/k/v/gate/o/x/k_sum/v_sum is desc->dtype.
  *  - stream is a hipStream_t passed as void* (NULL = default stream). Every
  *    call only enqueues work on it and returns; results are ready when the
@@ -65,12 +72,12 @@
 extern "C" {
 #endif
 
-#define PACK3D_ABI_VERSION 1
+#define PACK3D_ABI_VERSION 2
 
 typedef enum pack3d_status {
   PACK3D_OK = 0,
   PACK3D_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad enum */
-  PACK3D_ERR_SHAPE = -2,       /* N != Z*Y*X, D % 6 != 0, block < 1, size overflow */
+  PACK3D_ERR_SHAPE = -2,       /* N != Z*Y*X, D % 6, block < 1, H % kv_heads, overflow */
   PACK3D_ERR_WORKSPACE = -3,   /* workspace smaller than pack3d_workspace_bytes */
   PACK3D_ERR_UNSUPPORTED = -4, /* dtype / D / exclusion combination not built */
   PACK3D_ERR_HIP = -5,         /* a HIP launch or runtime call failed */
@@ -113,7 +120,8 @@ typedef struct pack3d_desc {
   float scale;         /* softmax scale; <= 0 selects 1/sqrt(D)                  */
   int32_t dtype;       /* pack3d_dtype of every float tensor                     */
   int32_t exclusion;   /* pack3d_exclusion                                       */
-  uint32_t flags;      /* PACK3D_VALIDATE                                        */
+  uint32_t flags;      /* PACK3D_VALIDATE | PACK3D_EXACT_SOFTMAX | ..._CENTRE     */
+  int32_t kv_heads;    /* key/value heads Hkv; 0 selects H; H % Hkv == 0         */
 } pack3d_desc;
 
 /* Library ABI version (PACK3D_ABI_VERSION). */
@@ -165,13 +173,15 @@ int pack3d_index_build(const pack3d_desc *desc, const int32_t *coords, void *geo
  * Computed in fp32 from cos/sin evaluated in double; bf16 output is rounded
  * to nearest even. The other entry points take UNROTATED q and k and rotate
  * them as they load them; this call exists for tests and for callers that
- * want rotated tensors. */
+ * want rotated tensors. x has desc->H heads; to rotate keys with fewer KV
+ * heads, pass a descriptor whose H is the KV head count. */
 int pack3d_rope_coords(const pack3d_desc *desc, const int32_t *coords, const void *x,
                        void *x_rot, void *stream);
 
 /* Rotate-then-pool block summaries (project page Ch. 3, "Rotate first, then
- * pool"; paper summary §3.2, §B.5): k_sum[b,h,m] = mean over the members j of
- * block m of R(c_j) k[b,j,h]; v_sum[b,h,m] = mean of v[b,j,h]. Members are
+ * pool"; paper summary §3.2, §B.5): for every KV head h,
+ * k_sum[b,h,m] = mean over the members j of block m of R(c_j) k[b,j,h];
+ * v_sum[b,h,m] = mean of v[b,j,h]. Members are
  * summed in fp32 in within-block-slot order, so the result does not depend on
  * the packing. geom must hold metadata built by pack3d_index_build for the
  * same desc. Blocks with no member present get zeros. */
@@ -181,7 +191,8 @@ int pack3d_block_summarize(const pack3d_desc *desc, const void *geom, const void
 /* Exact local attention (project page Ch. 3, Contract 1; paper summary §3.2,
  * §3.5): for each token i, head h, softmax over the valid tokens j of the
  * 3x3x3 coordinate neighbourhood of scale * <R(c_i) q_i, R(c_j) k_j>, then
- * the weighted sum of the unrotated v_j. fp32 softmax and accumulation;
+ * the weighted sum of the unrotated v_j (k and v of KV head h / (H / Hkv)).
+ * fp32 softmax and accumulation;
  * neighbours are visited in the fixed offset order. o_local may not alias
  * q, k or v. */
 int pack3d_local_attn(const pack3d_desc *desc, const void *geom, const void *q, const void *k,
@@ -190,7 +201,8 @@ int pack3d_local_attn(const pack3d_desc *desc, const void *geom, const void *q, 
 /* Query-to-summary attention (project page Ch. 3, Contract 2; paper summary
  * §3.5, §B.10): for each token i, head h, softmax over the summaries m (all
  * of them, or those desc->exclusion leaves) of
- * scale * <R(c_i) q_i, k_sum[b,h,m]>, then the weighted sum of v_sum[b,h,m];
+ * scale * <R(c_i) q_i, k_sum[b,hk,m]>, then the weighted sum of
+ * v_sum[b,hk,m], hk = h / (H / Hkv);
  * zero when every summary is excluded. bf16 with D in {48, 96} and no
  * exclusion runs on bf16 matrix cores with an fp32 online softmax; every
  * other case runs an fp32 vector kernel. o_global may not alias q. */

@@ -37,9 +37,10 @@ def desc_pair(w, exclusion=0, validate=False):
     import geometry_aware_sparse_amd as gas
     d = gas.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block,
                       dtype=gas.PACK3D_BF16 if w.dtype == "bf16" else gas.PACK3D_F32,
-                      rope_base=w.rope_base, exclusion=exclusion, validate=validate)
+                      rope_base=w.rope_base, exclusion=exclusion, validate=validate,
+                      kv_heads=w.kv_heads)
     od = oracle.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block, rope_base=w.rope_base,
-                          exclusion=exclusion)
+                          exclusion=exclusion, kv_heads=w.kv_heads)
     return d, od
 
 

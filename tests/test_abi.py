@@ -33,7 +33,9 @@ def test_library_exports_every_declared_symbol(gas):
 
 def test_version_and_strerror(gas):
     lib = gas.library()
-    assert lib.pack3d_abi_version() == 1
+    assert lib.pack3d_abi_version() == 2
+    # the ctypes descriptor matches the C struct: kv_heads is the last field
+    assert C.sizeof(gas.Desc) == 4 * 4 + 4 * 6 + 4 * 2 + 4 * 4
     for code in (0, -1, -2, -3, -4, -5, -6, -99):
         assert lib.pack3d_strerror(code)
 
@@ -41,15 +43,18 @@ def test_version_and_strerror(gas):
 def _desc(gas, **kw):
     base = dict(B=1, N=512, H=2, D=48, grid=(8, 8, 8), block=(2, 2, 2), dtype=gas.PACK3D_BF16)
     base.update(kw)
-    return gas.make_desc(base["B"], base["N"], base["H"], base["D"], base["grid"], base["block"],
-                         dtype=base["dtype"], rope_base=base.get("rope_base", 10000.0),
-                         exclusion=base.get("exclusion", 0))
+    d = gas.make_desc(base["B"], base["N"], base["H"], base["D"], base["grid"], base["block"],
+                      dtype=base["dtype"], rope_base=base.get("rope_base", 10000.0),
+                      exclusion=base.get("exclusion", 0))
+    d.kv_heads = base.get("kv_heads", 0)
+    return d
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(N=500), -2), (dict(D=40), -2), (dict(block=(0, 2, 2)), -2), (dict(grid=(8, 8, -8)), -2),
     (dict(B=0), -1), (dict(H=-1), -1), (dict(dtype=7), -1), (dict(exclusion=5), -1),
     (dict(rope_base=0.0), -1), (dict(H=64, D=48), -2),
+    (dict(H=6, kv_heads=4), -2), (dict(kv_heads=-1), -1),
 ])
 def test_bad_descriptors_are_rejected(gas, kw, code):
     d = _desc(gas, **kw)
@@ -85,10 +90,15 @@ def test_geometry_and_workspace_sizes(gas):
     so, to, nb = gas.pack3d_geometry_layout(d)
     assert so == 256 and so % 256 == 0 and to % 256 == 0
     assert to >= so + 4 * 512
-    assert nb >= to + (8 + 8 + 8) * (48 // 6) * 8
+    assert nb >= to + (8 + 8 + 8 + 1) * (48 // 6) * 8  # a row per coordinate, one half-angle row
     M = gas.pack3d_num_summaries(d)
     assert M == 64
     assert gas.pack3d_workspace_bytes(d) >= nb + 2 * (1 * 2 * M * 48 * 2)
+    # summaries are stored per KV head: 4 query heads over 2 KV heads need
+    # the workspace of 2 heads, less than 4
+    ws = gas.pack3d_workspace_bytes
+    assert ws(_desc(gas, H=4, kv_heads=2)) == ws(_desc(gas, H=2)) < ws(_desc(gas, H=4))
+    assert ws(_desc(gas, H=4, kv_heads=4)) == ws(_desc(gas, H=4))
     with pytest.raises(gas.Pack3DError, match="SHAPE"):
         gas.pack3d_num_summaries(_desc(gas, N=7))
 

@@ -23,6 +23,11 @@ SMALL = [
      "random", "block_morton"),
     (W(112, "d96", (6, 8, 12), 1, 2, 96, (2, 2, 4), "bf16", "smooth", "block", "raster"),
      "block", "raster"),
+    # grouped key/value heads
+    (W(113, "gqa4x2", (10, 13, 19), 1, 4, 48, (2, 2, 2), "bf16", "iid", "random", "raster", Hkv=2),
+     "random", "block_morton"),
+    (W(114, "mqa_f32", (6, 7, 9), 2, 3, 24, (2, 2, 2), "f32", "iid", "raster", "random", Hkv=1),
+     "raster", "random"),
 ]
 
 

@@ -26,6 +26,14 @@ CASES = [
     W(105, "f32_d96", (4, 5, 6), 1, 1, 96, (2, 2, 2), "f32", "iid", "random", "raster"),
     W(106, "bf16_d24_peaked", (6, 6, 6), 1, 2, 24, (3, 3, 3), "bf16", "smooth", "block", "raster"),
     W(107, "single_site", (1, 1, 1), 1, 1, 48, (1, 1, 1), "bf16", "iid", "raster", "raster"),
+    # grouped key/value heads (GQA, MQA): query head h reads KV head h // (H // Hkv)
+    W(110, "gqa4x2_bf16_d48", (10, 13, 19), 1, 4, 48, (2, 2, 2), "bf16", "iid", "random", "morton",
+      Hkv=2),
+    W(111, "mqa4_bf16_d96", (6, 9, 11), 1, 4, 96, (2, 3, 2), "bf16", "smooth", "morton", "raster",
+      Hkv=1),
+    W(112, "gqa6x3_f32_d24", (5, 7, 9), 2, 6, 24, (2, 2, 3), "f32", "iid", "block", "random", Hkv=3),
+    W(113, "gqa8x2_bf16_d48", (12, 16, 20), 1, 8, 48, (2, 2, 2), "bf16", "iid", "block", "random",
+      Hkv=2),
 ]
 IDS = [c.name for c in CASES]
 
@@ -103,9 +111,9 @@ def test_block_summarize(w):
     assert_close(w, host(gas.vsum_to_rows(vs, M)), ovs, "v_sum")
     # padding slots of the blocked layouts are zero
     Mp, Dp = (M + 31) // 32 * 32, (w.D + 7) // 8 * 8
-    krows = ks.permute(0, 1, 2, 4, 3, 5).reshape(w.B, w.H, Mp, Dp)
+    krows = ks.permute(0, 1, 2, 4, 3, 5).reshape(w.B, w.kv_heads, Mp, Dp)
     assert torch.count_nonzero(krows[:, :, :, w.D:]).item() == 0
-    vrows = vs.permute(0, 1, 2, 4, 3).reshape(w.B, w.H, Mp, w.D)
+    vrows = vs.permute(0, 1, 2, 4, 3).reshape(w.B, w.kv_heads, Mp, w.D)
     assert torch.count_nonzero(krows[:, :, M:]).item() == 0
     assert torch.count_nonzero(vrows[:, :, M:]).item() == 0
 
@@ -142,9 +150,9 @@ def test_global_attn(w):
 @pytest.mark.parametrize("w", CASES, ids=IDS)
 def test_mix(w):
     gas, w, d, od, coords, (q, k, v, g), dev, geom, _ = _setup(w)
-    a, b = dev["q"], dev["k"]
+    a, b = dev["q"], dev["q"].flip(1).contiguous()
     o = gas.pack3d_mix(d, dev["g"], a, b)
-    assert_close(w, host(o), oracle.mix(od, g, q, k), "mix")
+    assert_close(w, host(o), oracle.mix(od, g, q, q[:, ::-1]), "mix")
     # aliasing the output with an input is allowed
     a2 = a.clone()
     gas.pack3d_mix(d, dev["g"], a2, b, out=a2)
@@ -166,7 +174,8 @@ def test_forward(w):
 
 
 @pytest.mark.parametrize("mode", [1, 2], ids=["own_block", "neighbourhood_blocks"])
-@pytest.mark.parametrize("w", [CASES[0], CASES[2], CASES[4]], ids=[IDS[0], IDS[2], IDS[4]])
+@pytest.mark.parametrize("w", [CASES[0], CASES[2], CASES[4], CASES[9], CASES[11]],
+                         ids=[IDS[0], IDS[2], IDS[4], IDS[9], IDS[11]])
 def test_global_exclusion_readings(w, mode):
     import geometry_aware_sparse_amd as gas
     coords, q, k, v, g = inputs(w)
@@ -191,7 +200,7 @@ def test_all_summaries_excluded_gives_local_only_mix():
     assert torch.count_nonzero(og).item() == 0
 
 
-MFMA_CASES = [CASES[1], CASES[2], CASES[3], CASES[8]]
+MFMA_CASES = [CASES[1], CASES[2], CASES[3], CASES[8], CASES[9], CASES[10], CASES[12]]
 
 
 @pytest.mark.parametrize("w", MFMA_CASES, ids=[c.name for c in MFMA_CASES])
@@ -202,7 +211,7 @@ def test_global_exact_softmax_flag(w):
     coords, q, k, v, g = inputs(w)
     d, od = desc_pair(w)
     de = gas.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block, dtype=gas.PACK3D_BF16,
-                       exact_softmax=True)
+                       exact_softmax=True, kv_heads=w.kv_heads)
     dt = tdtype(w)
     dc, dq = to_dev(coords, torch.int32), to_dev(q, dt)
     geom, _, _, _ = gas.pack3d_index_build(d, dc)
@@ -260,15 +269,16 @@ def test_global_overflowing_scores_fall_back_per_query():
 # Summary-centre variant (paper summary §B.7, §B.8): keys pooled unrotated,
 # the mean rotated once at the block centre. Cases with even, odd and clipped
 # block extents, fp32 and bf16 (both pooling kernels).
-CENTRE_CASES = [CASES[0], CASES[1], CASES[2], CASES[3], CASES[4], CASES[5]]
+CENTRE_CASES = [CASES[0], CASES[1], CASES[2], CASES[3], CASES[4], CASES[5], CASES[9], CASES[11]]
 
 
 def _centre_pair(w):
     import geometry_aware_sparse_amd as gas
     d = gas.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block,
                       dtype=gas.PACK3D_BF16 if w.dtype == "bf16" else gas.PACK3D_F32,
-                      rope_base=w.rope_base, summary_centre=True)
-    od = oracle.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block, rope_base=w.rope_base)
+                      rope_base=w.rope_base, summary_centre=True, kv_heads=w.kv_heads)
+    od = oracle.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block, rope_base=w.rope_base,
+                          kv_heads=w.kv_heads)
     return d, od
 
 
@@ -302,3 +312,34 @@ def test_forward_centre(w):
                            to_dev(v, dt), to_dev(g, dt))
     ref = oracle.forward(od, coords, q, k, v, g, summary_rope="centre")
     assert_close(w, host(o), ref, "centre forward")
+
+
+GQA_CASES = [CASES[9], CASES[10], CASES[11], CASES[12]]
+
+
+@pytest.mark.parametrize("w", GQA_CASES, ids=[c.name for c in GQA_CASES])
+@pytest.mark.parametrize("centre", [False, True], ids=["token", "centre"])
+def test_gqa_equals_mha_over_repeated_kv_bitwise(w, centre):
+    """GQA through the library gives the same bits as multi-head attention
+    over K/V repeated per group (query head h -> KV head h // (H // Hkv)):
+    the same members, in the same order, with the same arithmetic."""
+    import geometry_aware_sparse_amd as gas
+    coords, q, k, v, g = inputs(w)
+    dt = tdtype(w)
+    G = w.H // w.kv_heads
+    dc, dq, dg = to_dev(coords, torch.int32), to_dev(q, dt), to_dev(g, dt)
+    args = dict(dtype=gas.PACK3D_BF16 if w.dtype == "bf16" else gas.PACK3D_F32,
+                rope_base=w.rope_base, summary_centre=centre)
+    dg_ = gas.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block, kv_heads=w.kv_heads, **args)
+    dm = gas.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block, **args)
+    og = gas.pack3d_forward(dg_, dc, dq, to_dev(k, dt), to_dev(v, dt), dg)
+    om = gas.pack3d_forward(dm, dc, dq, to_dev(np.repeat(k, G, axis=2), dt),
+                            to_dev(np.repeat(v, G, axis=2), dt), dg)
+    assert torch.equal(og, om)
+    # and the summaries of the grouped call are the repeated call's, one per KV head
+    geom, _, _, _ = gas.pack3d_index_build(dg_, dc)
+    ks, vs = gas.pack3d_block_summarize(dg_, geom, to_dev(k, dt), to_dev(v, dt))
+    ksm, vsm = gas.pack3d_block_summarize(dm, geom, to_dev(np.repeat(k, G, axis=2), dt),
+                                          to_dev(np.repeat(v, G, axis=2), dt))
+    assert ks.shape[1] == w.kv_heads and ksm.shape[1] == w.H
+    assert torch.equal(ks, ksm[:, ::G]) and torch.equal(vs, vsm[:, ::G])
