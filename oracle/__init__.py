@@ -50,6 +50,8 @@ def _load(path):
     L.ork_global.argtypes = [P] * 6 + [C.c_int, P]
     L.ork_mix.restype = None
     L.ork_mix.argtypes = [P] * 5 + [C.c_int, P]
+    L.ork_backward.restype = C.c_int
+    L.ork_backward.argtypes = [P] * 7 + [C.c_int] + [P] * 4
     return L
 
 
@@ -263,3 +265,30 @@ def forward(desc, coords, q, k, v, gate, rows=None, rope="axial", return_parts=F
     if return_parts:
         return o, dict(slot=slot, qr=qr, kr=kr, ks=ks, vs=vs, local=ol, glob=og)
     return o
+
+
+def backward(desc, coords, q, k, v, gate, dout, summary_rope="token"):
+    """Gradients (dq, dk, dv, dgate) of sum(dout * forward(...)) with respect
+    to the unrotated q, k, v and the gate logits, axial RoPE. summary_rope:
+    "token" or "centre" as in forward()."""
+    if summary_rope not in ("token", "centre"):
+        raise ValueError(summary_rope)
+    q, k, v, gate, dout = _f64(q), _f64(k), _f64(v), _f64(gate), _f64(dout)
+    _check_kv(desc, k, v)
+    for x, shp in ((q, (desc.B, desc.N, desc.H, desc.D)), (dout, (desc.B, desc.N, desc.H, desc.D)),
+                   (gate, (desc.B, desc.N, desc.H))):
+        if x.shape != shp:
+            raise ValueError(f"shape {x.shape}: expected {shp}")
+    dq, dout_ = np.empty_like(q), dout
+    dk, dv = np.empty_like(k), np.empty_like(v)
+    dgate = np.empty_like(gate)
+    rc = lib().ork_backward(C.byref(desc), _ptr(_i32(coords)), _ptr(q), _ptr(k), _ptr(v),
+                            _ptr(gate), _ptr(dout_), 1 if summary_rope == "centre" else 0,
+                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgate))
+    if rc == -2:
+        raise OracleError("coordinate out of range")
+    if rc == -3:
+        raise OracleError("duplicate coordinate")
+    if rc != 0:
+        raise OracleError(f"backward error {rc}")
+    return dq, dk, dv, dgate

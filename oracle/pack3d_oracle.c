@@ -249,6 +249,18 @@ void ork_summaries(const ork_desc *d, const int32_t *slot, const double *kr, con
   }
 }
 
+/* Block centre of block m: origin + (extent - 1) / 2 per axis, the extent
+ * clipped at the grid edge (a half-integer coordinate for an even extent). */
+static void block_centre(const ork_desc *d, int m, double *centre) {
+  const int My = blocks_along(d, 1), Mx = blocks_along(d, 2);
+  const int o[3] = {(m / (My * Mx)) * d->block[0], ((m / Mx) % My) * d->block[1],
+                    (m % Mx) * d->block[2]};
+  for (int a = 0; a < 3; a++) {
+    int extent = d->grid[a] - o[a] < d->block[a] ? d->grid[a] - o[a] : d->block[a];
+    centre[a] = o[a] + 0.5 * (extent - 1);
+  }
+}
+
 /* Summary-centre variant (paper summary §B.7, §B.8; project page Ch. 3, the
  * cheaper summary that pools unrotated keys and rotates the result once at a
  * representative coordinate). The keys k are the unrotated inputs; each
@@ -259,17 +271,11 @@ void ork_summaries_centre(const ork_desc *d, const int32_t *slot, const double *
                           const double *v, double *ks, double *vs) {
   ork_summaries(d, slot, k, v, ks, vs); /* plain means of the unrotated keys */
   const int D = d->D, H = kv_heads(d), M = ork_num_blocks(d), da = D / 3, P = da / 2;
-  const int My = blocks_along(d, 1), Mx = blocks_along(d, 2);
 #pragma omp parallel for collapse(2) schedule(static)
   for (int b = 0; b < d->B; b++) {
     for (int m = 0; m < M; m++) {
-      const int o[3] = {(m / (My * Mx)) * d->block[0], ((m / Mx) % My) * d->block[1],
-                        (m % Mx) * d->block[2]};
       double centre[3];
-      for (int a = 0; a < 3; a++) {
-        int extent = d->grid[a] - o[a] < d->block[a] ? d->grid[a] - o[a] : d->block[a];
-        centre[a] = o[a] + 0.5 * (extent - 1);
-      }
+      block_centre(d, m, centre);
       for (int h = 0; h < H; h++) {
         double *ko = ks + (((int64_t)b * H + h) * M + m) * D;
         for (int a = 0; a < 3; a++) {
@@ -413,4 +419,248 @@ void ork_mix(const ork_desc *d, const double *gate, const double *oloc, const do
         for (int c = 0; c < D; c++) out[base + c] = (1.0 - g) * oloc[base + c] + g * oglob[base + c];
       }
     }
+}
+
+/* ------------------------------------------------------------------------
+ * Backward of the whole operator: the gradients of a scalar loss with
+ * respect to q, k, v and the gate logits, given dout = dL/dO. The pages'
+ * operator is trained end to end and its backward follows the forward's
+ * access pattern (paper summary §1, §3.4); the steps below are the chain
+ * rule through steps 5, 4, 3, 2 and 1 in reverse order, each one the plain
+ * derivative of the forward step it undoes:
+ *
+ *   mix     g = sigmoid(G): dG = g (1 - g) <dO, O_glob - O_loc>,
+ *           dO_loc = (1 - g) dO, dO_glob = g dO
+ *   softmax attention (local over the neighbours, global over the allowed
+ *           summaries), P = softmax(s <q~, k>), O = sum P v:
+ *           dP_j = <dO, v_j>, Delta = sum_j P_j dP_j,
+ *           dS_j = P_j (dP_j - Delta), dq~ += s sum_j dS_j k_j,
+ *           dk_j += s dS_j q~, dv_j += P_j dO
+ *   pooling mean over the n_m members present: each member receives
+ *           dk_sum / n_m and dv_sum / n_m (token summaries: the rotated key
+ *           k~_j; centre summaries: R(centre)^T dk_sum / n_m on the
+ *           unrotated key)
+ *   RoPE    x~ = R(c) x is orthogonal: dx = R(c)^T dx~
+ *
+ * With grouped KV heads the key and value gradients of a KV head sum over
+ * its group of query heads. Inputs as in the forward (q [B,N,H,D],
+ * k, v [B,N,Hkv,D], gate [B,N,H]); dout, dq [B,N,H,D]; dk, dv [B,N,Hkv,D];
+ * dgate [B,N,H]. centre selects the summary-centre variant. Returns
+ * ORK_OK, or an index error (off-grid / duplicate coordinate).
+ */
+
+/* x~ = R(c) x (sign +1) or x = R(c)^T x~ (sign -1) on one [D] row at the
+ * real coordinate c (z, y, x). */
+static void rotate_row(const ork_desc *d, const double *c, const double *x, double *y, int sign) {
+  const int D = d->D, da = D / 3, P = da / 2;
+  for (int a = 0; a < 3; a++) {
+    for (int p = 0; p < P; p++) {
+      const double theta = pow(d->rope_base, -(2.0 * p) / (double)da);
+      const double cs = cos(c[a] * theta), sn = sign * sin(c[a] * theta);
+      const int ch = 2 * p + a * da; /* plane p of axis a: channels ch, ch + 1 */
+      const double x0 = x[ch], x1 = x[ch + 1];
+      y[ch] = x0 * cs - x1 * sn;
+      y[ch + 1] = x0 * sn + x1 * cs;
+    }
+  }
+}
+
+static void rotate_rows(const ork_desc *d, const int32_t *coords, int heads, const double *x,
+                        double *y, int sign) {
+#pragma omp parallel for schedule(static)
+  for (int64_t row = 0; row < (int64_t)d->B * d->N * heads; row++) {
+    int i = (int)((row / heads) % d->N);
+    double c[3] = {coords[3 * i], coords[3 * i + 1], coords[3 * i + 2]};
+    rotate_row(d, c, x + row * d->D, y + row * d->D, sign);
+  }
+}
+
+int ork_backward(const ork_desc *d, const int32_t *coords, const double *q, const double *k,
+                 const double *v, const double *gate, const double *dout, int centre,
+                 double *dq, double *dk, double *dv, double *dgate) {
+  const int B = d->B, N = d->N, H = d->H, Hk = kv_heads(d), D = d->D, M = ork_num_blocks(d);
+  const int G = H / Hk;
+  const double s = scale_of(d);
+  const int64_t nq = (int64_t)B * N * H * D, nk = (int64_t)B * N * Hk * D,
+                ns = (int64_t)B * Hk * M * D;
+  int64_t S = (int64_t)d->grid[0] * d->grid[1] * d->grid[2];
+  int32_t *slot = malloc(sizeof(int32_t) * S);
+  int rc = ork_index(d, coords, slot, NULL, NULL);
+  if (rc != ORK_OK) {
+    free(slot);
+    return rc;
+  }
+  double *qr = malloc(sizeof(double) * nq), *kr = malloc(sizeof(double) * nk);
+  double *ks = malloc(sizeof(double) * ns), *vs = malloc(sizeof(double) * ns);
+  double *ol = malloc(sizeof(double) * nq), *og = malloc(sizeof(double) * nq);
+  double *dol = malloc(sizeof(double) * nq), *dog = malloc(sizeof(double) * nq);
+  double *dqr = calloc(nq, sizeof(double)), *dkr = calloc(nk, sizeof(double));
+  double *dks = calloc(ns, sizeof(double)), *dvs = calloc(ns, sizeof(double));
+
+  /* forward values the derivatives need */
+  rotate_rows(d, coords, H, q, qr, +1);
+  rotate_rows(d, coords, Hk, k, kr, +1);
+  if (centre)
+    ork_summaries_centre(d, slot, k, v, ks, vs);
+  else
+    ork_summaries(d, slot, kr, v, ks, vs);
+  ork_local(d, coords, slot, qr, kr, v, NULL, 0, ol);
+  ork_global(d, coords, qr, ks, vs, NULL, 0, og);
+
+  /* mix */
+  for (int64_t r = 0; r < (int64_t)B * N * H; r++) {
+    double g = 1.0 / (1.0 + exp(-gate[r]));
+    const double *o0 = ol + r * D, *o1 = og + r * D, *dor = dout + r * D;
+    double acc = 0.0;
+    for (int c = 0; c < D; c++) {
+      acc += dor[c] * (o1[c] - o0[c]);
+      dol[r * D + c] = (1.0 - g) * dor[c];
+      dog[r * D + c] = g * dor[c];
+    }
+    dgate[r] = g * (1.0 - g) * acc;
+  }
+  for (int64_t e = 0; e < nk; e++) dv[e] = 0.0;
+
+  /* local attention; each (b, KV head) owns its key and value gradients */
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int b = 0; b < B; b++) {
+    for (int hk = 0; hk < Hk; hk++) {
+      for (int h = hk * G; h < (hk + 1) * G; h++) {
+        for (int i = 0; i < N; i++) {
+          int nb[27];
+          double logit[27], p[27], dp[27], mx = -INFINITY, den = 0.0, delta = 0.0;
+          const double *qi = qr + (((int64_t)b * N + i) * H + h) * D;
+          const double *doi = dol + (((int64_t)b * N + i) * H + h) * D;
+          double *dqi = dqr + (((int64_t)b * N + i) * H + h) * D;
+          for (int n = 0; n < 27; n++) {
+            nb[n] = neighbour(d, slot, coords + 3 * i, n);
+            if (nb[n] < 0) continue;
+            logit[n] = s * dot(qi, kr + (((int64_t)b * N + nb[n]) * Hk + hk) * D, D);
+            if (logit[n] > mx) mx = logit[n];
+          }
+          for (int n = 0; n < 27; n++)
+            if (nb[n] >= 0) den += exp(logit[n] - mx);
+          for (int n = 0; n < 27; n++) {
+            if (nb[n] < 0) continue;
+            p[n] = exp(logit[n] - mx) / den;
+            dp[n] = dot(doi, v + (((int64_t)b * N + nb[n]) * Hk + hk) * D, D);
+            delta += p[n] * dp[n];
+          }
+          for (int n = 0; n < 27; n++) {
+            if (nb[n] < 0) continue;
+            const double ds = p[n] * (dp[n] - delta);
+            const int64_t jo = (((int64_t)b * N + nb[n]) * Hk + hk) * D;
+            for (int c = 0; c < D; c++) {
+              dqi[c] += s * ds * kr[jo + c];
+              dkr[jo + c] += s * ds * qi[c];
+              dv[jo + c] += p[n] * doi[c];
+            }
+          }
+        }
+      }
+    }
+  }
+
+  /* global attention over the summaries */
+#pragma omp parallel
+  {
+    double *logit = malloc(sizeof(double) * (size_t)M);
+#pragma omp for collapse(2) schedule(static)
+    for (int b = 0; b < B; b++) {
+      for (int hk = 0; hk < Hk; hk++) {
+        for (int h = hk * G; h < (hk + 1) * G; h++) {
+          for (int i = 0; i < N; i++) {
+            const double *qi = qr + (((int64_t)b * N + i) * H + h) * D;
+            const double *doi = dog + (((int64_t)b * N + i) * H + h) * D;
+            double *dqi = dqr + (((int64_t)b * N + i) * H + h) * D;
+            const int64_t sb = ((int64_t)b * Hk + hk) * M;
+            double mx = -INFINITY, den = 0.0, delta = 0.0;
+            for (int m = 0; m < M; m++) {
+              logit[m] = excluded(d, coords + 3 * i, m) ? -INFINITY
+                                                         : s * dot(qi, ks + (sb + m) * D, D);
+              if (logit[m] > mx) mx = logit[m];
+            }
+            if (mx == -INFINITY) continue; /* every summary excluded: O_glob = 0 */
+            for (int m = 0; m < M; m++)
+              if (logit[m] != -INFINITY) den += exp(logit[m] - mx);
+            for (int m = 0; m < M; m++)
+              if (logit[m] != -INFINITY)
+                delta += exp(logit[m] - mx) / den * dot(doi, vs + (sb + m) * D, D);
+            for (int m = 0; m < M; m++) {
+              if (logit[m] == -INFINITY) continue;
+              const double pm = exp(logit[m] - mx) / den;
+              const double dt = pm * (dot(doi, vs + (sb + m) * D, D) - delta);
+              for (int c = 0; c < D; c++) {
+                dqi[c] += s * dt * ks[(sb + m) * D + c];
+                dks[(sb + m) * D + c] += s * dt * qi[c];
+                dvs[(sb + m) * D + c] += pm * doi[c];
+              }
+            }
+          }
+        }
+      }
+    }
+    free(logit);
+  }
+
+  /* pooling: each member present gets the block's gradient over n_m */
+  const int My = blocks_along(d, 1), Mx = blocks_along(d, 2);
+  const int bz = d->block[0], by = d->block[1], bx = d->block[2];
+  double *dkc = centre ? calloc(nk, sizeof(double)) : NULL; /* unrotated-key part */
+  int *members = malloc(sizeof(int) * (size_t)bz * by * bx);
+  double *gku = malloc(sizeof(double) * D);
+  for (int b = 0; b < B; b++) {
+    for (int m = 0; m < M; m++) {
+      const int oz = bz * (m / (My * Mx)), oy = by * ((m / Mx) % My), ox = bx * (m % Mx);
+      int count = 0;
+      for (int r = 0; r < bz * by * bx; r++) {
+        int z = oz + r / (by * bx), y = oy + (r / bx) % by, x = ox + r % bx;
+        if (z >= d->grid[0] || y >= d->grid[1] || x >= d->grid[2]) continue;
+        int j = slot[site_of(d, z, y, x)];
+        if (j >= 0) members[count++] = j;
+      }
+      if (count == 0) continue;
+      double cm[3];
+      block_centre(d, m, cm);
+      for (int hk = 0; hk < Hk; hk++) {
+        const double *gk = dks + (((int64_t)b * Hk + hk) * M + m) * D;
+        const double *gv = dvs + (((int64_t)b * Hk + hk) * M + m) * D;
+        if (centre) rotate_row(d, cm, gk, gku, -1);
+        for (int t = 0; t < count; t++) {
+          const int64_t jo = (((int64_t)b * N + members[t]) * Hk + hk) * D;
+          for (int c = 0; c < D; c++) {
+            if (centre)
+              dkc[jo + c] += gku[c] / count;
+            else
+              dkr[jo + c] += gk[c] / count;
+            dv[jo + c] += gv[c] / count;
+          }
+        }
+      }
+    }
+  }
+  free(members);
+  free(gku);
+
+  /* RoPE: back through the orthogonal rotations */
+  rotate_rows(d, coords, H, dqr, dq, -1);
+  rotate_rows(d, coords, Hk, dkr, dk, -1);
+  if (centre)
+    for (int64_t e = 0; e < nk; e++) dk[e] += dkc[e];
+
+  free(slot);
+  free(qr);
+  free(kr);
+  free(ks);
+  free(vs);
+  free(ol);
+  free(og);
+  free(dol);
+  free(dog);
+  free(dqr);
+  free(dkr);
+  free(dks);
+  free(dvs);
+  free(dkc);
+  return ORK_OK;
 }

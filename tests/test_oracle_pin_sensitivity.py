@@ -121,6 +121,32 @@ def pin_gqa():
     return np.allclose(oracle.local(d, c, slot, qr, kr, v), ref, atol=1e-12)
 
 
+def pin_backward():
+    # central differences of the forward on a tiny grouped case
+    grid, block = (3, 3, 2), (2, 2, 2)
+    c = pi.packing_coords(grid, "random", block=block, seed=2)
+    rng = np.random.default_rng(4)
+    N, H, Hkv, D = c.shape[0], 2, 1, 6
+    q, dout = (rng.standard_normal((1, N, H, D)) for _ in range(2))
+    k, v = (rng.standard_normal((1, N, Hkv, D)) for _ in range(2))
+    g = rng.standard_normal((1, N, H))
+    d = oracle.make_desc(1, N, H, D, grid, block, kv_heads=Hkv)
+    grads = oracle.backward(d, c, q, k, v, g, dout)
+    eps = 1e-5
+    for x, grad in zip((q, k, v, g), grads):
+        flat = x.reshape(-1)
+        for e in range(0, flat.size, 5):
+            keep = flat[e]
+            flat[e] = keep + eps
+            lp = float((dout * oracle.forward(d, c, q, k, v, g)).sum())
+            flat[e] = keep - eps
+            lm = float((dout * oracle.forward(d, c, q, k, v, g)).sum())
+            flat[e] = keep
+            if abs((lp - lm) / (2 * eps) - grad.reshape(-1)[e]) > 1e-7:
+                return False
+    return True
+
+
 MUTANTS = [
     ("rope_sin_sign", "yr[c0 + 1] = x0 * sn + x1 * cs;", "yr[c0 + 1] = -x0 * sn + x1 * cs;", pin_rope),
     ("rope_frequency", "pow(d->rope_base, -2.0 * p / (double)da)", "pow(d->rope_base, -2.0 * p / (double)D)", pin_rope),
@@ -138,13 +164,18 @@ MUTANTS = [
     ("local_kv_head_ignored", "logit[k] = s * dot(q, kr + (((int64_t)b * d->N + nb[k]) * Hk + kv_of(d, h)) * D, D);", "logit[k] = s * dot(q, kr + (((int64_t)b * d->N + nb[k]) * Hk + 0) * D, D);", pin_gqa),
     ("centre_extent", "centre[a] = o[a] + 0.5 * (extent - 1);", "centre[a] = o[a] + 0.5 * extent;", pin_summary_centre),
     ("centre_unclipped", "int extent = d->grid[a] - o[a] < d->block[a] ? d->grid[a] - o[a] : d->block[a];", "int extent = d->block[a];", pin_summary_centre),
+    ("bwd_local_no_delta", "const double ds = p[n] * (dp[n] - delta);", "const double ds = p[n] * dp[n];", pin_backward),
+    ("bwd_global_value_weight", "dvs[(sb + m) * D + c] += pm * doi[c];", "dvs[(sb + m) * D + c] += doi[c];", pin_backward),
+    ("bwd_rope_forward_turn", "rotate_rows(d, coords, H, dqr, dq, -1);", "rotate_rows(d, coords, H, dqr, dq, +1);", pin_backward),
+    ("bwd_pool_no_count", "dkr[jo + c] += gk[c] / count;", "dkr[jo + c] += gk[c];", pin_backward),
+    ("bwd_gate_derivative", "dgate[r] = g * (1.0 - g) * acc;", "dgate[r] = g * acc;", pin_backward),
     ("mix_swapped", "out[base + c] = (1.0 - g) * oloc[base + c] + g * oglob[base + c];", "out[base + c] = g * oloc[base + c] + (1.0 - g) * oglob[base + c];", pin_mix),
 ]
 
 
 def test_unmodified_oracle_passes_every_pin():
     for f in (pin_rope, pin_neighbours, pin_local, pin_summaries, pin_global, pin_mix,
-              pin_summary_centre, pin_gqa):
+              pin_summary_centre, pin_gqa, pin_backward):
         assert f(), f.__name__
 
 
