@@ -196,7 +196,7 @@ int pack3d_global_attn(const pack3d_desc *desc, const void *geom, const int32_t 
   if (rc) return rc;
   if (!geom || !coords || !q || !k_sum || !v_sum || !o_global) return PACK3D_ERR_INVALID_ARG;
   bool ok = false;
-  hipError_t e = launch_global(g, desc->dtype, geom, coords, q, k_sum, v_sum, o_global,
+  hipError_t e = launch_global(g, desc->dtype, geom, coords, q, k_sum, v_sum, o_global, nullptr,
                                static_cast<hipStream_t>(stream), &ok);
   if (!ok) return PACK3D_ERR_UNSUPPORTED;
   return hip_status(e);
@@ -212,9 +212,30 @@ int pack3d_mix(const pack3d_desc *desc, const void *gate, const void *o_local,
       launch_mix(g, desc->dtype, gate, o_local, o_global, o, static_cast<hipStream_t>(stream)));
 }
 
-int pack3d_forward(const pack3d_desc *desc, const int32_t *coords, const void *q, const void *k,
-                   const void *v, const void *gate, void *o, void *ws, size_t ws_bytes,
-                   void *stream, void *const *stage_events) {
+}  // extern "C"
+
+namespace {
+
+bool shape_supported(const pack3d_desc *desc, const Geo &g) {
+  const bool mfma = desc->dtype == PACK3D_BF16 && desc->exclusion == PACK3D_EXCL_NONE &&
+                    (g.D == 48 || g.D == 96);
+  const bool valu = g.D == 6 || g.D == 12 || g.D == 24 || g.D == 48 || g.D == 96;
+  return mfma || valu;
+}
+
+// saved = [O_glob [B, N, H, D] in dtype | lse_glob [B, N, H] fp32], 256-aligned
+size_t saved_oglob_bytes(const Geo &g, int dtype) {
+  return align_up((size_t)g.B * g.N * g.H * g.D * elem_size(dtype));
+}
+size_t saved_bytes(const Geo &g, int dtype) {
+  return saved_oglob_bytes(g, dtype) + align_up((size_t)g.B * g.N * g.H * 4);
+}
+
+// The forward pipeline; oglob / lse are where the global branch writes (o
+// itself and no lse for inference, the saved buffer for training).
+int forward_impl(const pack3d_desc *desc, const int32_t *coords, const void *q, const void *k,
+                 const void *v, const void *gate, void *o, void *oglob, float *lse, void *ws,
+                 size_t ws_bytes, void *stream, void *const *stage_events) {
   Geo g;
   int rc = make_geo(desc, &g);
   if (rc) return rc;
@@ -223,12 +244,7 @@ int pack3d_forward(const pack3d_desc *desc, const int32_t *coords, const void *q
                vbytes = vsum_bytes(g, desc->dtype);
   if (ws_bytes < gbytes + kbytes + vbytes) return PACK3D_ERR_WORKSPACE;
   // shape support is decided before anything is enqueued
-  {
-    const bool mfma = desc->dtype == PACK3D_BF16 && desc->exclusion == PACK3D_EXCL_NONE &&
-                      (g.D == 48 || g.D == 96);
-    const bool valu = g.D == 6 || g.D == 12 || g.D == 24 || g.D == 48 || g.D == 96;
-    if (!mfma && !valu) return PACK3D_ERR_UNSUPPORTED;
-  }
+  if (!shape_supported(desc, g)) return PACK3D_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char *base = static_cast<char *>(ws);
   void *geom = base;
@@ -247,14 +263,143 @@ int pack3d_forward(const pack3d_desc *desc, const int32_t *coords, const void *q
   if ((rc = hip_status(launch_summarize(g, desc->dtype, geom, k, v, ksum, vsum, s)))) return rc;
   if ((rc = mark(3))) return rc;
   if ((rc = mark(4))) return rc;
-  if ((rc = hip_status(launch_global(g, desc->dtype, geom, coords, q, ksum, vsum, o, s, &ok))))
+  if ((rc = hip_status(launch_global(g, desc->dtype, geom, coords, q, ksum, vsum, oglob, lse, s, &ok))))
     return rc;
   if (!ok) return PACK3D_ERR_UNSUPPORTED;
   if ((rc = mark(5))) return rc;
   if ((rc = mark(6))) return rc;
-  if ((rc = hip_status(launch_local(g, desc->dtype, geom, q, k, v, gate, o, o, s, &ok)))) return rc;
+  if ((rc = hip_status(launch_local(g, desc->dtype, geom, q, k, v, gate, oglob, o, s, &ok)))) return rc;
   if (!ok) return PACK3D_ERR_UNSUPPORTED;
   return mark(7);
+}
+
+// Backward workspace: geometry | k_sum | v_sum | fp32 intermediates
+struct BwdLayout {
+  size_t geom, ks, vs, qr, dog, delta_g, dqg, dks, dvs, lse_l, delta_l, total;
+};
+BwdLayout bwd_layout(const Geo &g, int dtype) {
+  BwdLayout L;
+  const size_t rows = (size_t)g.B * g.N * g.H;
+  const size_t sum = (size_t)g.B * g.Hkv * g.M * g.D * 4;
+  size_t off = 0;
+  auto take = [&](size_t n) { size_t at = off; off += align_up(n); return at; };
+  L.geom = take(geometry_bytes(g));
+  L.ks = take(ksum_bytes(g, dtype));
+  L.vs = take(vsum_bytes(g, dtype));
+  L.qr = take(rows * g.D * 4);
+  L.dog = take(rows * g.D * 4);
+  L.delta_g = take(rows * 4);
+  L.dqg = take(rows * g.D * 4);
+  L.dks = take(sum);
+  L.dvs = take(sum);
+  L.lse_l = take(rows * 4);
+  L.delta_l = take(rows * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pack3d_forward(const pack3d_desc *desc, const int32_t *coords, const void *q, const void *k,
+                   const void *v, const void *gate, void *o, void *ws, size_t ws_bytes,
+                   void *stream, void *const *stage_events) {
+  return forward_impl(desc, coords, q, k, v, gate, o, o, nullptr, ws, ws_bytes, stream,
+                      stage_events);
+}
+
+int pack3d_saved_bytes(const pack3d_desc *desc, size_t *bytes) {
+  Geo g;
+  if (!bytes) return PACK3D_ERR_INVALID_ARG;
+  int rc = make_geo(desc, &g);
+  if (rc) return rc;
+  *bytes = saved_bytes(g, desc->dtype);
+  return PACK3D_OK;
+}
+
+int pack3d_forward_train(const pack3d_desc *desc, const int32_t *coords, const void *q,
+                         const void *k, const void *v, const void *gate, void *o, void *saved,
+                         size_t saved_bytes_, void *ws, size_t ws_bytes, void *stream,
+                         void *const *stage_events) {
+  Geo g;
+  int rc = make_geo(desc, &g);
+  if (rc) return rc;
+  if (!saved) return PACK3D_ERR_INVALID_ARG;
+  if (saved_bytes_ < saved_bytes(g, desc->dtype)) return PACK3D_ERR_WORKSPACE;
+  char *sv = static_cast<char *>(saved);
+  return forward_impl(desc, coords, q, k, v, gate, o, sv,
+                      reinterpret_cast<float *>(sv + saved_oglob_bytes(g, desc->dtype)), ws,
+                      ws_bytes, stream, stage_events);
+}
+
+int pack3d_backward_workspace_bytes(const pack3d_desc *desc, size_t *bytes) {
+  Geo g;
+  if (!bytes) return PACK3D_ERR_INVALID_ARG;
+  int rc = make_geo(desc, &g);
+  if (rc) return rc;
+  *bytes = bwd_layout(g, desc->dtype).total;
+  return PACK3D_OK;
+}
+
+int pack3d_backward(const pack3d_desc *desc, const int32_t *coords, const void *q, const void *k,
+                    const void *v, const void *gate, const void *saved, size_t saved_bytes_,
+                    const void *dout, void *dq, void *dk, void *dv, void *dgate, void *ws,
+                    size_t ws_bytes, void *stream, void *const *stage_events) {
+  Geo g;
+  int rc = make_geo(desc, &g);
+  if (rc) return rc;
+  if (!coords || !q || !k || !v || !gate || !saved || !dout || !dq || !dk || !dv || !dgate || !ws)
+    return PACK3D_ERR_INVALID_ARG;
+  if (saved_bytes_ < saved_bytes(g, desc->dtype)) return PACK3D_ERR_WORKSPACE;
+  const BwdLayout L = bwd_layout(g, desc->dtype);
+  if (ws_bytes < L.total) return PACK3D_ERR_WORKSPACE;
+  if (!shape_supported(desc, g)) return PACK3D_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *base = static_cast<char *>(ws);
+  auto mark = [&](int idx) -> int {
+    if (!stage_events) return PACK3D_OK;
+    return hip_status(hipEventRecord(static_cast<hipEvent_t>(stage_events[idx]), s));
+  };
+  BwdArgs a;
+  a.geom = base + L.geom;
+  a.coords = coords;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.gate = gate;
+  a.dout = dout;
+  a.oglob = saved;
+  a.lse_g = reinterpret_cast<const float *>(static_cast<const char *>(saved) +
+                                            saved_oglob_bytes(g, desc->dtype));
+  a.ks = base + L.ks;
+  a.vs = base + L.vs;
+  a.qr = reinterpret_cast<float *>(base + L.qr);
+  a.dog = reinterpret_cast<float *>(base + L.dog);
+  a.delta_g = reinterpret_cast<float *>(base + L.delta_g);
+  a.dqg = reinterpret_cast<float *>(base + L.dqg);
+  a.dks = reinterpret_cast<float *>(base + L.dks);
+  a.dvs = reinterpret_cast<float *>(base + L.dvs);
+  a.lse_l = reinterpret_cast<float *>(base + L.lse_l);
+  a.delta_l = reinterpret_cast<float *>(base + L.delta_l);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dgate = dgate;
+  a.events = stage_events;
+  if ((rc = mark(0))) return rc;
+  if ((rc = hip_status(launch_index(g, coords, base + L.geom, nullptr, nullptr, nullptr, s))))
+    return rc;
+  if ((rc = validate_coords(desc, base + L.geom, s))) return rc;
+  if ((rc = hip_status(launch_summarize(g, desc->dtype, base + L.geom, k, v, base + L.ks,
+                                        base + L.vs, s))))
+    return rc;
+  if ((rc = mark(1))) return rc;
+  if ((rc = mark(2))) return rc;
+  bool ok = true;
+  if ((rc = hip_status(launch_backward(g, desc->dtype, a, s, &ok)))) return rc;
+  if (!ok) return PACK3D_ERR_UNSUPPORTED;
+  return mark(5);
 }
 
 }  // extern "C"

@@ -85,7 +85,7 @@ template <int D, int G, int TS>
 __global__ __launch_bounds__(256, 2) void k_global_mfma(
     Geo g, const void *geom, const int32_t *__restrict__ coords, const bf16 *__restrict__ q,
     const bf16 *__restrict__ ks, const bf16 *__restrict__ vsb, bf16 *__restrict__ out,
-    int ntiles) {
+    float *__restrict__ lse, int ntiles) {
   constexpr int DA = D / 3;
   constexpr int KD = D / 16;             // 16-deep steps of Ksum * Q~^T
   constexpr bool ONES = (D % 32) != 0;   // spare output rows carry the denominator
@@ -412,7 +412,11 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
     bad |= __shfl_xor(bad, 32);
     redo[gi] = cok[gi] && (force_exact || bad);
     any_redo = any_redo || redo[gi];
-    if (active[gi] && !redo[gi]) store_rows(gi, cok[gi] ? 1.0f / den : 0.f);
+    if (active[gi] && !redo[gi]) {
+      store_rows(gi, cok[gi] ? 1.0f / den : 0.f);
+      // scores were not shifted: the log-sum-exp is log2 of the denominator
+      if (lse && hi == 0) lse[((int64_t)b * g.N + qi[gi]) * g.H + h] = cok[gi] ? __log2f(den) : -INFINITY;
+    }
   }
   if (!__ballot(any_redo)) return;
 
@@ -505,36 +509,40 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
       den = __shfl(acc[gi][DT - 1][8], l32);
     else
       den = lsum[gi] + __shfl_xor(lsum[gi], 32);
-    if (active[gi] && redo[gi]) store_rows(gi, den > 0.f ? 1.0f / den : 0.f);
+    if (active[gi] && redo[gi]) {
+      store_rows(gi, den > 0.f ? 1.0f / den : 0.f);
+      if (lse && hi == 0)
+        lse[((int64_t)b * g.N + qi[gi]) * g.H + h] = den > 0.f ? mrow[gi] + __log2f(den) : -INFINITY;
+    }
   }
 }
 
 hipError_t launch_global_valu(const Geo &g, int dtype, const void *geom, const int32_t *coords,
                               const void *q, const void *ks, const void *vs, void *out,
-                              hipStream_t s, bool *supported);
+                              float *lse, hipStream_t s, bool *supported);
 
 namespace {
 template <int D, int G, int TS>
 hipError_t run_global_mfma(const Geo &g, const void *geom, const int32_t *coords, const void *q,
-                           const void *ks, const void *vs, void *out, hipStream_t s) {
+                           const void *ks, const void *vs, void *out, float *lse, hipStream_t s) {
   const int ntiles = (g.N + kWaves * 32 * G - 1) / (kWaves * 32 * G);
   const int64_t nwg = (int64_t)ntiles * g.B * g.H;
   hipLaunchKernelGGL((k_global_mfma<D, G, TS>), dim3((unsigned)nwg), dim3(256), 0, s, g, geom, coords,
                      static_cast<const bf16 *>(q), static_cast<const bf16 *>(ks),
-                     static_cast<const bf16 *>(vs), static_cast<bf16 *>(out), ntiles);
+                     static_cast<const bf16 *>(vs), static_cast<bf16 *>(out), lse, ntiles);
   return hipGetLastError();
 }
 }  // namespace
 
 hipError_t launch_global(const Geo &g, int dtype, const void *geom, const int32_t *coords,
-                         const void *q, const void *ks, const void *vs, void *out, hipStream_t s,
-                         bool *supported) {
+                         const void *q, const void *ks, const void *vs, void *out, float *lse,
+                         hipStream_t s, bool *supported) {
   if (dtype == PACK3D_BF16 && g.excl == PACK3D_EXCL_NONE) {
     *supported = true;
-    if (g.D == 48) return run_global_mfma<48, 2, 128>(g, geom, coords, q, ks, vs, out, s);
-    if (g.D == 96) return run_global_mfma<96, 1, 64>(g, geom, coords, q, ks, vs, out, s);
+    if (g.D == 48) return run_global_mfma<48, 2, 128>(g, geom, coords, q, ks, vs, out, lse, s);
+    if (g.D == 96) return run_global_mfma<96, 1, 64>(g, geom, coords, q, ks, vs, out, lse, s);
   }
-  return launch_global_valu(g, dtype, geom, coords, q, ks, vs, out, s, supported);
+  return launch_global_valu(g, dtype, geom, coords, q, ks, vs, out, lse, s, supported);
 }
 
 }  // namespace pk

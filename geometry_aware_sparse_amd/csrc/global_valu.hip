@@ -24,7 +24,7 @@ __global__ __launch_bounds__(kNT) void k_global_valu(Geo g, const void *geom,
                                                      const T *__restrict__ q,
                                                      const T *__restrict__ ks,
                                                      const T *__restrict__ vs, T *out,
-                                                     int ntiles) {
+                                                     float *lse, int ntiles) {
   constexpr int DA = D / 3;
   __shared__ float sK[kTS * D];
   __shared__ float sV[kTS * D];
@@ -113,40 +113,41 @@ __global__ __launch_bounds__(kNT) void k_global_valu(Geo g, const void *geom,
   const float inv = (den > 0.f && cok) ? 1.0f / den : 0.f;
 #pragma unroll
   for (int d = 0; d < D; d++) out[off + d] = from_f32<T>(o[d] * inv);
+  if (lse) lse[((int64_t)b * g.N + i) * g.H + h] = (den > 0.f && cok) ? mx + log2f(den) : -INFINITY;
 }
 
 namespace {
 template <typename T, int D>
 hipError_t run_global_valu(const Geo &g, const void *geom, const int32_t *coords, const void *q,
-                           const void *ks, const void *vs, void *out, hipStream_t s) {
+                           const void *ks, const void *vs, void *out, float *lse, hipStream_t s) {
   const int ntiles = (g.N + kNT - 1) / kNT;
   const int64_t nwg = (int64_t)ntiles * g.B * g.H;
   hipLaunchKernelGGL((k_global_valu<T, D>), dim3((unsigned)nwg), dim3(kNT), 0, s, g, geom, coords,
                      static_cast<const T *>(q), static_cast<const T *>(ks),
-                     static_cast<const T *>(vs), static_cast<T *>(out), ntiles);
+                     static_cast<const T *>(vs), static_cast<T *>(out), lse, ntiles);
   return hipGetLastError();
 }
 }  // namespace
 
 hipError_t launch_global_valu(const Geo &g, int dtype, const void *geom, const int32_t *coords,
                               const void *q, const void *ks, const void *vs, void *out,
-                              hipStream_t s, bool *supported) {
+                              float *lse, hipStream_t s, bool *supported) {
   *supported = true;
   if (dtype == PACK3D_BF16) {
     switch (g.D) {
-      case 6: return run_global_valu<bf16, 6>(g, geom, coords, q, ks, vs, out, s);
-      case 12: return run_global_valu<bf16, 12>(g, geom, coords, q, ks, vs, out, s);
-      case 24: return run_global_valu<bf16, 24>(g, geom, coords, q, ks, vs, out, s);
-      case 48: return run_global_valu<bf16, 48>(g, geom, coords, q, ks, vs, out, s);
-      case 96: return run_global_valu<bf16, 96>(g, geom, coords, q, ks, vs, out, s);
+      case 6: return run_global_valu<bf16, 6>(g, geom, coords, q, ks, vs, out, lse, s);
+      case 12: return run_global_valu<bf16, 12>(g, geom, coords, q, ks, vs, out, lse, s);
+      case 24: return run_global_valu<bf16, 24>(g, geom, coords, q, ks, vs, out, lse, s);
+      case 48: return run_global_valu<bf16, 48>(g, geom, coords, q, ks, vs, out, lse, s);
+      case 96: return run_global_valu<bf16, 96>(g, geom, coords, q, ks, vs, out, lse, s);
     }
   } else {
     switch (g.D) {
-      case 6: return run_global_valu<float, 6>(g, geom, coords, q, ks, vs, out, s);
-      case 12: return run_global_valu<float, 12>(g, geom, coords, q, ks, vs, out, s);
-      case 24: return run_global_valu<float, 24>(g, geom, coords, q, ks, vs, out, s);
-      case 48: return run_global_valu<float, 48>(g, geom, coords, q, ks, vs, out, s);
-      case 96: return run_global_valu<float, 96>(g, geom, coords, q, ks, vs, out, s);
+      case 6: return run_global_valu<float, 6>(g, geom, coords, q, ks, vs, out, lse, s);
+      case 12: return run_global_valu<float, 12>(g, geom, coords, q, ks, vs, out, lse, s);
+      case 24: return run_global_valu<float, 24>(g, geom, coords, q, ks, vs, out, lse, s);
+      case 48: return run_global_valu<float, 48>(g, geom, coords, q, ks, vs, out, lse, s);
+      case 96: return run_global_valu<float, 96>(g, geom, coords, q, ks, vs, out, lse, s);
     }
   }
   *supported = false;

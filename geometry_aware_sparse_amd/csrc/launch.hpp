@@ -18,9 +18,28 @@ hipError_t launch_summarize(const Geo &g, int dtype, const void *geom, const voi
 hipError_t launch_local(const Geo &g, int dtype, const void *geom, const void *q, const void *k,
                         const void *v, const void *gate, const void *oglob, void *out,
                         hipStream_t s, bool *supported);
+// lse may be null; when set it receives each (token, head)'s log-sum-exp of
+// the scaled scores in log2 units ([B, N, H] fp32; -inf when nothing is
+// attendable), which the backward uses to rebuild the probabilities.
 hipError_t launch_global(const Geo &g, int dtype, const void *geom, const int32_t *coords,
-                         const void *q, const void *ks, const void *vs, void *out, hipStream_t s,
-                         bool *supported);
+                         const void *q, const void *ks, const void *vs, void *out, float *lse,
+                         hipStream_t s, bool *supported);
+
+// Operands of the backward (device pointers). Inputs as in the forward plus
+// dout, the saved O_glob and lse_g, the recomputed summaries ks / vs and the
+// fp32 intermediates; outputs dq, dk, dv, dgate in the input dtype.
+struct BwdArgs {
+  const void *geom;
+  const int32_t *coords;
+  const void *q, *k, *v, *gate, *dout, *oglob;
+  const float *lse_g;
+  const void *ks, *vs;
+  float *qr, *dog, *delta_g, *dqg, *dks, *dvs, *lse_l, *delta_l;  // workspace
+  void *dq, *dk, *dv, *dgate;
+  void *const *events;  // null, or stage events: [3] after the global branch, [4] before local
+};
+hipError_t launch_backward(const Geo &g, int dtype, const BwdArgs &a, hipStream_t s,
+                           bool *supported);
 hipError_t launch_mix(const Geo &g, int dtype, const void *gate, const void *ol, const void *og,
                       void *o, hipStream_t s);
 

@@ -3,7 +3,8 @@ import ctypes as C
 
 import torch
 
-from ._lib import (PACK3D_BF16, PACK3D_EXACT_SOFTMAX, PACK3D_F32, PACK3D_NUM_STAGES,
+from ._lib import (PACK3D_BF16, PACK3D_EXACT_SOFTMAX, PACK3D_F32, PACK3D_NUM_BWD_STAGES,
+                   PACK3D_NUM_STAGES,
                    PACK3D_SUMMARY_CENTRE,
                    PACK3D_VALIDATE, Desc, Pack3DError, library)
 
@@ -251,3 +252,90 @@ def pack3d_forward(desc, coords, q, k, v, gate, out=None, workspace=None, stage_
                                     _ptr(gate), _ptr(out), _ptr(workspace), C.c_size_t(ws_bytes),
                                     _stream(), ev), "pack3d_forward")
     return out
+
+
+def _events(stage_events, n):
+    if stage_events is None:
+        return None
+    if len(stage_events) != 2 * n:
+        raise ValueError(f"stage_events needs {2 * n} events")
+    return (C.c_void_p * len(stage_events))(*[C.c_void_p(e.cuda_event) for e in stage_events])
+
+
+def pack3d_saved_bytes(desc):
+    n = C.c_size_t()
+    _check(library().pack3d_saved_bytes(C.byref(desc), C.byref(n)), "pack3d_saved_bytes")
+    return n.value
+
+
+def saved_views(desc, saved):
+    """(O_glob [B, N, H, D] in the descriptor's dtype, lse [B, N, H] fp32):
+    views into the buffer pack3d_forward_train fills."""
+    es = 2 if desc.dtype == PACK3D_BF16 else 4
+    nrow = desc.B * desc.N * desc.H
+    ob = (nrow * desc.D * es + 255) // 256 * 256
+    og = saved[:nrow * desc.D * es].view(_DTYPES[desc.dtype]).view(_bnhd(desc))
+    lse = saved[ob:ob + 4 * nrow].view(torch.float32).view(desc.B, desc.N, desc.H)
+    return og, lse
+
+
+def pack3d_forward_train(desc, coords, q, k, v, gate, out=None, saved=None, workspace=None,
+                         stage_events=None):
+    """The forward, also filling the buffer the backward needs. Returns
+    (out, saved)."""
+    _need(coords, "coords", desc, (desc.N, 3), torch.int32)
+    _need(q, "q", desc, _bnhd(desc))
+    _need(k, "k", desc, _bnkd(desc))
+    _need(v, "v", desc, _bnkd(desc))
+    _need(gate, "gate", desc, (desc.B, desc.N, desc.H))
+    out = torch.empty_like(q) if out is None else out
+    _need(out, "out", desc, _bnhd(desc))
+    sb = pack3d_saved_bytes(desc)
+    if saved is None:
+        saved = torch.empty(sb, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(pack3d_workspace_bytes(desc), dtype=torch.uint8, device=q.device)
+    _check(library().pack3d_forward_train(
+        C.byref(desc), _ptr(coords), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(out),
+        _ptr(saved), C.c_size_t(saved.numel() * saved.element_size()), _ptr(workspace),
+        C.c_size_t(workspace.numel() * workspace.element_size()), _stream(),
+        _events(stage_events, PACK3D_NUM_STAGES)), "pack3d_forward_train")
+    return out, saved
+
+
+def pack3d_backward_workspace_bytes(desc):
+    n = C.c_size_t()
+    _check(library().pack3d_backward_workspace_bytes(C.byref(desc), C.byref(n)),
+           "pack3d_backward_workspace_bytes")
+    return n.value
+
+
+def pack3d_backward(desc, coords, q, k, v, gate, saved, dout, workspace=None, grads=None,
+                    stage_events=None):
+    """Gradients (dq, dk, dv, dgate) of sum(dout * O) with respect to the
+    unrotated q, k, v and the gate logits. saved: from pack3d_forward_train
+    on the same inputs. grads: optional preallocated (dq, dk, dv, dgate)."""
+    _need(coords, "coords", desc, (desc.N, 3), torch.int32)
+    _need(q, "q", desc, _bnhd(desc))
+    _need(k, "k", desc, _bnkd(desc))
+    _need(v, "v", desc, _bnkd(desc))
+    _need(gate, "gate", desc, (desc.B, desc.N, desc.H))
+    _need(dout, "dout", desc, _bnhd(desc))
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+                 torch.empty_like(gate))
+    dq, dk, dv, dg = grads
+    _need(dq, "dq", desc, _bnhd(desc))
+    _need(dk, "dk", desc, _bnkd(desc))
+    _need(dv, "dv", desc, _bnkd(desc))
+    _need(dg, "dgate", desc, (desc.B, desc.N, desc.H))
+    if workspace is None:
+        workspace = torch.empty(pack3d_backward_workspace_bytes(desc), dtype=torch.uint8,
+                                device=q.device)
+    _check(library().pack3d_backward(
+        C.byref(desc), _ptr(coords), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(saved),
+        C.c_size_t(saved.numel() * saved.element_size()), _ptr(dout), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(dg), _ptr(workspace),
+        C.c_size_t(workspace.numel() * workspace.element_size()), _stream(),
+        _events(stage_events, PACK3D_NUM_BWD_STAGES)), "pack3d_backward")
+    return dq, dk, dv, dg

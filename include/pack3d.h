@@ -233,6 +233,42 @@ int pack3d_forward(const pack3d_desc *desc, const int32_t *coords, const void *q
                    const void *v, const void *gate, void *o, void *ws, size_t ws_bytes,
                    void *stream, void *const *stage_events);
 
+/* ---------------------------------------------------------------------------
+ * Training (paper summary §1, §3.4: the operator is trained end to end, with
+ * a backward that follows the forward's streamed access pattern).
+ *
+ * pack3d_forward_train is pack3d_forward that also fills `saved`, a device
+ * buffer of at least pack3d_saved_bytes bytes, laid out as
+ *   [0, ...)          O_glob [B, N, H, D] in desc->dtype (the global branch)
+ *   [256-aligned)     lse [B, N, H] fp32: log2 of the global softmax
+ *                     denominator of the scores scaled by scale * log2(e)
+ *                     (-inf when no summary is attendable)
+ * o is the same as pack3d_forward's. saved_bytes says how large saved is.
+ *
+ * pack3d_backward takes the forward's inputs, its saved buffer and dout =
+ * dL/dO [B, N, H, D] and writes the gradients of L with respect to the
+ * UNROTATED inputs: dq [B, N, H, D], dk and dv [B, N, Hkv, D] (summed over
+ * each KV head's group of query heads) and dgate [B, N, H] (with respect to
+ * the gate logits G), all in desc->dtype. It recomputes the geometry, the
+ * summaries and both softmaxes (the global one from the saved log-sum-exp);
+ * accumulation is fp32. Every reduction has a fixed order: results are
+ * deterministic, and a repack of the tokens permutes every gradient bit for
+ * bit. ws: device workspace of at least pack3d_backward_workspace_bytes
+ * bytes. stage_events: NULL or 2*PACK3D_NUM_BWD_STAGES hipEvent_t recorded
+ * around each stage (geometry + summaries, global branch, local branch).
+ * None of the outputs may alias an input. */
+int pack3d_saved_bytes(const pack3d_desc *desc, size_t *bytes);
+int pack3d_forward_train(const pack3d_desc *desc, const int32_t *coords, const void *q,
+                         const void *k, const void *v, const void *gate, void *o, void *saved,
+                         size_t saved_bytes, void *ws, size_t ws_bytes, void *stream,
+                         void *const *stage_events);
+#define PACK3D_NUM_BWD_STAGES 3
+int pack3d_backward_workspace_bytes(const pack3d_desc *desc, size_t *bytes);
+int pack3d_backward(const pack3d_desc *desc, const int32_t *coords, const void *q, const void *k,
+                    const void *v, const void *gate, const void *saved, size_t saved_bytes,
+                    const void *dout, void *dq, void *dk, void *dv, void *dgate, void *ws,
+                    size_t ws_bytes, void *stream, void *const *stage_events);
+
 #ifdef __cplusplus
 }
 #endif

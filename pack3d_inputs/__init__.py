@@ -14,11 +14,11 @@ from .configs import WORKLOADS, Workload, workload
 from .packing import (packing_coords, raster_coords, morton_coords, block_contiguous_coords,
                       block_morton_coords, random_coords, group_permuted_coords,
                       coords_to_sites, order_between)
-from .fields import make_fields, pack_fields, round_bf16
+from .fields import make_dout, make_fields, pack_fields, round_bf16
 
 __all__ = [
     "WORKLOADS", "Workload", "workload",
     "packing_coords", "raster_coords", "morton_coords", "block_contiguous_coords",
     "block_morton_coords", "random_coords", "group_permuted_coords", "coords_to_sites",
-    "order_between", "make_fields", "pack_fields", "round_bf16",
+    "order_between", "make_dout", "make_fields", "pack_fields", "round_bf16",
 ]

@@ -42,7 +42,8 @@ class Workload:
         return self.B * self.N
 
     def seed(self, what: str) -> int:
-        return 1000 * self.wid + {"q": 0, "k": 1, "v": 2, "g": 3, "perm": 4, "perm2": 5}[what]
+        return 1000 * self.wid + {"q": 0, "k": 1, "v": 2, "g": 3, "perm": 4, "perm2": 5,
+                                  "dout": 6}[what]
 
 
 def _ceil(a: int, b: int) -> int:

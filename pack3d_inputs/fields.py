@@ -72,6 +72,14 @@ def make_fields(w, values=None, shape_override=None):
     return tuple(out)
 
 
+def make_dout(w):
+    """Output gradient dO [B, sites, H, D] for the backward: iid N(0,1) in
+    raster site order (bf16-representable when the workload is bf16)."""
+    rng = np.random.Generator(np.random.PCG64(w.seed("dout")))
+    d = rng.standard_normal((w.B, w.N, w.H, w.D), dtype=np.float32)
+    return round_bf16(d) if w.dtype == "bf16" else d
+
+
 def pack_fields(fields, coords, grid):
     """Reorder site-ordered fields into the memory order given by coords."""
     Z, Y, X = grid

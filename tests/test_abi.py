@@ -25,7 +25,7 @@ def gas():
 def test_library_exports_every_declared_symbol(gas):
     lib = C.CDLL(gas.LIB_PATH)
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), f"{n} declared in pack3d.h but not exported"
     assert sorted(gas.EXPORTED_SYMBOLS) == names
