@@ -1,6 +1,8 @@
 // C ABI of the PACK3D forward (declarations and contracts in pack3d.h).
 // Host-side argument validation, workspace layout and kernel launches.
 #include <math.h>
+
+#include <algorithm>
 #include <string.h>
 
 #include "launch.hpp"
@@ -273,27 +275,56 @@ int forward_impl(const pack3d_desc *desc, const int32_t *coords, const void *q, 
   return mark(7);
 }
 
-// Backward workspace: geometry | k_sum | v_sum | fp32 intermediates
+// Backward workspace: geometry | k_sum | v_sum | fp32 intermediates, then
+// the matrix-core operands when that path runs (the vector-unit query
+// buffers are left out there)
 struct BwdLayout {
-  size_t geom, ks, vs, qr, dog, delta_g, dqg, dks, dvs, lse_l, delta_l, total;
+  size_t geom, ks, vs, qr, dog, delta_g, dqg, dks, dvs, lse_l, delta_l;
+  bool mfma;
+  int nsplit;
+  size_t qn, qt, dn, dt, lse_p, dl_p, tok, vk, kt, dks_part, dvs_part;
+  size_t total;
 };
 BwdLayout bwd_layout(const Geo &g, int dtype) {
   BwdLayout L;
   const size_t rows = (size_t)g.B * g.N * g.H;
   const size_t sum = (size_t)g.B * g.Hkv * g.M * g.D * 4;
+  L.mfma = bwd_global_mfma_supported(g, dtype);
   size_t off = 0;
   auto take = [&](size_t n) { size_t at = off; off += align_up(n); return at; };
   L.geom = take(geometry_bytes(g));
   L.ks = take(ksum_bytes(g, dtype));
   L.vs = take(vsum_bytes(g, dtype));
-  L.qr = take(rows * g.D * 4);
-  L.dog = take(rows * g.D * 4);
-  L.delta_g = take(rows * 4);
+  L.qr = take(L.mfma ? 0 : rows * g.D * 4);
+  L.dog = take(L.mfma ? 0 : rows * g.D * 4);
+  L.delta_g = take(L.mfma ? 0 : rows * 4);
   L.dqg = take(rows * g.D * 4);
   L.dks = take(sum);
   L.dvs = take(sum);
   L.lse_l = take(rows * 4);
   L.delta_l = take(rows * 4);
+  L.nsplit = 1;
+  L.qn = L.qt = L.dn = L.dt = L.lse_p = L.dl_p = L.tok = L.vk = L.kt = L.dks_part =
+      L.dvs_part = 0;
+  if (L.mfma) {
+    // the summary side runs (Mp/128) x B x Hkv workgroups per split: split
+    // the query sites until about 2048 workgroups fill the chip
+    const size_t Np = ((size_t)g.N + 31) / 32 * 32, Mp = ((size_t)g.M + 31) / 32 * 32;
+    const size_t wgs = (Mp / 32 + 3) / 4 * g.B * g.Hkv;
+    L.nsplit = (int)std::min<size_t>(16, std::max<size_t>(1, (2048 + wgs - 1) / wgs));
+    const size_t prow = (size_t)g.B * g.H * Np;
+    L.qn = take(prow * g.D * 2);
+    L.qt = take(prow * g.D * 2);
+    L.dn = take(prow * g.D * 2);
+    L.dt = take(prow * g.D * 2);
+    L.lse_p = take(prow * 4);
+    L.dl_p = take(prow * 4);
+    L.tok = take((size_t)g.B * Np * 4);
+    L.vk = take((size_t)g.B * g.Hkv * Mp * g.D * 2);
+    L.kt = take((size_t)g.B * g.Hkv * Mp * g.D * 2);
+    L.dks_part = take(sum * L.nsplit);
+    L.dvs_part = take(sum * L.nsplit);
+  }
   L.total = off;
   return L;
 }
@@ -387,6 +418,23 @@ int pack3d_backward(const pack3d_desc *desc, const int32_t *coords, const void *
   a.dv = dv;
   a.dgate = dgate;
   a.events = stage_events;
+  BwdMfmaArgs mf;
+  a.mfma = nullptr;
+  if (L.mfma) {
+    mf.qn = reinterpret_cast<bf16 *>(base + L.qn);
+    mf.qt = reinterpret_cast<bf16 *>(base + L.qt);
+    mf.dn = reinterpret_cast<bf16 *>(base + L.dn);
+    mf.dt = reinterpret_cast<bf16 *>(base + L.dt);
+    mf.lse_p = reinterpret_cast<float *>(base + L.lse_p);
+    mf.dl_p = reinterpret_cast<float *>(base + L.dl_p);
+    mf.tok = reinterpret_cast<int32_t *>(base + L.tok);
+    mf.vk = reinterpret_cast<bf16 *>(base + L.vk);
+    mf.kt = reinterpret_cast<bf16 *>(base + L.kt);
+    mf.dks_part = reinterpret_cast<float *>(base + L.dks_part);
+    mf.dvs_part = reinterpret_cast<float *>(base + L.dvs_part);
+    mf.nsplit = L.nsplit;
+    a.mfma = &mf;
+  }
   if ((rc = mark(0))) return rc;
   if ((rc = hip_status(launch_index(g, coords, base + L.geom, nullptr, nullptr, nullptr, s))))
     return rc;

@@ -553,6 +553,9 @@ namespace {
 template <typename T, int D, int TZ, int TY, int TX>
 hipError_t run_backward_t(const Geo &g, const BwdArgs &a, hipStream_t s) {
   const int64_t rows = (int64_t)g.B * g.N * g.H;
+  if (a.mfma) {
+    if (hipError_t e = launch_bwd_global_mfma(g, a, *a.mfma, s)) return e;
+  } else {
   hipLaunchKernelGGL((k_bwd_prep<T, D>), dim3((unsigned)((rows + kNT - 1) / kNT)), dim3(kNT), 0, s,
                      g, a.geom, a.coords, static_cast<const T *>(a.q), static_cast<const T *>(a.gate),
                      static_cast<const T *>(a.dout), static_cast<const T *>(a.oglob), a.qr, a.dog,
@@ -570,10 +573,13 @@ hipError_t run_backward_t(const Geo &g, const BwdArgs &a, hipStream_t s) {
                        (int)(sizeof(T) == 2), a.dks, a.dvs, mtiles);
     if (hipError_t e = hipGetLastError()) return e;
   }
+  }
   if (a.events) {
     if (hipError_t e = hipEventRecord(static_cast<hipEvent_t>(a.events[3]), s)) return e;
     if (hipError_t e = hipEventRecord(static_cast<hipEvent_t>(a.events[4]), s)) return e;
   }
+  if (bwd_local_pair_supported(g, sizeof(T) == 2 ? PACK3D_BF16 : PACK3D_F32))
+    return launch_bwd_local_pair(g, a, s);
   const int ntz = (g.Z + TZ - 1) / TZ, nty = (g.Y + TY - 1) / TY, ntx = (g.X + TX - 1) / TX;
   hipLaunchKernelGGL((k_bwd_local_q<T, D, TZ, TY, TX>), dim3((unsigned)(g.B * ntz * nty * ntx * g.H)),
                      dim3(TZ * TY * TX), 0, s, g, a.geom, static_cast<const T *>(a.q),

@@ -1,0 +1,483 @@
+// Global branch of the backward on bf16 matrix cores (Geometry Matters in
+// Packed 3D Attention: the backward of the query-to-summary attention,
+// project page Ch. 3, Contract 2; paper summary §3.4, §3.5). With
+// t_im = <q~_i, k_sum_m> * s * log2(e) and the forward's log-sum-exp lse_i:
+//   P = exp2(t - lse), dP = dO_glob * v_sum^T, dT = P (dP - Delta),
+//   dq~   = s    * dT  * k_sum            (query side)
+//   dk_sum = s   * dT^T * q~,  dv_sum = P^T * dO_glob   (summary side)
+// Three dense contractions per (query, summary) pair on the query side and
+// four on the summary side; like the forward, no token x summary matrix is
+// ever stored.
+//
+// Both sides use the forward's register trick: a 32x32 score block comes out
+// of v_mfma_f32_32x32x16_bf16 with each lane holding 16 values of one column,
+// and placing the contraction rows in bit-2/3-swapped order makes those 16
+// values exactly the next product's operand fragment (k index
+// 16*c2 + 8*hi + e for register 8*c2 + e of half-wave hi).
+//
+//   k_bwd_prep_mfma   per (batch, query head, grid site): bf16 q~ s log2(e)
+//                     and dO_glob = g dO (rounded as the forward rounds q~),
+//                     in 32-row blocks and 8-row transposed blocks, with the
+//                     saved lse and Delta = <dO_glob, O_glob>, in grid-site
+//                     (raster) order -- the order every reduction runs in
+//   k_bwd_relayout    v_sum in the key-summary layout and k_sum in the
+//                     value-summary layout, the operand shapes the
+//                     contractions above need
+//   k_bwd_gq_mfma     query side: a wave owns 32 query sites and streams the
+//                     summaries through LDS
+//   k_bwd_gk_mfma     summary side: a wave owns 32 summaries and streams the
+//                     query sites of one split of the site range through LDS
+//   k_bwd_split_sum   the splits' partial sums, added in split order
+#include "launch.hpp"
+
+namespace pk {
+
+namespace {
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kWaves = 4;
+
+__device__ __forceinline__ int swap23(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Position p of (b, h) is grid site p (raster order), p < Np = 32*ceil(N/32):
+//   qn [B*H, Np/32, D/8, 32, 8]  q~ s log2(e): row p%32 of 32-row block p/32
+//   qt [B*H, Np/8, D, 8]         the same, channel-major: 8 sites per chunk
+//   dn, dt                       dO_glob, likewise
+//   lse_p, dl_p [B*H, Np]        saved lse (+inf where no token: P = 0), Delta
+//   tok [B, Np]                  token at the site (-1: none)
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_prep_mfma(
+    Geo g, const void *geom, const bf16 *__restrict__ q, const bf16 *__restrict__ gate,
+    const bf16 *__restrict__ dout, const bf16 *__restrict__ oglob, const float *__restrict__ lse,
+    bf16 *qn, bf16 *qt, bf16 *dn, bf16 *dt, float *lse_p, float *dl_p, int32_t *tok, int Np) {
+  constexpr int DA = D / 3, NCH = D / 8;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;  // ((b*H + h) * Np + p)
+  if (t >= (int64_t)g.B * g.H * Np) return;
+  const int p = (int)(t % Np);
+  const int64_t bh = t / Np;
+  const int h = (int)(bh % g.H), b = (int)(bh / g.H);
+  const int32_t *slot = slot_map(geom, g);
+  const float2 *tab = rope_table(geom, g);
+  const int i = p < g.N ? slot[p] : -1;
+  if (h == 0) tok[(int64_t)b * Np + p] = i;
+  const int c3[3] = {p / (g.Y * g.X), (p / g.X) % g.Y, p % g.X};
+  const int64_t row = ((int64_t)b * g.N + max(i, 0)) * g.H + h;
+  const float qscale = g.scale * kLog2e;
+  const float gg = i >= 0 ? 1.0f / (1.0f + expf(-(float)gate[row])) : 0.f;
+  float dl = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; c++) {
+    bf16x8 qv, dv;
+    if (i >= 0) {
+      const bf16x8 raw = *reinterpret_cast<const bf16x8 *>(q + row * D + 8 * c);
+      const bf16x8 draw = *reinterpret_cast<const bf16x8 *>(dout + row * D + 8 * c);
+      const bf16x8 oraw = *reinterpret_cast<const bf16x8 *>(oglob + row * D + 8 * c);
+      const int a = (8 * c) / DA, p0 = ((8 * c) % DA) / 2;
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        float x0 = (float)raw[2 * u], x1 = (float)raw[2 * u + 1];
+        rotate(x0, x1, rope_cs(tab, g, a, c3[a], p0 + u));
+        qv[2 * u] = (bf16)(x0 * qscale);
+        qv[2 * u + 1] = (bf16)(x1 * qscale);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        dv[e] = (bf16)(gg * (float)draw[e]);
+        dl += (float)dv[e] * (float)oraw[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; e++) qv[e] = dv[e] = (bf16)0.0f;
+    }
+    const int64_t nb = (((bh * (Np / 32) + p / 32) * NCH + c) * 32 + p % 32) * 8;
+    *reinterpret_cast<bf16x8 *>(qn + nb) = qv;
+    *reinterpret_cast<bf16x8 *>(dn + nb) = dv;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const int64_t tb = ((bh * (Np / 8) + p / 8) * D + 8 * c + e) * 8 + p % 8;
+      qt[tb] = qv[e];
+      dt[tb] = dv[e];
+    }
+  }
+  lse_p[t] = i >= 0 ? lse[row] : INFINITY;
+  dl_p[t] = dl;
+}
+
+// v_sum [B*Hkv, Mp/8, D, 8] -> vk [B*Hkv, Mp/32, D/8, 32, 8] and
+// k_sum [B*Hkv, Mp/32, D/8, 32, 8] -> kt [B*Hkv, Mp/8, D, 8]
+template <int D>
+__global__ void k_bwd_relayout(int64_t n, int Mp, const bf16 *__restrict__ ks,
+                               const bf16 *__restrict__ vs, bf16 *vk, bf16 *kt) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (bk, m, d)
+  if (e >= n) return;
+  const int d = (int)(e % D);
+  const int m = (int)((e / D) % Mp);
+  const int64_t bk = e / ((int64_t)D * Mp);
+  const int64_t kso = (((bk * (Mp / 32) + m / 32) * (D / 8) + d / 8) * 32 + m % 32) * 8 + d % 8;
+  const int64_t vso = ((bk * (Mp / 8) + m / 8) * D + d) * 8 + m % 8;
+  vk[kso] = vs[vso];
+  kt[vso] = ks[kso];
+}
+
+// ---------------------------------------------------------------------------
+// Query side. Workgroup: 4 waves x 32 query sites of one (b, h); summary tiles
+// of TS (two 32-summary sub-tiles for TS = 64) double-buffered in LDS.
+template <int D, int TS>
+__global__ __launch_bounds__(256, 2) void k_bwd_gq_mfma(
+    Geo g, const bf16 *__restrict__ qn, const bf16 *__restrict__ dn,
+    const float *__restrict__ lse_p, const float *__restrict__ dl_p,
+    const int32_t *__restrict__ tok, const bf16 *__restrict__ ks, const bf16 *__restrict__ vk,
+    const bf16 *__restrict__ kt, float *dqg, int Np, int ntiles) {
+  constexpr int KD = D / 16, NCH = D / 8, DT = (D + 31) / 32, NSUB = TS / 32;
+  constexpr int NJ8 = TS / 8;
+  // chunks per tile: k_sum and vk rows (NCH x TS), kt (NJ8 x D)
+  constexpr int NKC = NCH * TS, NTC = NJ8 * D;
+  __shared__ bf16x8 sK[2][NKC], sVK[2][NKC], sKT[2][NTC];
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = w % ntiles, bh = w / ntiles;
+  const int h = bh % g.H, b = bh / g.H;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hi = lane >> 5, l32 = lane & 31;
+  const int Mp = (g.M + 31) / 32 * 32;
+  const int64_t bk = (int64_t)b * g.Hkv + h / g.G;
+  // this lane's query site; past Np (the last tile's tail) it loads site
+  // Np - 1 and takes no part (P = 0)
+  const int p = tile * (kWaves * 32) + wv * 32 + l32;
+  const int pc = min(p, Np - 1);
+  bf16x8 qf[KD], df[KD];
+#pragma unroll
+  for (int c = 0; c < KD; c++) {
+    const int64_t o = ((((int64_t)bh * (Np / 32) + pc / 32) * NCH + 2 * c + hi) * 32 + pc % 32) * 8;
+    qf[c] = *reinterpret_cast<const bf16x8 *>(qn + o);
+    df[c] = *reinterpret_cast<const bf16x8 *>(dn + o);
+  }
+  const float lq = p < Np ? lse_p[(int64_t)bh * Np + pc] : INFINITY;
+  const float dq = dl_p[(int64_t)bh * Np + pc];
+  f32x16 acc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; t++)
+#pragma unroll
+    for (int j = 0; j < 16; j++) acc[t][j] = 0.f;
+  const f32x16 zero16 = {};
+
+  // tile loads: chunk e of a row tile = (ch, pos), pos = 32*sub + r holding
+  // summary swap23(r) of sub-tile sub; chunk e of the kt tile = (j8, d)
+  const int ntile = Mp / TS + (Mp % TS ? 1 : 0);
+  constexpr int RK = (NKC + 255) / 256, RT = (NTC + 255) / 256;
+  bf16x8 rk[RK], rv[RK], rt[RT];
+  auto load = [&](int tt) {
+#pragma unroll
+    for (int r = 0; r < RK; r++) {
+      const int e = min((int)threadIdx.x + 256 * r, NKC - 1);
+      const int ch = e / TS, pos = e % TS;
+      const int m = min(tt * TS + 32 * (pos / 32) + swap23(pos % 32), Mp - 1);
+      const int64_t o = (((bk * (Mp / 32) + m / 32) * NCH + ch) * 32 + m % 32) * 8;
+      rk[r] = *reinterpret_cast<const bf16x8 *>(ks + o);
+      rv[r] = *reinterpret_cast<const bf16x8 *>(vk + o);
+    }
+#pragma unroll
+    for (int r = 0; r < RT; r++) {
+      const int e = min((int)threadIdx.x + 256 * r, NTC - 1);
+      const int j8 = e / D, d = e % D;
+      const int g8 = min(tt * NJ8 + j8, Mp / 8 - 1);
+      rt[r] = *reinterpret_cast<const bf16x8 *>(kt + ((bk * (Mp / 8) + g8) * D + d) * 8);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < RK; r++) {
+      const int e = (int)threadIdx.x + 256 * r;
+      if (e < NKC) {
+        sK[buf][e] = rk[r];
+        sVK[buf][e] = rv[r];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RT; r++) {
+      const int e = (int)threadIdx.x + 256 * r;
+      if (e < NTC) sKT[buf][e] = rt[r];
+    }
+  };
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int tt = 0; tt < ntile; tt++) {
+    const int buf = tt & 1;
+    if (tt + 1 < ntile) load(tt + 1);
+#pragma unroll
+    for (int sub = 0; sub < NSUB; sub++) {
+      if (tt * TS + 32 * sub >= Mp) break;  // uniform
+      f32x16 s, dp;
+#pragma unroll
+      for (int c = 0; c < KD; c++) {
+        const bf16x8 kf = sK[buf][(2 * c + hi) * TS + 32 * sub + l32];
+        const bf16x8 vf = sVK[buf][(2 * c + hi) * TS + 32 * sub + l32];
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], c == 0 ? zero16 : s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[c], c == 0 ? zero16 : dp, 0, 0, 0);
+      }
+      // register j <-> summary mbase + 16*(j/8) + 8*hi + j%8; summaries past M
+      // (zero padding) are forced to 0 so that no inf * 0 can reach the sum
+      const int mbase = tt * TS + 32 * sub;
+      bf16x8 tf[2];
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        const float pr = __builtin_amdgcn_exp2f(s[j] - lq);
+        const bool real = mbase + 16 * (j >> 3) + 8 * hi + (j & 7) < g.M;
+        tf[j >> 3][j & 7] = (bf16)(real ? pr * (dp[j] - dq) : 0.f);
+      }
+#pragma unroll
+      for (int t = 0; t < DT; t++) {
+        const int d = min(32 * t + l32, D - 1);
+#pragma unroll
+        for (int c2 = 0; c2 < 2; c2++) {
+          const bf16x8 kf = sKT[buf][(4 * sub + 2 * c2 + hi) * D + d];
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, tf[c2], acc[t], 0, 0, 0);
+        }
+      }
+    }
+    if (tt + 1 < ntile) store(buf ^ 1);
+    __syncthreads();
+  }
+  // lane: query site p (column l32), rows d = 32t + 8jj + 4hi + u
+  const int i = p < g.N ? tok[(int64_t)b * Np + p] : -1;
+  if (i < 0) return;
+  float *orow = dqg + (((int64_t)b * g.N + i) * g.H + h) * D;
+#pragma unroll
+  for (int t = 0; t < DT; t++)
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) {
+      const int d = 32 * t + 8 * jj + 4 * hi;
+      if (d < D) {
+        f32x4 o4;
+#pragma unroll
+        for (int u = 0; u < 4; u++) o4[u] = g.scale * acc[t][4 * jj + u];
+        *reinterpret_cast<f32x4 *>(orow + d) = o4;
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Summary side. Workgroup: 4 waves x 32 summaries of one (b, hk), one split
+// [p_begin, p_end) of the query sites of every head of the group; query
+// tiles of TQ sites double-buffered in LDS. Writes the split's partial sums.
+template <int D, int TQ>
+__global__ __launch_bounds__(256, 2) void k_bwd_gk_mfma(
+    Geo g, const bf16 *__restrict__ qn, const bf16 *__restrict__ qt, const bf16 *__restrict__ dn,
+    const bf16 *__restrict__ dt, const float *__restrict__ lse_p, const float *__restrict__ dl_p,
+    const bf16 *__restrict__ ks, const bf16 *__restrict__ vk, float *dks_part, float *dvs_part,
+    int Np, int mtiles, int nsplit) {
+  constexpr int KD = D / 16, NCH = D / 8, DT = (D + 31) / 32, NSUB = TQ / 32, NJ8 = TQ / 8;
+  constexpr int NNC = NCH * TQ, NTC = NJ8 * D;  // chunks per tile: row-blocked, transposed
+  __shared__ bf16x8 sQ[2][NNC], sDO[2][NNC], sQT[2][NTC], sDT[2][NTC];
+  __shared__ float sL[2][TQ], sDl[2][TQ];
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = w % nsplit, mt = (w / nsplit) % mtiles, bk = w / (nsplit * mtiles);
+  const int b = bk / g.Hkv, hk = bk % g.Hkv;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hi = lane >> 5, l32 = lane & 31;
+  const int Mp = (g.M + 31) / 32 * 32;
+  const int m32 = min(mt * kWaves + wv, Mp / 32 - 1);  // this wave's 32 summaries
+  const bool wave_live = mt * kWaves + wv < Mp / 32;
+  bf16x8 kb[KD], vb[KD];
+#pragma unroll
+  for (int c = 0; c < KD; c++) {
+    const int64_t o = ((((int64_t)bk * (Mp / 32) + m32) * NCH + 2 * c + hi) * 32 + l32) * 8;
+    kb[c] = *reinterpret_cast<const bf16x8 *>(ks + o);
+    vb[c] = *reinterpret_cast<const bf16x8 *>(vk + o);
+  }
+  f32x16 aK[DT], aV[DT];
+#pragma unroll
+  for (int t = 0; t < DT; t++)
+#pragma unroll
+    for (int j = 0; j < 16; j++) aK[t][j] = aV[t][j] = 0.f;
+  const f32x16 zero16 = {};
+
+  // this split's query sites, in TQ tiles
+  const int nqt = Np / TQ + (Np % TQ ? 1 : 0);
+  const int per = (nqt + nsplit - 1) / nsplit;
+  const int qt0 = split * per, qt1 = min(nqt, qt0 + per);
+  const int ntile = max(qt1 - qt0, 0) * g.G;  // (head of the group, query tile) pairs
+  constexpr int RN = (NNC + 255) / 256, RTT = (NTC + 255) / 256;
+  bf16x8 rq[RN], rd[RN], rqt[RTT], rdt[RTT];
+  float rl = 0.f, rdl = 0.f;
+  auto load = [&](int it) {
+    const int h = hk * g.G + it / (qt1 - qt0), qtile = qt0 + it % (qt1 - qt0);
+    const int64_t bh = (int64_t)b * g.H + h;
+#pragma unroll
+    for (int r = 0; r < RN; r++) {
+      const int e = min((int)threadIdx.x + 256 * r, NNC - 1);
+      const int ch = e / TQ, pos = e % TQ;
+      const int p = min(qtile * TQ + 32 * (pos / 32) + swap23(pos % 32), Np - 1);
+      const int64_t o = (((bh * (Np / 32) + p / 32) * NCH + ch) * 32 + p % 32) * 8;
+      rq[r] = *reinterpret_cast<const bf16x8 *>(qn + o);
+      rd[r] = *reinterpret_cast<const bf16x8 *>(dn + o);
+    }
+#pragma unroll
+    for (int r = 0; r < RTT; r++) {
+      const int e = min((int)threadIdx.x + 256 * r, NTC - 1);
+      const int j8 = e / D, d = e % D;
+      const int p8 = min(qtile * NJ8 + j8, Np / 8 - 1);
+      const int64_t o = ((bh * (Np / 8) + p8) * D + d) * 8;
+      rqt[r] = *reinterpret_cast<const bf16x8 *>(qt + o);
+      rdt[r] = *reinterpret_cast<const bf16x8 *>(dt + o);
+    }
+    if (threadIdx.x < TQ) {
+      const int p = qtile * TQ + threadIdx.x;
+      // sites past Np do not exist: P = 0 there
+      rl = p < Np ? lse_p[bh * Np + p] : INFINITY;
+      rdl = p < Np ? dl_p[bh * Np + p] : 0.f;
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < RN; r++) {
+      const int e = (int)threadIdx.x + 256 * r;
+      if (e < NNC) {
+        sQ[buf][e] = rq[r];
+        sDO[buf][e] = rd[r];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RTT; r++) {
+      const int e = (int)threadIdx.x + 256 * r;
+      if (e < NTC) {
+        sQT[buf][e] = rqt[r];
+        sDT[buf][e] = rdt[r];
+      }
+    }
+    if (threadIdx.x < TQ) {
+      sL[buf][threadIdx.x] = rl;
+      sDl[buf][threadIdx.x] = rdl;
+    }
+  };
+  if (ntile > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntile; it++) {
+    const int buf = it & 1;
+    if (it + 1 < ntile) load(it + 1);
+#pragma unroll
+    for (int sub = 0; sub < NSUB; sub++) {
+      // C[query rows][summary columns]: row r holds query site swap23(r)
+      f32x16 s, dp;
+#pragma unroll
+      for (int c = 0; c < KD; c++) {
+        const bf16x8 qa = sQ[buf][(2 * c + hi) * TQ + 32 * sub + l32];
+        const bf16x8 da = sDO[buf][(2 * c + hi) * TQ + 32 * sub + l32];
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb[c], c == 0 ? zero16 : s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vb[c], c == 0 ? zero16 : dp, 0, 0, 0);
+      }
+      // register 8*c2 + e of half hi <-> site 32*sub + 16*c2 + 8*hi + e
+      bf16x8 pa[2], ta[2];
+#pragma unroll
+      for (int c2 = 0; c2 < 2; c2++) {
+        const int q0 = 32 * sub + 16 * c2 + 8 * hi;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const float pr = __builtin_amdgcn_exp2f(s[8 * c2 + e] - sL[buf][q0 + e]);
+          pa[c2][e] = (bf16)pr;
+          ta[c2][e] = (bf16)(pr * (dp[8 * c2 + e] - sDl[buf][q0 + e]));
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < DT; t++) {
+        const int d = min(32 * t + l32, D - 1);
+#pragma unroll
+        for (int c2 = 0; c2 < 2; c2++) {
+          const int j8 = 4 * sub + 2 * c2 + hi;
+          const bf16x8 qb = sQT[buf][j8 * D + d];
+          const bf16x8 db = sDT[buf][j8 * D + d];
+          aK[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[c2], qb, aK[t], 0, 0, 0);
+          aV[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[c2], db, aV[t], 0, 0, 0);
+        }
+      }
+    }
+    if (it + 1 < ntile) store(buf ^ 1);
+    __syncthreads();
+  }
+  if (!wave_live) return;
+  // lane: channel column 32t + l32, rows = summaries 8jj + 4hi + u of the group
+  const int64_t base = (((int64_t)split * g.B * g.Hkv + bk) * g.M) * D;
+#pragma unroll
+  for (int t = 0; t < DT; t++) {
+    const int d = 32 * t + l32;
+    if (d >= D) continue;
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const int m = m32 * 32 + (j >> 2) * 8 + hi * 4 + (j & 3);
+      if (m < g.M) {
+        dks_part[base + (int64_t)m * D + d] = kLn2 * aK[t][j];  // s / (s log2 e)
+        dvs_part[base + (int64_t)m * D + d] = aV[t][j];
+      }
+    }
+  }
+}
+
+__global__ void k_bwd_split_sum(int64_t n, int nsplit, const float *__restrict__ part, float *out) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  float s = 0.f;
+  for (int k = 0; k < nsplit; k++) s += part[k * n + e];
+  out[e] = s;
+}
+
+// ---------------------------------------------------------------------------
+namespace {
+template <int D, int TS, int TQ>
+hipError_t run_bwd_global_mfma(const Geo &g, const BwdArgs &a, const BwdMfmaArgs &m,
+                               hipStream_t s) {
+  const int Np = (g.N + 31) / 32 * 32, Mp = (g.M + 31) / 32 * 32;
+  {
+    const int64_t n = (int64_t)g.B * g.H * Np;
+    hipLaunchKernelGGL((k_bwd_prep_mfma<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, g,
+                       a.geom, static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.gate),
+                       static_cast<const bf16 *>(a.dout), static_cast<const bf16 *>(a.oglob),
+                       a.lse_g, m.qn, m.qt, m.dn, m.dt, m.lse_p, m.dl_p, m.tok, Np);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  {
+    const int64_t n = (int64_t)g.B * g.Hkv * Mp * D;
+    hipLaunchKernelGGL((k_bwd_relayout<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n,
+                       Mp, static_cast<const bf16 *>(a.ks), static_cast<const bf16 *>(a.vs), m.vk,
+                       m.kt);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  {
+    const int ntiles = Np / (kWaves * 32) + (Np % (kWaves * 32) ? 1 : 0);
+    hipLaunchKernelGGL((k_bwd_gq_mfma<D, TS>), dim3((unsigned)(ntiles * g.B * g.H)), dim3(256), 0, s,
+                       g, m.qn, m.dn, m.lse_p, m.dl_p, m.tok, static_cast<const bf16 *>(a.ks), m.vk,
+                       m.kt, a.dqg, Np, ntiles);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  {
+    const int mtiles = (Mp / 32 + kWaves - 1) / kWaves;
+    hipLaunchKernelGGL((k_bwd_gk_mfma<D, TQ>), dim3((unsigned)(m.nsplit * mtiles * g.B * g.Hkv)),
+                       dim3(256), 0, s, g, m.qn, m.qt, m.dn, m.dt, m.lse_p, m.dl_p,
+                       static_cast<const bf16 *>(a.ks), m.vk, m.dks_part, m.dvs_part, Np, mtiles,
+                       m.nsplit);
+    if (hipError_t e = hipGetLastError()) return e;
+    const int64_t n = (int64_t)g.B * g.Hkv * g.M * D;
+    hipLaunchKernelGGL(k_bwd_split_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n,
+                       m.nsplit, m.dks_part, a.dks);
+    hipLaunchKernelGGL(k_bwd_split_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n,
+                       m.nsplit, m.dvs_part, a.dvs);
+  }
+  return hipGetLastError();
+}
+}  // namespace
+
+bool bwd_global_mfma_supported(const Geo &g, int dtype) {
+  return dtype == PACK3D_BF16 && g.excl == PACK3D_EXCL_NONE && (g.D == 48 || g.D == 96);
+}
+
+hipError_t launch_bwd_global_mfma(const Geo &g, const BwdArgs &a, const BwdMfmaArgs &m,
+                                  hipStream_t s) {
+  if (g.D == 48) return run_bwd_global_mfma<48, 64, 64>(g, a, m, s);
+  return run_bwd_global_mfma<96, 64, 32>(g, a, m, s);
+}
+
+}  // namespace pk

@@ -37,7 +37,25 @@ struct BwdArgs {
   float *qr, *dog, *delta_g, *dqg, *dks, *dvs, *lse_l, *delta_l;  // workspace
   void *dq, *dk, *dv, *dgate;
   void *const *events;  // null, or stage events: [3] after the global branch, [4] before local
+  const struct BwdMfmaArgs *mfma;  // null: vector-unit global branch
 };
+// Matrix-core global branch of the backward (bf16, D in {48, 96}, no
+// exclusion): the prepared query operands (Np = 32*ceil(N/32) grid sites),
+// the relaid summaries and the split partial sums.
+struct BwdMfmaArgs {
+  bf16 *qn, *qt, *dn, *dt;  // [B*H, Np, D] blocked / transposed
+  float *lse_p, *dl_p;      // [B*H, Np]
+  int32_t *tok;             // [B, Np]
+  bf16 *vk, *kt;            // [B*Hkv, Mp, D] relaid summaries
+  float *dks_part, *dvs_part;  // [nsplit, B*Hkv, M, D]
+  int nsplit;
+};
+bool bwd_global_mfma_supported(const Geo &g, int dtype);
+hipError_t launch_bwd_global_mfma(const Geo &g, const BwdArgs &a, const BwdMfmaArgs &m,
+                                  hipStream_t s);
+// Local branch of the backward, bf16 with D in {48, 96}: D/24 lanes per site.
+bool bwd_local_pair_supported(const Geo &g, int dtype);
+hipError_t launch_bwd_local_pair(const Geo &g, const BwdArgs &a, hipStream_t s);
 hipError_t launch_backward(const Geo &g, int dtype, const BwdArgs &a, hipStream_t s,
                            bool *supported);
 hipError_t launch_mix(const Geo &g, int dtype, const void *gate, const void *ol, const void *og,

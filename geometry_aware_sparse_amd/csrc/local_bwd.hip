@@ -1,0 +1,507 @@
+// Local branch of the backward for bf16 rows of 48 or 96 channels (Geometry
+// Matters in Packed 3D Attention: exact 3x3x3 local attention, project page
+// Ch. 3, Contract 1; its gradients, paper summary §3.4), laid out like the
+// forward's k_local_pair: D/24 lanes per site, each owning 24 consecutive
+// channels; dot products by v_dot2_f32_bf16 with the lanes of a site met by
+// DPP swaps; sums over neighbours taken two neighbours at a time with one
+// v_dot2 per channel (the pair formed by v_perm_b32).
+//
+//   k_bwd_local_q_pair   per query site: logits as the forward computes them
+//                        (rotated, scaled, bf16-rounded q~ against the staged
+//                        rotated keys), P in fp32, u_j = <dO, v_j>,
+//                        dq = R^T (s sum_j dS_j k~_j + dq~_glob), dG, and
+//                        the log-sum-exp and Delta for the key side
+//   k_bwd_local_kv_pair  per key site: for every query head of the KV head's
+//                        group, the neighbour queries are staged (rotated,
+//                        scaled, bf16-rounded exactly as the query side rounds
+//                        its own) with dO and the per-site statistics; the
+//                        logits are recomputed bit for bit (the same products
+//                        summed in the same order), then
+//                        dk~ += s dS q~, dv += P (1 - g) dO, and the pooling
+//                        and RoPE transposes
+#include "launch.hpp"
+
+namespace pk {
+
+namespace {
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <int LPQ>
+__device__ __forceinline__ float lane_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xf,
+                                                          0xf, false));  // quad_perm 1,0,3,2
+  if constexpr (LPQ == 4)
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xf,
+                                                            0xf, false));  // 2,3,0,1
+  return x;
+}
+
+__device__ __forceinline__ void rotate_t(float &x0, float &x1, float2 cs) {
+  float y0 = x0 * cs.x + x1 * cs.y;
+  float y1 = -x0 * cs.y + x1 * cs.x;
+  x0 = y0;
+  x1 = y1;
+}
+
+// o[c] += w0 * A[c] + w1 * B[c] for the DH channels of two staged bf16 rows
+template <int DH>
+__device__ __forceinline__ void pair_accumulate(float *o, float w0, float w1, const bf16 *A,
+                                                const bf16 *B) {
+  bf16x2 pp;
+  pp[0] = (bf16)w0;
+  pp[1] = (bf16)w1;
+  const uint32_t *a = reinterpret_cast<const uint32_t *>(A);
+  const uint32_t *b = reinterpret_cast<const uint32_t *>(B);
+#pragma unroll
+  for (int j = 0; j < DH / 2; j++) {
+    const uint32_t x = a[j], y = b[j];
+    const uint32_t lo = __builtin_amdgcn_perm(y, x, 0x05040100u);   // (x.lo, y.lo)
+    const uint32_t hi = __builtin_amdgcn_perm(y, x, 0x07060302u);   // (x.hi, y.hi)
+    o[2 * j] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2, lo), o[2 * j], false);
+    o[2 * j + 1] =
+        __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2, hi), o[2 * j + 1], false);
+  }
+}
+
+__device__ __forceinline__ int halo_offset(int kk, int HY, int HX) {
+  return ((kk / 9) - 1) * HY * HX + (((kk / 3) % 3) - 1) * HX + (kk % 3) - 1;
+}
+}  // namespace
+
+// Stages the slots of the halo box (-1 off the grid) and the (cos, sin) rows
+// of its coordinate range; all loads first, then the LDS writes.
+template <int NT, int HZ, int HY, int HX, int P>
+__device__ __forceinline__ void stage_box(const Geo &g, const int32_t *slot, const float2 *tab,
+                                          int z0, int y0, int x0, int *sSlot, float2 *sCS) {
+  constexpr int NH = HZ * HY * HX, NTAB = (HZ + HY + HX) * P;
+  constexpr int RT = (NTAB + NT - 1) / NT, RSL = (NH + NT - 1) / NT;
+  float2 tv[RT];
+  int sv[RSL];
+#pragma unroll
+  for (int r = 0; r < RT; r++) {
+    const int e = min((int)threadIdx.x + r * NT, NTAB - 1);
+    const int row = e / P, p = e % P;
+    int a, c;
+    if (row < HZ) { a = 0; c = z0 - 1 + row; }
+    else if (row < HZ + HY) { a = 1; c = y0 - 1 + row - HZ; }
+    else { a = 2; c = x0 - 1 + row - HZ - HY; }
+    const int dim = a == 0 ? g.Z : (a == 1 ? g.Y : g.X);
+    tv[r] = rope_cs(tab, g, a, min(max(c, 0), dim - 1), p);
+  }
+#pragma unroll
+  for (int r = 0; r < RSL; r++) {
+    const int hs = min((int)threadIdx.x + r * NT, NH - 1);
+    const int hz = hs / (HY * HX), hy = (hs / HX) % HY, hx = hs % HX;
+    const int z = z0 - 1 + hz, y = y0 - 1 + hy, x = x0 - 1 + hx;
+    const bool on = z >= 0 && y >= 0 && x >= 0 && z < g.Z && y < g.Y && x < g.X;
+    const int j = slot[on ? site_of(g, z, y, x) : 0];
+    sv[r] = on ? j : -1;
+  }
+#pragma unroll
+  for (int r = 0; r < RT; r++)
+    if ((int)threadIdx.x + r * NT < NTAB) sCS[threadIdx.x + r * NT] = tv[r];
+#pragma unroll
+  for (int r = 0; r < RSL; r++)
+    if ((int)threadIdx.x + r * NT < NH) sSlot[threadIdx.x + r * NT] = sv[r];
+}
+
+// ---------------------------------------------------------------------------
+template <int D, int TZ, int TY, int TX>
+__global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_bwd_local_q_pair(
+    Geo g, const void *geom, const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+    const bf16 *__restrict__ v, const bf16 *__restrict__ gate, const bf16 *__restrict__ dout,
+    const bf16 *__restrict__ oglob, const float *__restrict__ dqg, bf16 *dq, bf16 *dgate,
+    float *lse_l, float *delta_l, int ntz, int nty, int ntx) {
+  constexpr int HZ = TZ + 2, HY = TY + 2, HX = TX + 2, NH = HZ * HY * HX, NQ = TZ * TY * TX;
+  constexpr int LPQ = D / 24, NT = LPQ * NQ, DA = D / 3, DH = 24, P = D / 6;
+  constexpr int CPS = D / 8, NCK = NH * CPS, RS = (NCK + NT - 1) / NT;
+  static_assert(D % 48 == 0 && (LPQ == 2 || LPQ == 4), "head dim 48 or 96");
+  __shared__ __attribute__((aligned(16))) bf16 sK[RS * NT * 8];
+  __shared__ __attribute__((aligned(16))) bf16 sV[RS * NT * 8];
+  __shared__ int sSlot[NH];
+  __shared__ float2 sCS[(HZ + HY + HX) * P];
+
+  const int ntiles = ntz * nty * ntx;
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = w % g.H, tile = (w / g.H) % ntiles, b = w / (g.H * ntiles);
+  const int hk = h / g.G;
+  const int z0 = (tile / (nty * ntx)) * TZ, y0 = ((tile / ntx) % nty) * TY, x0 = (tile % ntx) * TX;
+  const int64_t bN = (int64_t)b * g.N;
+  auto cs_at = [&](int a, int rc, int p) {
+    const int base = a == 0 ? 0 : (a == 1 ? HZ : HZ + HY);
+    return sCS[(base + rc) * P + p];
+  };
+  stage_box<NT, HZ, HY, HX, P>(g, slot_map(geom, g), rope_table(geom, g), z0, y0, x0, sSlot, sCS);
+  __syncthreads();
+
+  const int qn = threadIdx.x / LPQ, hh = threadIdx.x % LPQ;
+  const int tz = qn / (TY * TX), ty = (qn / TX) % TY, tx = qn % TX;
+  const int qs = ((tz + 1) * HY + (ty + 1)) * HX + (tx + 1);
+  const int i = sSlot[qs];
+  const int wbase = __builtin_amdgcn_readfirstlane(threadIdx.x & ~63);
+  // all global loads first: raw K chunks, V straight to LDS, this lane's q,
+  // dO, O_glob, dq~_glob slices and the gate
+  bf16x8 kraw[RS];
+#pragma unroll
+  for (int r = 0; r < RS; r++) {
+    const int e = min((int)threadIdx.x + r * NT, NCK - 1);
+    const int hs = e / CPS, ch = e % CPS;
+    const int64_t off = ((bN + max(sSlot[hs], 0)) * g.Hkv + hk) * D + ch * 8;
+    kraw[r] = *reinterpret_cast<const bf16x8 *>(k + off);
+    __builtin_amdgcn_global_load_lds(v + off, (lds_ptr)&sV[(wbase + r * NT) * 8], 16, 0, 0);
+  }
+  const int64_t row = (bN + max(i, 0)) * g.H + h;
+  const int64_t off = row * D + hh * DH;
+  bf16x8 qraw[DH / 8], draw[DH / 8], oraw[DH / 8];
+  f32x4 gq[DH / 4];
+#pragma unroll
+  for (int c8 = 0; c8 < DH / 8; c8++) {
+    qraw[c8] = *reinterpret_cast<const bf16x8 *>(q + off + 8 * c8);
+    draw[c8] = *reinterpret_cast<const bf16x8 *>(dout + off + 8 * c8);
+    oraw[c8] = *reinterpret_cast<const bf16x8 *>(oglob + off + 8 * c8);
+  }
+#pragma unroll
+  for (int c4 = 0; c4 < DH / 4; c4++) gq[c4] = *reinterpret_cast<const f32x4 *>(dqg + off + 4 * c4);
+  const float gl = (float)gate[row];
+  // rotate the staged keys at their own coordinates, as the forward does
+#pragma unroll
+  for (int r = 0; r < RS; r++) {
+    const int e = (int)threadIdx.x + r * NT;
+    const int ec = min(e, NCK - 1);
+    const int hs = ec / CPS, ch = ec % CPS;
+    const int rc3[3] = {hs / (HY * HX), (hs / HX) % HY, hs % HX};
+    const int a = (ch * 8) / DA, p0 = ((ch * 8) % DA) / 2;
+    bf16x8 ko;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      float k0 = (float)kraw[r][2 * u], k1 = (float)kraw[r][2 * u + 1];
+      rotate(k0, k1, cs_at(a, rc3[a], p0 + u));
+      ko[2 * u] = (bf16)k0;
+      ko[2 * u + 1] = (bf16)k1;
+    }
+    *reinterpret_cast<bf16x8 *>(&sK[e * 8]) = ko;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (i < 0) return;
+  const float qscale = g.scale * kLog2e;
+  const int rc3[3] = {tz + 1, ty + 1, tx + 1};
+
+  bf16x2 qp[DH / 2], dp[DH / 2];
+#pragma unroll
+  for (int c8 = 0; c8 < DH / 8; c8++) {
+    const int d0 = hh * DH + 8 * c8, a = d0 / DA, p0 = (d0 % DA) / 2;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      float x0 = (float)qraw[c8][2 * u], x1 = (float)qraw[c8][2 * u + 1];
+      rotate(x0, x1, cs_at(a, rc3[a], p0 + u));
+      qp[4 * c8 + u][0] = (bf16)(x0 * qscale);
+      qp[4 * c8 + u][1] = (bf16)(x1 * qscale);
+      dp[4 * c8 + u][0] = draw[c8][2 * u];
+      dp[4 * c8 + u][1] = draw[c8][2 * u + 1];
+    }
+  }
+  // logits (log2 units) and u_j = <dO, v_j>, canonical offset order
+  float lg[27], uu[27];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kk = 0; kk < 27; kk++) {
+    const int hs = qs + halo_offset(kk, HY, HX);
+    const bf16x2 *kr = reinterpret_cast<const bf16x2 *>(sK + hs * D + hh * DH);
+    const bf16x2 *vr = reinterpret_cast<const bf16x2 *>(sV + hs * D + hh * DH);
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < DH / 2; j++) {
+      a0 = __builtin_amdgcn_fdot2_f32_bf16(qp[j], kr[j], a0, false);
+      a1 = __builtin_amdgcn_fdot2_f32_bf16(dp[j], vr[j], a1, false);
+    }
+    a0 = lane_sum<LPQ>(a0);
+    uu[kk] = lane_sum<LPQ>(a1);
+    lg[kk] = sSlot[hs] >= 0 ? a0 : -INFINITY;
+    mx = fmaxf(mx, lg[kk]);
+  }
+  float den = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < 27; kk++) {
+    lg[kk] = __builtin_amdgcn_exp2f(lg[kk] - mx);  // 0 for an invalid neighbour
+    den += lg[kk];
+  }
+  const float inv = 1.0f / den;
+  asm volatile("" ::: "memory");  // the next phase re-reads its rows from LDS
+  float dol = 0.f;  // <dO, O_loc>
+#pragma unroll
+  for (int kk = 0; kk < 27; kk++) {
+    lg[kk] *= inv;
+    dol += lg[kk] * uu[kk];
+  }
+  const float gg = 1.0f / (1.0f + expf(-gl)), omg = 1.0f - gg;
+  const float delta = omg * dol;
+  // dq~ = sum_j dS_j k~_j, two neighbours per step (the last step's second
+  // member has weight 0)
+  float acc[DH];
+#pragma unroll
+  for (int d = 0; d < DH; d++) acc[d] = 0.f;
+#pragma unroll
+  for (int kp = 0; kp < 14; kp++) {
+    const int k0 = 2 * kp, k1 = kp < 13 ? 2 * kp + 1 : 2 * kp;
+    const float w0 = lg[k0] * (omg * uu[k0] - delta);
+    const float w1 = kp < 13 ? lg[k1] * (omg * uu[k1] - delta) : 0.f;
+    pair_accumulate<DH>(acc, w0, w1, sK + (qs + halo_offset(k0, HY, HX)) * D + hh * DH,
+                        sK + (qs + halo_offset(k1, HY, HX)) * D + hh * DH);
+  }
+  // dq = R^T (s dq~_loc + dq~_glob); dG = g (1 - g) (<dO, O_glob> - <dO, O_loc>)
+  float dgo = 0.f;
+  bf16x8 outv[DH / 8];
+#pragma unroll
+  for (int c8 = 0; c8 < DH / 8; c8++) {
+    const int d0 = hh * DH + 8 * c8, a = d0 / DA, p0 = (d0 % DA) / 2;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int c = 8 * c8 + 2 * u;
+      float x0 = g.scale * acc[c] + gq[c / 4][c % 4];
+      float x1 = g.scale * acc[c + 1] + gq[(c + 1) / 4][(c + 1) % 4];
+      rotate_t(x0, x1, cs_at(a, rc3[a], p0 + u));
+      outv[c8][2 * u] = (bf16)x0;
+      outv[c8][2 * u + 1] = (bf16)x1;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; e++) dgo += (float)draw[c8][e] * (float)oraw[c8][e];
+  }
+#pragma unroll
+  for (int c8 = 0; c8 < DH / 8; c8++) *reinterpret_cast<bf16x8 *>(dq + off + 8 * c8) = outv[c8];
+  dgo = lane_sum<LPQ>(dgo);
+  if (hh == 0) {
+    dgate[row] = (bf16)(gg * omg * (dgo - dol));
+    lse_l[row] = mx + __log2f(den);
+    delta_l[row] = delta;
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int D, int TZ, int TY, int TX, bool CENTRE>
+__global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_bwd_local_kv_pair(
+    Geo g, const void *geom, const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+    const bf16 *__restrict__ v, const bf16 *__restrict__ gate, const bf16 *__restrict__ dout,
+    const float *__restrict__ lse_l, const float *__restrict__ delta_l,
+    const float *__restrict__ dks, const float *__restrict__ dvs, bf16 *dk, bf16 *dv, int ntz,
+    int nty, int ntx) {
+  constexpr int HZ = TZ + 2, HY = TY + 2, HX = TX + 2, NH = HZ * HY * HX, NQ = TZ * TY * TX;
+  constexpr int LPQ = D / 24, NT = LPQ * NQ, DA = D / 3, DH = 24, P = D / 6;
+  constexpr int CPS = D / 8, NCK = NH * CPS, RS = (NCK + NT - 1) / NT, RSL = (NH + NT - 1) / NT;
+  static_assert(D % 48 == 0 && (LPQ == 2 || LPQ == 4), "head dim 48 or 96");
+  __shared__ __attribute__((aligned(16))) bf16 sQ[RS * NT * 8];
+  __shared__ __attribute__((aligned(16))) bf16 sO[RS * NT * 8];
+  __shared__ int sSlot[NH];
+  __shared__ float2 sCS[(HZ + HY + HX) * P];
+  __shared__ float sOmg[NH], sL[NH], sDl[NH];
+
+  const int ntiles = ntz * nty * ntx;
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int hk = w % g.Hkv, tile = (w / g.Hkv) % ntiles, b = w / (g.Hkv * ntiles);
+  const int z0 = (tile / (nty * ntx)) * TZ, y0 = ((tile / ntx) % nty) * TY, x0 = (tile % ntx) * TX;
+  const int64_t bN = (int64_t)b * g.N;
+  const float2 *tab = rope_table(geom, g);
+  auto cs_at = [&](int a, int rc, int p) {
+    const int base = a == 0 ? 0 : (a == 1 ? HZ : HZ + HY);
+    return sCS[(base + rc) * P + p];
+  };
+  stage_box<NT, HZ, HY, HX, P>(g, slot_map(geom, g), tab, z0, y0, x0, sSlot, sCS);
+  __syncthreads();
+
+  const int kn = threadIdx.x / LPQ, hh = threadIdx.x % LPQ;
+  const int tz = kn / (TY * TX), ty = (kn / TX) % TY, tx = kn % TX;
+  const int ks_ = ((tz + 1) * HY + (ty + 1)) * HX + (tx + 1);
+  const int j = sSlot[ks_];
+  const int rc3[3] = {tz + 1, ty + 1, tx + 1};
+  const int wbase = __builtin_amdgcn_readfirstlane(threadIdx.x & ~63);
+  const float qscale = g.scale * kLog2e;
+  // this key's rotated bf16 slice (as the query side staged it) and values
+  const int64_t jrow = (bN + max(j, 0)) * g.Hkv + hk;
+  const int64_t joff = jrow * D + hh * DH;
+  bf16x2 kp[DH / 2], vp[DH / 2];
+#pragma unroll
+  for (int c8 = 0; c8 < DH / 8; c8++) {
+    const bf16x8 kr = *reinterpret_cast<const bf16x8 *>(k + joff + 8 * c8);
+    const bf16x8 vr = *reinterpret_cast<const bf16x8 *>(v + joff + 8 * c8);
+    const int d0 = hh * DH + 8 * c8, a = d0 / DA, p0 = (d0 % DA) / 2;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      float k0 = (float)kr[2 * u], k1 = (float)kr[2 * u + 1];
+      rotate(k0, k1, cs_at(a, rc3[a], p0 + u));
+      kp[4 * c8 + u][0] = (bf16)k0;
+      kp[4 * c8 + u][1] = (bf16)k1;
+      vp[4 * c8 + u][0] = vr[2 * u];
+      vp[4 * c8 + u][1] = vr[2 * u + 1];
+    }
+  }
+  float adk[DH], adv[DH];
+#pragma unroll
+  for (int d = 0; d < DH; d++) adk[d] = adv[d] = 0.f;
+
+  for (int h = hk * g.G; h < (hk + 1) * g.G; h++) {
+    __syncthreads();  // the previous head's stage is no longer read
+    // all loads first: raw q chunks, dO straight to LDS, per-site statistics
+    bf16x8 qraw[RS];
+#pragma unroll
+    for (int r = 0; r < RS; r++) {
+      const int e = min((int)threadIdx.x + r * NT, NCK - 1);
+      const int hs = e / CPS, ch = e % CPS;
+      const int64_t off = ((bN + max(sSlot[hs], 0)) * g.H + h) * D + ch * 8;
+      qraw[r] = *reinterpret_cast<const bf16x8 *>(q + off);
+      __builtin_amdgcn_global_load_lds(dout + off, (lds_ptr)&sO[(wbase + r * NT) * 8], 16, 0, 0);
+    }
+    float st_g[RSL], st_l[RSL], st_d[RSL];
+#pragma unroll
+    for (int r = 0; r < RSL; r++) {
+      const int hs = min((int)threadIdx.x + r * NT, NH - 1);
+      const int64_t srow = (bN + max(sSlot[hs], 0)) * g.H + h;
+      st_g[r] = (float)gate[srow];
+      st_l[r] = lse_l[srow];
+      st_d[r] = delta_l[srow];
+    }
+#pragma unroll
+    for (int r = 0; r < RS; r++) {
+      const int e = (int)threadIdx.x + r * NT;
+      const int ec = min(e, NCK - 1);
+      const int hs = ec / CPS, ch = ec % CPS;
+      const int qc3[3] = {hs / (HY * HX), (hs / HX) % HY, hs % HX};
+      const int a = (ch * 8) / DA, p0 = ((ch * 8) % DA) / 2;
+      bf16x8 qo;
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        float x0 = (float)qraw[r][2 * u], x1 = (float)qraw[r][2 * u + 1];
+        rotate(x0, x1, cs_at(a, qc3[a], p0 + u));
+        qo[2 * u] = (bf16)(x0 * qscale);
+        qo[2 * u + 1] = (bf16)(x1 * qscale);
+      }
+      *reinterpret_cast<bf16x8 *>(&sQ[e * 8]) = qo;
+    }
+#pragma unroll
+    for (int r = 0; r < RSL; r++) {
+      const int hs = (int)threadIdx.x + r * NT;
+      if (hs < NH) {
+        sOmg[hs] = 1.0f - 1.0f / (1.0f + expf(-st_g[r]));
+        sL[hs] = st_l[r];
+        sDl[hs] = st_d[r];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j < 0) continue;
+    // logits (the query side's, bit for bit) and u_ij = <dO_i, v_j>
+    float pw[27], dsw[27];
+#pragma unroll
+    for (int kk = 0; kk < 27; kk++) {
+      const int hs = ks_ + halo_offset(kk, HY, HX);
+      const bf16x2 *qr = reinterpret_cast<const bf16x2 *>(sQ + hs * D + hh * DH);
+      const bf16x2 *orr = reinterpret_cast<const bf16x2 *>(sO + hs * D + hh * DH);
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < DH / 2; jj++) {
+        a0 = __builtin_amdgcn_fdot2_f32_bf16(qr[jj], kp[jj], a0, false);
+        a1 = __builtin_amdgcn_fdot2_f32_bf16(orr[jj], vp[jj], a1, false);
+      }
+      a0 = lane_sum<LPQ>(a0);
+      a1 = lane_sum<LPQ>(a1);
+      const bool valid = sSlot[hs] >= 0;
+      const float pr = valid ? __builtin_amdgcn_exp2f(a0 - sL[hs]) : 0.f;
+      pw[kk] = pr * sOmg[hs];
+      dsw[kk] = pr * (sOmg[hs] * a1 - sDl[hs]);
+    }
+    asm volatile("" ::: "memory");  // the next phase re-reads its rows from LDS
+#pragma unroll
+    for (int kp2 = 0; kp2 < 14; kp2++) {
+      const int k0 = 2 * kp2, k1 = kp2 < 13 ? 2 * kp2 + 1 : 2 * kp2;
+      const int hs0 = ks_ + halo_offset(k0, HY, HX), hs1 = ks_ + halo_offset(k1, HY, HX);
+      const float c1 = kp2 < 13 ? 1.f : 0.f;
+      pair_accumulate<DH>(adk, dsw[k0], c1 * dsw[k1], sQ + hs0 * D + hh * DH, sQ + hs1 * D + hh * DH);
+      pair_accumulate<DH>(adv, pw[k0], c1 * pw[k1], sO + hs0 * D + hh * DH, sO + hs1 * D + hh * DH);
+    }
+  }
+  if (j < 0) return;
+  // pooling transpose, then dk = R(c_j)^T dk~ (centre variant: its block part
+  // goes through R(centre)^T instead)
+  const int c3[3] = {z0 + tz, y0 + ty, x0 + tx};
+  const int m = block_of(g, c3[0], c3[1], c3[2]);
+  const int mz = m / (g.My * g.Mx), my = (m / g.Mx) % g.My, mx = m % g.Mx;
+  const int nm = min(g.bz, g.Z - mz * g.bz) * min(g.by, g.Y - my * g.by) * min(g.bx, g.X - mx * g.bx);
+  const float inv_n = 1.0f / (float)nm;
+  const float *gk = dks + ((((int64_t)b * g.Hkv + hk) * g.M + m) * D + hh * DH);
+  const float *gv = dvs + ((((int64_t)b * g.Hkv + hk) * g.M + m) * D + hh * DH);
+  bf16x8 okv[DH / 8], ovv[DH / 8];
+#pragma unroll
+  for (int c8 = 0; c8 < DH / 8; c8++) {
+    const int d0 = hh * DH + 8 * c8, a = d0 / DA, p0 = (d0 % DA) / 2;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int c = 8 * c8 + 2 * u;
+      float x0 = kLn2 * adk[c], x1 = kLn2 * adk[c + 1];  // s / (s log2 e)
+      if (!CENTRE) {
+        x0 += gk[c] * inv_n;
+        x1 += gk[c + 1] * inv_n;
+      }
+      rotate_t(x0, x1, cs_at(a, rc3[a], p0 + u));
+      if (CENTRE) {
+        const int mzz = m / (g.My * g.Mx), myy = (m / g.Mx) % g.My, mxx = m % g.Mx;
+        const int o = a == 0 ? mzz * g.bz : (a == 1 ? myy * g.by : mxx * g.bx);
+        const int ext = min(a == 0 ? g.bz : (a == 1 ? g.by : g.bx),
+                            (a == 0 ? g.Z : (a == 1 ? g.Y : g.X)) - o);
+        float2 t = rope_cs(tab, g, a, o + (ext - 1) / 2, p0 + u);
+        if ((ext & 1) == 0) {
+          const float2 hf = rope_half(tab, g, p0 + u);
+          t = make_float2(t.x * hf.x - t.y * hf.y, t.y * hf.x + t.x * hf.y);
+        }
+        float y0 = gk[c] * inv_n, y1 = gk[c + 1] * inv_n;
+        rotate_t(y0, y1, t);
+        x0 += y0;
+        x1 += y1;
+      }
+      okv[c8][2 * u] = (bf16)x0;
+      okv[c8][2 * u + 1] = (bf16)x1;
+      ovv[c8][2 * u] = (bf16)(adv[c] + gv[c] * inv_n);
+      ovv[c8][2 * u + 1] = (bf16)(adv[c + 1] + gv[c + 1] * inv_n);
+    }
+  }
+#pragma unroll
+  for (int c8 = 0; c8 < DH / 8; c8++) {
+    *reinterpret_cast<bf16x8 *>(dk + joff + 8 * c8) = okv[c8];
+    *reinterpret_cast<bf16x8 *>(dv + joff + 8 * c8) = ovv[c8];
+  }
+}
+
+// ---------------------------------------------------------------------------
+namespace {
+template <int D, int TZ, int TY, int TX>
+hipError_t run_local_bwd_pair(const Geo &g, const BwdArgs &a, hipStream_t s) {
+  const int ntz = (g.Z + TZ - 1) / TZ, nty = (g.Y + TY - 1) / TY, ntx = (g.X + TX - 1) / TX;
+  const int nt = (D / 24) * TZ * TY * TX;
+  hipLaunchKernelGGL((k_bwd_local_q_pair<D, TZ, TY, TX>),
+                     dim3((unsigned)(g.B * ntz * nty * ntx * g.H)), dim3(nt), 0, s, g, a.geom,
+                     static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.k),
+                     static_cast<const bf16 *>(a.v), static_cast<const bf16 *>(a.gate),
+                     static_cast<const bf16 *>(a.dout), static_cast<const bf16 *>(a.oglob), a.dqg,
+                     static_cast<bf16 *>(a.dq), static_cast<bf16 *>(a.dgate), a.lse_l, a.delta_l,
+                     ntz, nty, ntx);
+  if (hipError_t e = hipGetLastError()) return e;
+  auto kv = (g.flags & PACK3D_SUMMARY_CENTRE) ? k_bwd_local_kv_pair<D, TZ, TY, TX, true>
+                                               : k_bwd_local_kv_pair<D, TZ, TY, TX, false>;
+  hipLaunchKernelGGL(kv, dim3((unsigned)(g.B * ntz * nty * ntx * g.Hkv)), dim3(nt), 0, s, g, a.geom,
+                     static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.k),
+                     static_cast<const bf16 *>(a.v), static_cast<const bf16 *>(a.gate),
+                     static_cast<const bf16 *>(a.dout), a.lse_l, a.delta_l, a.dks, a.dvs,
+                     static_cast<bf16 *>(a.dk), static_cast<bf16 *>(a.dv), ntz, nty, ntx);
+  return hipGetLastError();
+}
+}  // namespace
+
+bool bwd_local_pair_supported(const Geo &g, int dtype) {
+  return dtype == PACK3D_BF16 && (g.D == 48 || g.D == 96);
+}
+
+hipError_t launch_bwd_local_pair(const Geo &g, const BwdArgs &a, hipStream_t s) {
+  if (g.D == 48) return run_local_bwd_pair<48, 4, 4, 8>(g, a, s);
+  return run_local_bwd_pair<96, 2, 4, 8>(g, a, s);
+}
+
+}  // namespace pk
