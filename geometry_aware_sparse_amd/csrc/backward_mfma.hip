@@ -28,6 +28,8 @@
 //   k_bwd_gk_mfma     summary side: a wave owns 32 summaries and streams the
 //                     query sites of one split of the site range through LDS
 //   k_bwd_split_sum   the splits' partial sums, added in split order
+#include <type_traits>
+
 #include "launch.hpp"
 
 namespace pk {
@@ -43,7 +45,7 @@ __device__ __forceinline__ int swap23(int r) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Position p of (b, h) is grid site p (raster order), p < Np = 32*ceil(N/32):
+// Position p of (b, h) is grid site p (raster order), p < Np = 128*ceil(N/128):
 //   qn [B*H, Np/32, D/8, 32, 8]  q~ s log2(e): row p%32 of 32-row block p/32
 //   qt [B*H, Np/8, D, 8]         the same, channel-major: 8 sites per chunk
 //   dn, dt                       dO_glob, likewise
@@ -125,7 +127,9 @@ __global__ void k_bwd_relayout(int64_t n, int Mp, const bf16 *__restrict__ ks,
 
 // ---------------------------------------------------------------------------
 // Query side. Workgroup: 4 waves x 32 query sites of one (b, h); summary tiles
-// of TS (two 32-summary sub-tiles for TS = 64) double-buffered in LDS.
+// of TS (NSUB 32-summary sub-tiles) double-buffered in LDS, filled by direct
+// global->LDS loads (16 bytes per lane, offsets computed once): the loads of
+// tile t+1 go out while tile t is used, one barrier per tile.
 template <int D, int TS>
 __global__ __launch_bounds__(256, 2) void k_bwd_gq_mfma(
     Geo g, const bf16 *__restrict__ qn, const bf16 *__restrict__ dn,
@@ -134,28 +138,27 @@ __global__ __launch_bounds__(256, 2) void k_bwd_gq_mfma(
     const bf16 *__restrict__ kt, float *dqg, int Np, int ntiles) {
   constexpr int KD = D / 16, NCH = D / 8, DT = (D + 31) / 32, NSUB = TS / 32;
   constexpr int NJ8 = TS / 8;
-  // chunks per tile: k_sum and vk rows (NCH x TS), kt (NJ8 x D)
+  // chunks per tile: k_sum and vk rows (NCH x TS), kt (NJ8 x D); whole waves
   constexpr int NKC = NCH * TS, NTC = NJ8 * D;
-  __shared__ bf16x8 sK[2][NKC], sVK[2][NKC], sKT[2][NTC];
+  static_assert(NKC % 64 == 0 && NTC % 64 == 0, "tile loads in whole waves");
+  constexpr int RK = (NKC + 255) / 256, RT = (NTC + 255) / 256;
+  __shared__ bf16x8 sK0[NKC], sK1[NKC], sV0[NKC], sV1[NKC], sT0[NTC], sT1[NTC];
   const int w = xcd_remap(blockIdx.x, gridDim.x);
   const int tile = w % ntiles, bh = w / ntiles;
   const int h = bh % g.H, b = bh / g.H;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hi = lane >> 5, l32 = lane & 31;
-  const int Mp = (g.M + 31) / 32 * 32;
+  const int lane = threadIdx.x & 63, hi = lane >> 5, l32 = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int Mp = (g.M + 31) / 32 * 32, M32 = Mp / 32;
   const int64_t bk = (int64_t)b * g.Hkv + h / g.G;
-  // this lane's query site; past Np (the last tile's tail) it loads site
-  // Np - 1 and takes no part (P = 0)
-  const int p = tile * (kWaves * 32) + wv * 32 + l32;
-  const int pc = min(p, Np - 1);
+  const int p = tile * (kWaves * 32) + wv * 32 + l32;  // this lane's query site (Np is 128-aligned)
   bf16x8 qf[KD], df[KD];
 #pragma unroll
   for (int c = 0; c < KD; c++) {
-    const int64_t o = ((((int64_t)bh * (Np / 32) + pc / 32) * NCH + 2 * c + hi) * 32 + pc % 32) * 8;
+    const int64_t o = ((((int64_t)bh * (Np / 32) + p / 32) * NCH + 2 * c + hi) * 32 + p % 32) * 8;
     qf[c] = *reinterpret_cast<const bf16x8 *>(qn + o);
     df[c] = *reinterpret_cast<const bf16x8 *>(dn + o);
   }
-  const float lq = p < Np ? lse_p[(int64_t)bh * Np + pc] : INFINITY;
-  const float dq = dl_p[(int64_t)bh * Np + pc];
+  const float lq = lse_p[(int64_t)bh * Np + p], dq = dl_p[(int64_t)bh * Np + p];
   f32x16 acc[DT];
 #pragma unroll
   for (int t = 0; t < DT; t++)
@@ -163,82 +166,92 @@ __global__ __launch_bounds__(256, 2) void k_bwd_gq_mfma(
     for (int j = 0; j < 16; j++) acc[t][j] = 0.f;
   const f32x16 zero16 = {};
 
-  // tile loads: chunk e of a row tile = (ch, pos), pos = 32*sub + r holding
-  // summary swap23(r) of sub-tile sub; chunk e of the kt tile = (j8, d)
-  const int ntile = Mp / TS + (Mp % TS ? 1 : 0);
-  constexpr int RK = (NKC + 255) / 256, RT = (NTC + 255) / 256;
-  bf16x8 rk[RK], rv[RK], rt[RT];
-  auto load = [&](int tt) {
+  // per-lane parts of the tile offsets: row chunk e = (ch, pos) holds summary
+  // 32*(pos/32) + swap23(pos%32) of the tile; kt chunk e = (j8, d)
+  int rk_sub[RK], rk_in[RK], rt_j8[RT], rt_d[RT];
+#pragma unroll
+  for (int r = 0; r < RK; r++) {
+    const int e = 256 * r + 64 * wv + lane;
+    const int ch = e / TS, pos = e % TS;
+    rk_sub[r] = pos / 32;
+    rk_in[r] = (ch * 32 + swap23(pos % 32)) * 8;
+  }
+#pragma unroll
+  for (int r = 0; r < RT; r++) {
+    const int e = 256 * r + 64 * wv + lane;
+    rt_j8[r] = e / D;
+    rt_d[r] = e % D;
+  }
+  auto issue = [&](int tt, bf16x8 *dK, bf16x8 *dV, bf16x8 *dT) {
 #pragma unroll
     for (int r = 0; r < RK; r++) {
-      const int e = min((int)threadIdx.x + 256 * r, NKC - 1);
-      const int ch = e / TS, pos = e % TS;
-      const int m = min(tt * TS + 32 * (pos / 32) + swap23(pos % 32), Mp - 1);
-      const int64_t o = (((bk * (Mp / 32) + m / 32) * NCH + ch) * 32 + m % 32) * 8;
-      rk[r] = *reinterpret_cast<const bf16x8 *>(ks + o);
-      rv[r] = *reinterpret_cast<const bf16x8 *>(vk + o);
-    }
-#pragma unroll
-    for (int r = 0; r < RT; r++) {
-      const int e = min((int)threadIdx.x + 256 * r, NTC - 1);
-      const int j8 = e / D, d = e % D;
-      const int g8 = min(tt * NJ8 + j8, Mp / 8 - 1);
-      rt[r] = *reinterpret_cast<const bf16x8 *>(kt + ((bk * (Mp / 8) + g8) * D + d) * 8);
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < RK; r++) {
-      const int e = (int)threadIdx.x + 256 * r;
-      if (e < NKC) {
-        sK[buf][e] = rk[r];
-        sVK[buf][e] = rv[r];
+      if (256 * r + 64 * wv < NKC) {  // wave-uniform
+        const int m32 = min(tt * NSUB + rk_sub[r], M32 - 1);
+        const int64_t o = (bk * M32 + m32) * (NCH * 256) + rk_in[r];
+        __builtin_amdgcn_global_load_lds(ks + o, (lds_ptr)&dK[256 * r + 64 * wv], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vk + o, (lds_ptr)&dV[256 * r + 64 * wv], 16, 0, 0);
       }
     }
 #pragma unroll
     for (int r = 0; r < RT; r++) {
-      const int e = (int)threadIdx.x + 256 * r;
-      if (e < NTC) sKT[buf][e] = rt[r];
+      if (256 * r + 64 * wv < NTC) {
+        const int g8 = min(tt * NJ8 + rt_j8[r], 4 * M32 - 1);
+        const int64_t o = ((bk * 4 * M32 + g8) * D + rt_d[r]) * 8;
+        __builtin_amdgcn_global_load_lds(kt + o, (lds_ptr)&dT[256 * r + 64 * wv], 16, 0, 0);
+      }
     }
   };
-  load(0);
-  store(0);
+  // one 32-summary sub-tile; MASK zeroes the summaries at or past M
+  auto sub_step = [&](const bf16x8 *K, const bf16x8 *V, const bf16x8 *T, int sub, int mbase,
+                      auto mask) {
+    f32x16 s, dp;
+#pragma unroll
+    for (int c = 0; c < KD; c++) {
+      const bf16x8 kf = K[(2 * c + hi) * TS + 32 * sub + l32];
+      const bf16x8 vf = V[(2 * c + hi) * TS + 32 * sub + l32];
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], c == 0 ? zero16 : s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[c], c == 0 ? zero16 : dp, 0, 0, 0);
+    }
+    // register j <-> summary mbase + 16*(j/8) + 8*hi + j%8
+    bf16x8 tf[2];
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      float t = __builtin_amdgcn_exp2f(s[j] - lq) * (dp[j] - dq);
+      if constexpr (decltype(mask)::value)
+        t = (mbase + 16 * (j >> 3) + 8 * hi + (j & 7) < g.M) ? t : 0.f;
+      tf[j >> 3][j & 7] = (bf16)t;
+    }
+#pragma unroll
+    for (int t = 0; t < DT; t++) {
+      const int d = min(32 * t + l32, D - 1);
+#pragma unroll
+      for (int c2 = 0; c2 < 2; c2++) {
+        const bf16x8 kf = T[(4 * sub + 2 * c2 + hi) * D + d];
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, tf[c2], acc[t], 0, 0, 0);
+      }
+    }
+  };
+  const int ntile = (M32 + NSUB - 1) / NSUB;
+  issue(0, sK0, sV0, sT0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int tt = 0; tt < ntile; tt++) {
-    const int buf = tt & 1;
-    if (tt + 1 < ntile) load(tt + 1);
+    const bool odd = tt & 1;
+    if (tt + 1 < ntile) {
+      if (odd) issue(tt + 1, sK0, sV0, sT0);
+      else issue(tt + 1, sK1, sV1, sT1);
+    }
+    const bf16x8 *K = odd ? sK1 : sK0, *V = odd ? sV1 : sV0, *T = odd ? sT1 : sT0;
 #pragma unroll
     for (int sub = 0; sub < NSUB; sub++) {
-      if (tt * TS + 32 * sub >= Mp) break;  // uniform
-      f32x16 s, dp;
-#pragma unroll
-      for (int c = 0; c < KD; c++) {
-        const bf16x8 kf = sK[buf][(2 * c + hi) * TS + 32 * sub + l32];
-        const bf16x8 vf = sVK[buf][(2 * c + hi) * TS + 32 * sub + l32];
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], c == 0 ? zero16 : s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[c], c == 0 ? zero16 : dp, 0, 0, 0);
-      }
-      // register j <-> summary mbase + 16*(j/8) + 8*hi + j%8; summaries past M
-      // (zero padding) are forced to 0 so that no inf * 0 can reach the sum
       const int mbase = tt * TS + 32 * sub;
-      bf16x8 tf[2];
-#pragma unroll
-      for (int j = 0; j < 16; j++) {
-        const float pr = __builtin_amdgcn_exp2f(s[j] - lq);
-        const bool real = mbase + 16 * (j >> 3) + 8 * hi + (j & 7) < g.M;
-        tf[j >> 3][j & 7] = (bf16)(real ? pr * (dp[j] - dq) : 0.f);
-      }
-#pragma unroll
-      for (int t = 0; t < DT; t++) {
-        const int d = min(32 * t + l32, D - 1);
-#pragma unroll
-        for (int c2 = 0; c2 < 2; c2++) {
-          const bf16x8 kf = sKT[buf][(4 * sub + 2 * c2 + hi) * D + d];
-          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, tf[c2], acc[t], 0, 0, 0);
-        }
-      }
+      if (mbase >= Mp) break;  // uniform: the last tile may be partial
+      if (mbase + 32 <= g.M)
+        sub_step(K, V, T, sub, mbase, std::false_type{});
+      else
+        sub_step(K, V, T, sub, mbase, std::true_type{});
     }
-    if (tt + 1 < ntile) store(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
     __syncthreads();
   }
   // lane: query site p (column l32), rows d = 32t + 8jj + 4hi + u
@@ -261,8 +274,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_gq_mfma(
 
 // ---------------------------------------------------------------------------
 // Summary side. Workgroup: 4 waves x 32 summaries of one (b, hk), one split
-// [p_begin, p_end) of the query sites of every head of the group; query
-// tiles of TQ sites double-buffered in LDS. Writes the split's partial sums.
+// of the query sites of every head of the group; query tiles of TQ sites
+// double-buffered in LDS by direct global->LDS loads (Np is a multiple of
+// 128, so every tile is whole). Writes the split's partial sums.
 template <int D, int TQ>
 __global__ __launch_bounds__(256, 2) void k_bwd_gk_mfma(
     Geo g, const bf16 *__restrict__ qn, const bf16 *__restrict__ qt, const bf16 *__restrict__ dn,
@@ -271,12 +285,16 @@ __global__ __launch_bounds__(256, 2) void k_bwd_gk_mfma(
     int Np, int mtiles, int nsplit) {
   constexpr int KD = D / 16, NCH = D / 8, DT = (D + 31) / 32, NSUB = TQ / 32, NJ8 = TQ / 8;
   constexpr int NNC = NCH * TQ, NTC = NJ8 * D;  // chunks per tile: row-blocked, transposed
-  __shared__ bf16x8 sQ[2][NNC], sDO[2][NNC], sQT[2][NTC], sDT[2][NTC];
-  __shared__ float sL[2][TQ], sDl[2][TQ];
+  static_assert(NNC % 64 == 0 && NTC % 64 == 0 && TQ <= 64, "tile loads in whole waves");
+  constexpr int RN = (NNC + 255) / 256, RTT = (NTC + 255) / 256;
+  __shared__ bf16x8 sQ0[NNC], sQ1[NNC], sD0[NNC], sD1[NNC];
+  __shared__ bf16x8 sQT0[NTC], sQT1[NTC], sDT0[NTC], sDT1[NTC];
+  __shared__ __attribute__((aligned(16))) float sL0[64], sL1[64], sDl0[64], sDl1[64];
   const int w = xcd_remap(blockIdx.x, gridDim.x);
   const int split = w % nsplit, mt = (w / nsplit) % mtiles, bk = w / (nsplit * mtiles);
   const int b = bk / g.Hkv, hk = bk % g.Hkv;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hi = lane >> 5, l32 = lane & 31;
+  const int lane = threadIdx.x & 63, hi = lane >> 5, l32 = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int Mp = (g.M + 31) / 32 * 32;
   const int m32 = min(mt * kWaves + wv, Mp / 32 - 1);  // this wave's 32 summaries
   const bool wave_live = mt * kWaves + wv < Mp / 32;
@@ -294,80 +312,72 @@ __global__ __launch_bounds__(256, 2) void k_bwd_gk_mfma(
     for (int j = 0; j < 16; j++) aK[t][j] = aV[t][j] = 0.f;
   const f32x16 zero16 = {};
 
-  // this split's query sites, in TQ tiles
-  const int nqt = Np / TQ + (Np % TQ ? 1 : 0);
+  const int nqt = Np / TQ;
   const int per = (nqt + nsplit - 1) / nsplit;
   const int qt0 = split * per, qt1 = min(nqt, qt0 + per);
-  const int ntile = max(qt1 - qt0, 0) * g.G;  // (head of the group, query tile) pairs
-  constexpr int RN = (NNC + 255) / 256, RTT = (NTC + 255) / 256;
-  bf16x8 rq[RN], rd[RN], rqt[RTT], rdt[RTT];
-  float rl = 0.f, rdl = 0.f;
-  auto load = [&](int it) {
-    const int h = hk * g.G + it / (qt1 - qt0), qtile = qt0 + it % (qt1 - qt0);
+  const int nq = max(qt1 - qt0, 0);
+  const int ntile = nq * g.G;  // (head of the group, query tile) pairs
+
+  int rn_sub[RN], rn_in[RN], rt_j8[RTT], rt_d[RTT];
+#pragma unroll
+  for (int r = 0; r < RN; r++) {
+    const int e = 256 * r + 64 * wv + lane;
+    const int ch = e / TQ, pos = e % TQ;
+    rn_sub[r] = pos / 32;
+    rn_in[r] = (ch * 32 + swap23(pos % 32)) * 8;
+  }
+#pragma unroll
+  for (int r = 0; r < RTT; r++) {
+    const int e = 256 * r + 64 * wv + lane;
+    rt_j8[r] = e / D;
+    rt_d[r] = e % D;
+  }
+  auto issue = [&](int it, bf16x8 *dQ, bf16x8 *dD, bf16x8 *dQT, bf16x8 *dDT, float *dL,
+                   float *dDl) {
+    const int h = hk * g.G + it / nq, qtile = qt0 + it % nq;
     const int64_t bh = (int64_t)b * g.H + h;
 #pragma unroll
     for (int r = 0; r < RN; r++) {
-      const int e = min((int)threadIdx.x + 256 * r, NNC - 1);
-      const int ch = e / TQ, pos = e % TQ;
-      const int p = min(qtile * TQ + 32 * (pos / 32) + swap23(pos % 32), Np - 1);
-      const int64_t o = (((bh * (Np / 32) + p / 32) * NCH + ch) * 32 + p % 32) * 8;
-      rq[r] = *reinterpret_cast<const bf16x8 *>(qn + o);
-      rd[r] = *reinterpret_cast<const bf16x8 *>(dn + o);
-    }
-#pragma unroll
-    for (int r = 0; r < RTT; r++) {
-      const int e = min((int)threadIdx.x + 256 * r, NTC - 1);
-      const int j8 = e / D, d = e % D;
-      const int p8 = min(qtile * NJ8 + j8, Np / 8 - 1);
-      const int64_t o = ((bh * (Np / 8) + p8) * D + d) * 8;
-      rqt[r] = *reinterpret_cast<const bf16x8 *>(qt + o);
-      rdt[r] = *reinterpret_cast<const bf16x8 *>(dt + o);
-    }
-    if (threadIdx.x < TQ) {
-      const int p = qtile * TQ + threadIdx.x;
-      // sites past Np do not exist: P = 0 there
-      rl = p < Np ? lse_p[bh * Np + p] : INFINITY;
-      rdl = p < Np ? dl_p[bh * Np + p] : 0.f;
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < RN; r++) {
-      const int e = (int)threadIdx.x + 256 * r;
-      if (e < NNC) {
-        sQ[buf][e] = rq[r];
-        sDO[buf][e] = rd[r];
+      if (256 * r + 64 * wv < NNC) {
+        const int64_t o = (bh * (Np / 32) + qtile * NSUB + rn_sub[r]) * (NCH * 256) + rn_in[r];
+        __builtin_amdgcn_global_load_lds(qn + o, (lds_ptr)&dQ[256 * r + 64 * wv], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(dn + o, (lds_ptr)&dD[256 * r + 64 * wv], 16, 0, 0);
       }
     }
 #pragma unroll
     for (int r = 0; r < RTT; r++) {
-      const int e = (int)threadIdx.x + 256 * r;
-      if (e < NTC) {
-        sQT[buf][e] = rqt[r];
-        sDT[buf][e] = rdt[r];
+      if (256 * r + 64 * wv < NTC) {
+        const int64_t o = ((bh * (Np / 8) + qtile * NJ8 + rt_j8[r]) * D + rt_d[r]) * 8;
+        __builtin_amdgcn_global_load_lds(qt + o, (lds_ptr)&dQT[256 * r + 64 * wv], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(dt + o, (lds_ptr)&dDT[256 * r + 64 * wv], 16, 0, 0);
       }
     }
-    if (threadIdx.x < TQ) {
-      sL[buf][threadIdx.x] = rl;
-      sDl[buf][threadIdx.x] = rdl;
+    // per-site statistics: wave 0 the log-sum-exp, wave 1 Delta (4 bytes a lane)
+    if (wv < 2) {
+      const float *src = (wv == 0 ? lse_p : dl_p) + bh * Np + qtile * TQ + min(lane, TQ - 1);
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr)(wv == 0 ? dL : dDl), 4, 0, 0);
     }
   };
-  if (ntile > 0) {
-    load(0);
-    store(0);
-  }
+  if (ntile > 0) issue(0, sQ0, sD0, sQT0, sDT0, sL0, sDl0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int it = 0; it < ntile; it++) {
-    const int buf = it & 1;
-    if (it + 1 < ntile) load(it + 1);
+    const bool odd = it & 1;
+    if (it + 1 < ntile) {
+      if (odd) issue(it + 1, sQ0, sD0, sQT0, sDT0, sL0, sDl0);
+      else issue(it + 1, sQ1, sD1, sQT1, sDT1, sL1, sDl1);
+    }
+    const bf16x8 *Q = odd ? sQ1 : sQ0, *Dd = odd ? sD1 : sD0;
+    const bf16x8 *QT = odd ? sQT1 : sQT0, *DTt = odd ? sDT1 : sDT0;
+    const float *L = odd ? sL1 : sL0, *Dl = odd ? sDl1 : sDl0;
 #pragma unroll
     for (int sub = 0; sub < NSUB; sub++) {
       // C[query rows][summary columns]: row r holds query site swap23(r)
       f32x16 s, dp;
 #pragma unroll
       for (int c = 0; c < KD; c++) {
-        const bf16x8 qa = sQ[buf][(2 * c + hi) * TQ + 32 * sub + l32];
-        const bf16x8 da = sDO[buf][(2 * c + hi) * TQ + 32 * sub + l32];
+        const bf16x8 qa = Q[(2 * c + hi) * TQ + 32 * sub + l32];
+        const bf16x8 da = Dd[(2 * c + hi) * TQ + 32 * sub + l32];
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb[c], c == 0 ? zero16 : s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vb[c], c == 0 ? zero16 : dp, 0, 0, 0);
       }
@@ -376,11 +386,16 @@ __global__ __launch_bounds__(256, 2) void k_bwd_gk_mfma(
 #pragma unroll
       for (int c2 = 0; c2 < 2; c2++) {
         const int q0 = 32 * sub + 16 * c2 + 8 * hi;
+        const f32x4 l0 = *reinterpret_cast<const f32x4 *>(L + q0);
+        const f32x4 l1 = *reinterpret_cast<const f32x4 *>(L + q0 + 4);
+        const f32x4 d0 = *reinterpret_cast<const f32x4 *>(Dl + q0);
+        const f32x4 d1 = *reinterpret_cast<const f32x4 *>(Dl + q0 + 4);
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-          const float pr = __builtin_amdgcn_exp2f(s[8 * c2 + e] - sL[buf][q0 + e]);
+          const float le = e < 4 ? l0[e] : l1[e - 4], de = e < 4 ? d0[e] : d1[e - 4];
+          const float pr = __builtin_amdgcn_exp2f(s[8 * c2 + e] - le);
           pa[c2][e] = (bf16)pr;
-          ta[c2][e] = (bf16)(pr * (dp[8 * c2 + e] - sDl[buf][q0 + e]));
+          ta[c2][e] = (bf16)(pr * (dp[8 * c2 + e] - de));
         }
       }
 #pragma unroll
@@ -389,14 +404,14 @@ __global__ __launch_bounds__(256, 2) void k_bwd_gk_mfma(
 #pragma unroll
         for (int c2 = 0; c2 < 2; c2++) {
           const int j8 = 4 * sub + 2 * c2 + hi;
-          const bf16x8 qb = sQT[buf][j8 * D + d];
-          const bf16x8 db = sDT[buf][j8 * D + d];
+          const bf16x8 qb = QT[j8 * D + d];
+          const bf16x8 db = DTt[j8 * D + d];
           aK[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[c2], qb, aK[t], 0, 0, 0);
           aV[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[c2], db, aV[t], 0, 0, 0);
         }
       }
     }
-    if (it + 1 < ntile) store(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   if (!wave_live) return;
@@ -430,7 +445,7 @@ namespace {
 template <int D, int TS, int TQ>
 hipError_t run_bwd_global_mfma(const Geo &g, const BwdArgs &a, const BwdMfmaArgs &m,
                                hipStream_t s) {
-  const int Np = (g.N + 31) / 32 * 32, Mp = (g.M + 31) / 32 * 32;
+  const int Np = (g.N + 127) / 128 * 128, Mp = (g.M + 31) / 32 * 32;
   {
     const int64_t n = (int64_t)g.B * g.H * Np;
     hipLaunchKernelGGL((k_bwd_prep_mfma<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, g,
@@ -447,7 +462,7 @@ hipError_t run_bwd_global_mfma(const Geo &g, const BwdArgs &a, const BwdMfmaArgs
     if (hipError_t e = hipGetLastError()) return e;
   }
   {
-    const int ntiles = Np / (kWaves * 32) + (Np % (kWaves * 32) ? 1 : 0);
+    const int ntiles = Np / (kWaves * 32);
     hipLaunchKernelGGL((k_bwd_gq_mfma<D, TS>), dim3((unsigned)(ntiles * g.B * g.H)), dim3(256), 0, s,
                        g, m.qn, m.dn, m.lse_p, m.dl_p, m.tok, static_cast<const bf16 *>(a.ks), m.vk,
                        m.kt, a.dqg, Np, ntiles);
