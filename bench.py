@@ -103,6 +103,106 @@ def cpu_baseline(w, coords, q, k, v, g, target_s=15.0):
                        f"(x batch {w.B}); {dt:.1f} s wall")}
 
 
+def algorithmic_backward(w, es=2):
+    """Algorithmic work of the backward's stages (bytes / flops per launch
+    sequence): what the gradients must read, write or compute once."""
+    B, N, H, D, M = w.B, w.N, w.H, w.D, w.M
+    row, kvrow = H * D * es, w.kv_heads * D * es
+    return {
+        # coords read, slot map written; K, V read and summaries written
+        "geom_summaries": {"bytes": N * 16 + B * N * 2 * kvrow + B * M * 2 * kvrow},
+        # 3 contractions per (token, query head, summary) on the query side
+        # (scores, dO v_sum^T, dT k_sum) and 4 on the summary side (scores,
+        # dO v_sum^T, dT^T q~, P^T dO): 14*D flops per pair
+        "global": {"flops": 14.0 * B * H * N * M * D,
+                   "bytes": B * N * (3 * row + H * 4) + B * M * 2 * kvrow},
+        # Q, dO, O_glob, gate read and dQ, dgate written (query side), K, V
+        # read and dK, dV written (key side), fp32 dq~_glob and the summary
+        # gradients read once
+        "local": {"bytes": B * N * (3 * row + 2 * H * es + 4 * kvrow + H * D * 4)
+                  + B * M * 2 * w.kv_heads * D * 4},
+    }
+
+
+def backward_bench(args, w, dt, es):
+    """fwd+bwd of the operator: pack3d_forward_train then pack3d_backward."""
+    import numpy as np
+    import torch
+
+    import geometry_aware_sparse_amd as gas
+    import pack3d_inputs as pi
+
+    coords = pi.packing_coords(w.grid, w.packing, block=w.block, seed=w.seed("perm"))
+    q, k, v, g = pi.pack_fields(pi.make_fields(w), coords, w.grid)
+    dout = pi.pack_fields((pi.make_dout(w),), coords, w.grid)[0]
+    dev = torch.device("cuda:0")
+    dc = torch.from_numpy(coords).to(dev)
+    dq, dk, dv, dg, ddo = (torch.from_numpy(a).to(dev).to(dt).contiguous()
+                           for a in (q, k, v, g, dout))
+    d = gas.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block, dtype=dt, rope_base=w.rope_base,
+                      summary_centre=args.summary_centre, kv_heads=w.kv_heads)
+    ws = torch.empty(gas.pack3d_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    bws = torch.empty(gas.pack3d_backward_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(dq)
+    saved = torch.empty(gas.pack3d_saved_bytes(d), dtype=torch.uint8, device=dev)
+    grads = (torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv), torch.empty_like(dg))
+    nf, nb = 2 * gas.PACK3D_NUM_STAGES, 2 * gas.PACK3D_NUM_BWD_STAGES
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(nf)] for _ in range(args.steps)]
+    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(nb)] for _ in range(args.steps)]
+    for evs in fev + bev:
+        for e in evs:
+            e.record()
+
+    def step(s=None):
+        gas.pack3d_forward_train(d, dc, dq, dk, dv, dg, out=out, saved=saved, workspace=ws,
+                                 stage_events=None if s is None else fev[s])
+        gas.pack3d_backward(d, dc, dq, dk, dv, dg, saved, ddo, workspace=bws, grads=grads,
+                            stage_events=None if s is None else bev[s])
+
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for s_ in range(args.steps):
+        step(s_)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(stop) / args.steps
+    fstage = {n: float(np.mean([e[2 * i].elapsed_time(e[2 * i + 1]) for e in fev]))
+              for i, n in enumerate(STAGES)}
+    bstage = {n: float(np.mean([e[2 * i].elapsed_time(e[2 * i + 1]) for e in bev]))
+              for i, n in enumerate(("geom_summaries", "global", "local"))}
+    bwork = algorithmic_backward(w, es)
+    gl_s = bstage["global"] * 1e-3
+    achieved = bwork["global"]["flops"] / gl_s / 1e12
+    roofline = {"bound": "mfma", "kernel": "global backward (k_bwd_gq_mfma + k_bwd_gk_mfma)",
+                "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4), "traffic": None}
+    stages = {"fwd_" + n: {"ms": round(v_, 4)} for n, v_ in fstage.items()}
+    for n, v_ in bstage.items():
+        gbs = bwork[n]["bytes"] / (v_ * 1e-3) / 1e9
+        stages["bwd_" + n] = {"ms": round(v_, 4), "algorithmic_bytes": bwork[n]["bytes"],
+                              "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    line = {
+        "metric": "PACK3D fwd+bwd tokens/sec (training forward + backward of the operator), 1 MI355X",
+        "value": round(w.tokens / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "grid_zyx": list(w.grid), "batch": w.B, "heads": w.H,
+                   "kv_heads": w.kv_heads, "head_dim": w.D, "block": list(w.block),
+                   "summaries": w.M, "tokens": w.tokens, "packing": w.packing,
+                   "summary_rope": "centre" if args.summary_centre else "token"},
+        "roofline": roofline, "stages": stages, "wall_s_timed_region": round(wall, 4),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def copy_calibration(nbytes=1 << 30, reps=5):
     """A plain device-to-device copy of known size, for scaling the HBM
     counters (FETCH_SIZE / WRITE_SIZE) of rocprofv3."""
@@ -127,6 +227,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summary-centre", action="store_true",
                     help="summary-centre variant: pool unrotated keys, rotate at the block centre")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the training step (forward that keeps the backward's inputs, "
+                         "then the backward) instead of the inference forward")
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="grouped key/value heads (GQA/MQA) for the workload; 0 keeps H")
     args = ap.parse_args()
@@ -151,6 +254,9 @@ def main():
         w = dataclasses.replace(w, Hkv=args.kv_heads)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     es = 2 if w.dtype == "bf16" else 4
+    if args.backward:
+        backward_bench(args, w, dt, es)
+        return
     coords = pi.packing_coords(w.grid, w.packing, block=w.block, seed=w.seed("perm"))
     q, k, v, g = pi.pack_fields(pi.make_fields(w), coords, w.grid)
     dev = torch.device("cuda:0")
