@@ -307,9 +307,9 @@ BwdLayout bwd_layout(const Geo &g, int dtype) {
   L.qn = L.qt = L.dn = L.dt = L.lse_p = L.dl_p = L.tok = L.vk = L.kt = L.dks_part =
       L.dvs_part = 0;
   if (L.mfma) {
-    // the summary side runs (Mp/128) x B x Hkv workgroups per split: split
-    // the query sites until about 2048 workgroups fill the chip
-    const size_t Np = ((size_t)g.N + 127) / 128 * 128, Mp = ((size_t)g.M + 31) / 32 * 32;
+    // the summary side runs (Mp/128) x B x Hkv workgroups of 4 waves per
+    // split: split the query sites until about 2048 workgroups fill the chip
+    const size_t Np = ((size_t)g.N + 255) / 256 * 256, Mp = ((size_t)g.M + 31) / 32 * 32;
     const size_t wgs = (Mp / 32 + 3) / 4 * g.B * g.Hkv;
     L.nsplit = (int)std::min<size_t>(16, std::max<size_t>(1, (2048 + wgs - 1) / wgs));
     const size_t prow = (size_t)g.B * g.H * Np;

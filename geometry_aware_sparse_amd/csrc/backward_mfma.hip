@@ -37,7 +37,7 @@ namespace pk {
 namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kWaves = 4;
+constexpr int kSiteAlign = 256;  // query sites padded to whole query tiles of every kernel
 
 __device__ __forceinline__ int swap23(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
@@ -45,7 +45,7 @@ __device__ __forceinline__ int swap23(int r) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Position p of (b, h) is grid site p (raster order), p < Np = 128*ceil(N/128):
+// Position p of (b, h) is grid site p (raster order), p < Np = 256*ceil(N/256):
 //   qn [B*H, Np/32, D/8, 32, 8]  q~ s log2(e): row p%32 of 32-row block p/32
 //   qt [B*H, Np/8, D, 8]         the same, channel-major: 8 sites per chunk
 //   dn, dt                       dO_glob, likewise
@@ -130,8 +130,8 @@ __global__ void k_bwd_relayout(int64_t n, int Mp, const bf16 *__restrict__ ks,
 // of TS (NSUB 32-summary sub-tiles) double-buffered in LDS, filled by direct
 // global->LDS loads (16 bytes per lane, offsets computed once): the loads of
 // tile t+1 go out while tile t is used, one barrier per tile.
-template <int D, int TS>
-__global__ __launch_bounds__(256, 2) void k_bwd_gq_mfma(
+template <int D, int TS, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void k_bwd_gq_mfma(
     Geo g, const bf16 *__restrict__ qn, const bf16 *__restrict__ dn,
     const float *__restrict__ lse_p, const float *__restrict__ dl_p,
     const int32_t *__restrict__ tok, const bf16 *__restrict__ ks, const bf16 *__restrict__ vk,
@@ -139,9 +139,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_gq_mfma(
   constexpr int KD = D / 16, NCH = D / 8, DT = (D + 31) / 32, NSUB = TS / 32;
   constexpr int NJ8 = TS / 8;
   // chunks per tile: k_sum and vk rows (NCH x TS), kt (NJ8 x D); whole waves
-  constexpr int NKC = NCH * TS, NTC = NJ8 * D;
+  constexpr int NKC = NCH * TS, NTC = NJ8 * D, NTH = 64 * NW;
   static_assert(NKC % 64 == 0 && NTC % 64 == 0, "tile loads in whole waves");
-  constexpr int RK = (NKC + 255) / 256, RT = (NTC + 255) / 256;
+  constexpr int RK = (NKC + NTH - 1) / NTH, RT = (NTC + NTH - 1) / NTH;
   __shared__ bf16x8 sK0[NKC], sK1[NKC], sV0[NKC], sV1[NKC], sT0[NTC], sT1[NTC];
   const int w = xcd_remap(blockIdx.x, gridDim.x);
   const int tile = w % ntiles, bh = w / ntiles;
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_gq_mfma(
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int Mp = (g.M + 31) / 32 * 32, M32 = Mp / 32;
   const int64_t bk = (int64_t)b * g.Hkv + h / g.G;
-  const int p = tile * (kWaves * 32) + wv * 32 + l32;  // this lane's query site (Np is 128-aligned)
+  const int p = tile * (NW * 32) + wv * 32 + l32;  // this lane's query site (Np is 256-aligned)
   bf16x8 qf[KD], df[KD];
 #pragma unroll
   for (int c = 0; c < KD; c++) {
@@ -171,33 +171,33 @@ __global__ __launch_bounds__(256, 2) void k_bwd_gq_mfma(
   int rk_sub[RK], rk_in[RK], rt_j8[RT], rt_d[RT];
 #pragma unroll
   for (int r = 0; r < RK; r++) {
-    const int e = 256 * r + 64 * wv + lane;
+    const int e = NTH * r + 64 * wv + lane;
     const int ch = e / TS, pos = e % TS;
     rk_sub[r] = pos / 32;
     rk_in[r] = (ch * 32 + swap23(pos % 32)) * 8;
   }
 #pragma unroll
   for (int r = 0; r < RT; r++) {
-    const int e = 256 * r + 64 * wv + lane;
+    const int e = NTH * r + 64 * wv + lane;
     rt_j8[r] = e / D;
     rt_d[r] = e % D;
   }
   auto issue = [&](int tt, bf16x8 *dK, bf16x8 *dV, bf16x8 *dT) {
 #pragma unroll
     for (int r = 0; r < RK; r++) {
-      if (256 * r + 64 * wv < NKC) {  // wave-uniform
+      if (NTH * r + 64 * wv < NKC) {  // wave-uniform
         const int m32 = min(tt * NSUB + rk_sub[r], M32 - 1);
         const int64_t o = (bk * M32 + m32) * (NCH * 256) + rk_in[r];
-        __builtin_amdgcn_global_load_lds(ks + o, (lds_ptr)&dK[256 * r + 64 * wv], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vk + o, (lds_ptr)&dV[256 * r + 64 * wv], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(ks + o, (lds_ptr)&dK[NTH * r + 64 * wv], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vk + o, (lds_ptr)&dV[NTH * r + 64 * wv], 16, 0, 0);
       }
     }
 #pragma unroll
     for (int r = 0; r < RT; r++) {
-      if (256 * r + 64 * wv < NTC) {
+      if (NTH * r + 64 * wv < NTC) {
         const int g8 = min(tt * NJ8 + rt_j8[r], 4 * M32 - 1);
         const int64_t o = ((bk * 4 * M32 + g8) * D + rt_d[r]) * 8;
-        __builtin_amdgcn_global_load_lds(kt + o, (lds_ptr)&dT[256 * r + 64 * wv], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(kt + o, (lds_ptr)&dT[NTH * r + 64 * wv], 16, 0, 0);
       }
     }
   };
@@ -242,14 +242,46 @@ __global__ __launch_bounds__(256, 2) void k_bwd_gq_mfma(
       else issue(tt + 1, sK1, sV1, sT1);
     }
     const bf16x8 *K = odd ? sK1 : sK0, *V = odd ? sV1 : sV0, *T = odd ? sT1 : sT0;
+    if ((tt + 1) * TS <= g.M) {
+      // a whole tile below M: the score products of every sub-tile first, so
+      // that each sub-tile's vector work overlaps the matrix core's work on
+      // the next sub-tile (and on the previous one's accumulation)
+      f32x16 s[NSUB], dp[NSUB];
 #pragma unroll
-    for (int sub = 0; sub < NSUB; sub++) {
-      const int mbase = tt * TS + 32 * sub;
-      if (mbase >= Mp) break;  // uniform: the last tile may be partial
-      if (mbase + 32 <= g.M)
-        sub_step(K, V, T, sub, mbase, std::false_type{});
-      else
-        sub_step(K, V, T, sub, mbase, std::true_type{});
+      for (int sub = 0; sub < NSUB; sub++)
+#pragma unroll
+        for (int c = 0; c < KD; c++) {
+          const bf16x8 kf = K[(2 * c + hi) * TS + 32 * sub + l32];
+          const bf16x8 vf = V[(2 * c + hi) * TS + 32 * sub + l32];
+          s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], c == 0 ? zero16 : s[sub], 0, 0, 0);
+          dp[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[c], c == 0 ? zero16 : dp[sub], 0, 0, 0);
+        }
+#pragma unroll
+      for (int sub = 0; sub < NSUB; sub++) {
+        bf16x8 tf[2];
+#pragma unroll
+        for (int j = 0; j < 16; j++)
+          tf[j >> 3][j & 7] = (bf16)(__builtin_amdgcn_exp2f(s[sub][j] - lq) * (dp[sub][j] - dq));
+#pragma unroll
+        for (int t = 0; t < DT; t++) {
+          const int d = min(32 * t + l32, D - 1);
+#pragma unroll
+          for (int c2 = 0; c2 < 2; c2++) {
+            const bf16x8 kf = T[(4 * sub + 2 * c2 + hi) * D + d];
+            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, tf[c2], acc[t], 0, 0, 0);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int sub = 0; sub < NSUB; sub++) {
+        const int mbase = tt * TS + 32 * sub;
+        if (mbase >= Mp) break;  // uniform: the last tile may be partial
+        if (mbase + 32 <= g.M)
+          sub_step(K, V, T, sub, mbase, std::false_type{});
+        else
+          sub_step(K, V, T, sub, mbase, std::true_type{});
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
     __syncthreads();
@@ -277,16 +309,16 @@ __global__ __launch_bounds__(256, 2) void k_bwd_gq_mfma(
 // of the query sites of every head of the group; query tiles of TQ sites
 // double-buffered in LDS by direct global->LDS loads (Np is a multiple of
 // 128, so every tile is whole). Writes the split's partial sums.
-template <int D, int TQ>
-__global__ __launch_bounds__(256, 2) void k_bwd_gk_mfma(
+template <int D, int TQ, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void k_bwd_gk_mfma(
     Geo g, const bf16 *__restrict__ qn, const bf16 *__restrict__ qt, const bf16 *__restrict__ dn,
     const bf16 *__restrict__ dt, const float *__restrict__ lse_p, const float *__restrict__ dl_p,
     const bf16 *__restrict__ ks, const bf16 *__restrict__ vk, float *dks_part, float *dvs_part,
     int Np, int mtiles, int nsplit) {
   constexpr int KD = D / 16, NCH = D / 8, DT = (D + 31) / 32, NSUB = TQ / 32, NJ8 = TQ / 8;
-  constexpr int NNC = NCH * TQ, NTC = NJ8 * D;  // chunks per tile: row-blocked, transposed
+  constexpr int NNC = NCH * TQ, NTC = NJ8 * D, NTH = 64 * NW;  // chunks per tile
   static_assert(NNC % 64 == 0 && NTC % 64 == 0 && TQ <= 64, "tile loads in whole waves");
-  constexpr int RN = (NNC + 255) / 256, RTT = (NTC + 255) / 256;
+  constexpr int RN = (NNC + NTH - 1) / NTH, RTT = (NTC + NTH - 1) / NTH;
   __shared__ bf16x8 sQ0[NNC], sQ1[NNC], sD0[NNC], sD1[NNC];
   __shared__ bf16x8 sQT0[NTC], sQT1[NTC], sDT0[NTC], sDT1[NTC];
   __shared__ __attribute__((aligned(16))) float sL0[64], sL1[64], sDl0[64], sDl1[64];
@@ -296,8 +328,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_gk_mfma(
   const int lane = threadIdx.x & 63, hi = lane >> 5, l32 = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int Mp = (g.M + 31) / 32 * 32;
-  const int m32 = min(mt * kWaves + wv, Mp / 32 - 1);  // this wave's 32 summaries
-  const bool wave_live = mt * kWaves + wv < Mp / 32;
+  const int m32 = min(mt * NW + wv, Mp / 32 - 1);  // this wave's 32 summaries
+  const bool wave_live = mt * NW + wv < Mp / 32;
   bf16x8 kb[KD], vb[KD];
 #pragma unroll
   for (int c = 0; c < KD; c++) {
@@ -321,14 +353,14 @@ __global__ __launch_bounds__(256, 2) void k_bwd_gk_mfma(
   int rn_sub[RN], rn_in[RN], rt_j8[RTT], rt_d[RTT];
 #pragma unroll
   for (int r = 0; r < RN; r++) {
-    const int e = 256 * r + 64 * wv + lane;
+    const int e = NTH * r + 64 * wv + lane;
     const int ch = e / TQ, pos = e % TQ;
     rn_sub[r] = pos / 32;
     rn_in[r] = (ch * 32 + swap23(pos % 32)) * 8;
   }
 #pragma unroll
   for (int r = 0; r < RTT; r++) {
-    const int e = 256 * r + 64 * wv + lane;
+    const int e = NTH * r + 64 * wv + lane;
     rt_j8[r] = e / D;
     rt_d[r] = e % D;
   }
@@ -338,18 +370,18 @@ __global__ __launch_bounds__(256, 2) void k_bwd_gk_mfma(
     const int64_t bh = (int64_t)b * g.H + h;
 #pragma unroll
     for (int r = 0; r < RN; r++) {
-      if (256 * r + 64 * wv < NNC) {
+      if (NTH * r + 64 * wv < NNC) {
         const int64_t o = (bh * (Np / 32) + qtile * NSUB + rn_sub[r]) * (NCH * 256) + rn_in[r];
-        __builtin_amdgcn_global_load_lds(qn + o, (lds_ptr)&dQ[256 * r + 64 * wv], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(dn + o, (lds_ptr)&dD[256 * r + 64 * wv], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(qn + o, (lds_ptr)&dQ[NTH * r + 64 * wv], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(dn + o, (lds_ptr)&dD[NTH * r + 64 * wv], 16, 0, 0);
       }
     }
 #pragma unroll
     for (int r = 0; r < RTT; r++) {
-      if (256 * r + 64 * wv < NTC) {
+      if (NTH * r + 64 * wv < NTC) {
         const int64_t o = ((bh * (Np / 8) + qtile * NJ8 + rt_j8[r]) * D + rt_d[r]) * 8;
-        __builtin_amdgcn_global_load_lds(qt + o, (lds_ptr)&dQT[256 * r + 64 * wv], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(dt + o, (lds_ptr)&dDT[256 * r + 64 * wv], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(qt + o, (lds_ptr)&dQT[NTH * r + 64 * wv], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(dt + o, (lds_ptr)&dDT[NTH * r + 64 * wv], 16, 0, 0);
       }
     }
     // per-site statistics: wave 0 the log-sum-exp, wave 1 Delta (4 bytes a lane)
@@ -370,17 +402,23 @@ __global__ __launch_bounds__(256, 2) void k_bwd_gk_mfma(
     const bf16x8 *Q = odd ? sQ1 : sQ0, *Dd = odd ? sD1 : sD0;
     const bf16x8 *QT = odd ? sQT1 : sQT0, *DTt = odd ? sDT1 : sDT0;
     const float *L = odd ? sL1 : sL0, *Dl = odd ? sDl1 : sDl0;
+    // the score products of every sub-tile of the tile first, so that each
+    // sub-tile's vector work runs while the matrix core still works on the
+    // next one's products (and on the previous one's accumulation)
+    // C[query rows][summary columns]: row r holds query site swap23(r)
+    f32x16 s[NSUB], dp[NSUB];
 #pragma unroll
     for (int sub = 0; sub < NSUB; sub++) {
-      // C[query rows][summary columns]: row r holds query site swap23(r)
-      f32x16 s, dp;
 #pragma unroll
       for (int c = 0; c < KD; c++) {
         const bf16x8 qa = Q[(2 * c + hi) * TQ + 32 * sub + l32];
         const bf16x8 da = Dd[(2 * c + hi) * TQ + 32 * sub + l32];
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb[c], c == 0 ? zero16 : s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vb[c], c == 0 ? zero16 : dp, 0, 0, 0);
+        s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb[c], c == 0 ? zero16 : s[sub], 0, 0, 0);
+        dp[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vb[c], c == 0 ? zero16 : dp[sub], 0, 0, 0);
       }
+    }
+#pragma unroll
+    for (int sub = 0; sub < NSUB; sub++) {
       // register 8*c2 + e of half hi <-> site 32*sub + 16*c2 + 8*hi + e
       bf16x8 pa[2], ta[2];
 #pragma unroll
@@ -393,9 +431,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_gk_mfma(
 #pragma unroll
         for (int e = 0; e < 8; e++) {
           const float le = e < 4 ? l0[e] : l1[e - 4], de = e < 4 ? d0[e] : d1[e - 4];
-          const float pr = __builtin_amdgcn_exp2f(s[8 * c2 + e] - le);
+          const float pr = __builtin_amdgcn_exp2f(s[sub][8 * c2 + e] - le);
           pa[c2][e] = (bf16)pr;
-          ta[c2][e] = (bf16)(pr * (dp[8 * c2 + e] - de));
+          ta[c2][e] = (bf16)(pr * (dp[sub][8 * c2 + e] - de));
         }
       }
 #pragma unroll
@@ -442,10 +480,10 @@ __global__ void k_bwd_split_sum(int64_t n, int nsplit, const float *__restrict__
 
 // ---------------------------------------------------------------------------
 namespace {
-template <int D, int TS, int TQ>
+template <int D, int TS, int TQ, int NWQ, int NWK>
 hipError_t run_bwd_global_mfma(const Geo &g, const BwdArgs &a, const BwdMfmaArgs &m,
                                hipStream_t s) {
-  const int Np = (g.N + 127) / 128 * 128, Mp = (g.M + 31) / 32 * 32;
+  const int Np = (g.N + kSiteAlign - 1) / kSiteAlign * kSiteAlign, Mp = (g.M + 31) / 32 * 32;
   {
     const int64_t n = (int64_t)g.B * g.H * Np;
     hipLaunchKernelGGL((k_bwd_prep_mfma<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, g,
@@ -462,16 +500,16 @@ hipError_t run_bwd_global_mfma(const Geo &g, const BwdArgs &a, const BwdMfmaArgs
     if (hipError_t e = hipGetLastError()) return e;
   }
   {
-    const int ntiles = Np / (kWaves * 32);
-    hipLaunchKernelGGL((k_bwd_gq_mfma<D, TS>), dim3((unsigned)(ntiles * g.B * g.H)), dim3(256), 0, s,
+    const int ntiles = Np / (NWQ * 32);
+    hipLaunchKernelGGL((k_bwd_gq_mfma<D, TS, NWQ>), dim3((unsigned)(ntiles * g.B * g.H)), dim3(64 * NWQ), 0, s,
                        g, m.qn, m.dn, m.lse_p, m.dl_p, m.tok, static_cast<const bf16 *>(a.ks), m.vk,
                        m.kt, a.dqg, Np, ntiles);
     if (hipError_t e = hipGetLastError()) return e;
   }
   {
-    const int mtiles = (Mp / 32 + kWaves - 1) / kWaves;
-    hipLaunchKernelGGL((k_bwd_gk_mfma<D, TQ>), dim3((unsigned)(m.nsplit * mtiles * g.B * g.Hkv)),
-                       dim3(256), 0, s, g, m.qn, m.qt, m.dn, m.dt, m.lse_p, m.dl_p,
+    const int mtiles = (Mp / 32 + NWK - 1) / NWK;
+    hipLaunchKernelGGL((k_bwd_gk_mfma<D, TQ, NWK>), dim3((unsigned)(m.nsplit * mtiles * g.B * g.Hkv)),
+                       dim3(64 * NWK), 0, s, g, m.qn, m.qt, m.dn, m.dt, m.lse_p, m.dl_p,
                        static_cast<const bf16 *>(a.ks), m.vk, m.dks_part, m.dvs_part, Np, mtiles,
                        m.nsplit);
     if (hipError_t e = hipGetLastError()) return e;
@@ -491,8 +529,8 @@ bool bwd_global_mfma_supported(const Geo &g, int dtype) {
 
 hipError_t launch_bwd_global_mfma(const Geo &g, const BwdArgs &a, const BwdMfmaArgs &m,
                                   hipStream_t s) {
-  if (g.D == 48) return run_bwd_global_mfma<48, 64, 64>(g, a, m, s);
-  return run_bwd_global_mfma<96, 64, 32>(g, a, m, s);
+  if (g.D == 48) return run_bwd_global_mfma<48, 64, 64, 4, 4>(g, a, m, s);
+  return run_bwd_global_mfma<96, 64, 32, 4, 4>(g, a, m, s);
 }
 
 }  // namespace pk

@@ -40,7 +40,7 @@ struct BwdArgs {
   const struct BwdMfmaArgs *mfma;  // null: vector-unit global branch
 };
 // Matrix-core global branch of the backward (bf16, D in {48, 96}, no
-// exclusion): the prepared query operands (Np = 128*ceil(N/128) grid sites),
+// exclusion): the prepared query operands (Np = 256*ceil(N/256) grid sites),
 // the relaid summaries and the split partial sums.
 struct BwdMfmaArgs {
   bf16 *qn, *qt, *dn, *dt;  // [B*H, Np, D] blocked / transposed
