@@ -126,12 +126,14 @@ __global__ void k_bwd_relayout(int64_t n, int Mp, const bf16 *__restrict__ ks,
 }
 
 // ---------------------------------------------------------------------------
-// Query side. Workgroup: 4 waves x 32 query sites of one (b, h); summary tiles
-// of TS (NSUB 32-summary sub-tiles) double-buffered in LDS, filled by direct
+// Query side. Workgroup: NW waves, each owning G groups of 32 query sites of
+// one (b, h) that share every LDS fragment read; summary tiles of TS (NSUB
+// 32-summary sub-tiles) double-buffered in LDS, filled by direct
 // global->LDS loads (16 bytes per lane, offsets computed once): the loads of
-// tile t+1 go out while tile t is used, one barrier per tile.
-template <int D, int TS, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void k_bwd_gq_mfma(
+// tile t+1 go out while tile t is used, one barrier per tile. With G = 2 one
+// group's vector work runs while the matrix core works on the other's.
+template <int D, int TS, int NW, int G>
+__global__ __launch_bounds__(64 * NW, G == 1 ? 2 : 1) void k_bwd_gq_mfma(
     Geo g, const bf16 *__restrict__ qn, const bf16 *__restrict__ dn,
     const float *__restrict__ lse_p, const float *__restrict__ dl_p,
     const int32_t *__restrict__ tok, const bf16 *__restrict__ ks, const bf16 *__restrict__ vk,
@@ -150,20 +152,28 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gq_mfma(
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int Mp = (g.M + 31) / 32 * 32, M32 = Mp / 32;
   const int64_t bk = (int64_t)b * g.Hkv + h / g.G;
-  const int p = tile * (NW * 32) + wv * 32 + l32;  // this lane's query site (Np is 256-aligned)
-  bf16x8 qf[KD], df[KD];
+  // this lane's query site of each group (Np is a multiple of NW * 32 * G)
+  int p[G];
+  bf16x8 qf[G][KD], df[G][KD];
+  float lq[G], dq[G];
+  f32x16 acc[G][DT];
 #pragma unroll
-  for (int c = 0; c < KD; c++) {
-    const int64_t o = ((((int64_t)bh * (Np / 32) + p / 32) * NCH + 2 * c + hi) * 32 + p % 32) * 8;
-    qf[c] = *reinterpret_cast<const bf16x8 *>(qn + o);
-    df[c] = *reinterpret_cast<const bf16x8 *>(dn + o);
+  for (int gi = 0; gi < G; gi++) {
+    p[gi] = tile * (NW * 32 * G) + (wv * G + gi) * 32 + l32;
+#pragma unroll
+    for (int c = 0; c < KD; c++) {
+      const int64_t o =
+          ((((int64_t)bh * (Np / 32) + p[gi] / 32) * NCH + 2 * c + hi) * 32 + p[gi] % 32) * 8;
+      qf[gi][c] = *reinterpret_cast<const bf16x8 *>(qn + o);
+      df[gi][c] = *reinterpret_cast<const bf16x8 *>(dn + o);
+    }
+    lq[gi] = lse_p[(int64_t)bh * Np + p[gi]];
+    dq[gi] = dl_p[(int64_t)bh * Np + p[gi]];
+#pragma unroll
+    for (int t = 0; t < DT; t++)
+#pragma unroll
+      for (int j = 0; j < 16; j++) acc[gi][t][j] = 0.f;
   }
-  const float lq = lse_p[(int64_t)bh * Np + p], dq = dl_p[(int64_t)bh * Np + p];
-  f32x16 acc[DT];
-#pragma unroll
-  for (int t = 0; t < DT; t++)
-#pragma unroll
-    for (int j = 0; j < 16; j++) acc[t][j] = 0.f;
   const f32x16 zero16 = {};
 
   // per-lane parts of the tile offsets: row chunk e = (ch, pos) holds summary
@@ -201,33 +211,40 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gq_mfma(
       }
     }
   };
-  // one 32-summary sub-tile; MASK zeroes the summaries at or past M
+  // one 32-summary sub-tile for every group; MASK zeroes the summaries at or
+  // past M
   auto sub_step = [&](const bf16x8 *K, const bf16x8 *V, const bf16x8 *T, int sub, int mbase,
                       auto mask) {
-    f32x16 s, dp;
+    f32x16 s[G], dp[G];
 #pragma unroll
     for (int c = 0; c < KD; c++) {
       const bf16x8 kf = K[(2 * c + hi) * TS + 32 * sub + l32];
       const bf16x8 vf = V[(2 * c + hi) * TS + 32 * sub + l32];
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], c == 0 ? zero16 : s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[c], c == 0 ? zero16 : dp, 0, 0, 0);
-    }
-    // register j <-> summary mbase + 16*(j/8) + 8*hi + j%8
-    bf16x8 tf[2];
 #pragma unroll
-    for (int j = 0; j < 16; j++) {
-      float t = __builtin_amdgcn_exp2f(s[j] - lq) * (dp[j] - dq);
-      if constexpr (decltype(mask)::value)
-        t = (mbase + 16 * (j >> 3) + 8 * hi + (j & 7) < g.M) ? t : 0.f;
-      tf[j >> 3][j & 7] = (bf16)t;
+      for (int gi = 0; gi < G; gi++) {
+        s[gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[gi][c], c == 0 ? zero16 : s[gi], 0, 0, 0);
+        dp[gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[gi][c], c == 0 ? zero16 : dp[gi], 0, 0, 0);
+      }
     }
 #pragma unroll
-    for (int t = 0; t < DT; t++) {
-      const int d = min(32 * t + l32, D - 1);
+    for (int gi = 0; gi < G; gi++) {
+      // register j <-> summary mbase + 16*(j/8) + 8*hi + j%8
+      bf16x8 tf[2];
 #pragma unroll
-      for (int c2 = 0; c2 < 2; c2++) {
-        const bf16x8 kf = T[(4 * sub + 2 * c2 + hi) * D + d];
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, tf[c2], acc[t], 0, 0, 0);
+      for (int j = 0; j < 16; j++) {
+        float t = __builtin_amdgcn_exp2f(s[gi][j] - lq[gi]) * (dp[gi][j] - dq[gi]);
+        if constexpr (decltype(mask)::value)
+          t = (mbase + 16 * (j >> 3) + 8 * hi + (j & 7) < g.M) ? t : 0.f;
+        tf[j >> 3][j & 7] = (bf16)t;
+      }
+#pragma unroll
+      for (int t = 0; t < DT; t++) {
+        const int d = min(32 * t + l32, D - 1);
+#pragma unroll
+        for (int c2 = 0; c2 < 2; c2++) {
+          const bf16x8 kf2 = T[(4 * sub + 2 * c2 + hi) * D + d];
+          acc[gi][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf2, tf[c2], acc[gi][t], 0, 0, 0);
+        }
       }
     }
   };
@@ -242,7 +259,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gq_mfma(
       else issue(tt + 1, sK1, sV1, sT1);
     }
     const bf16x8 *K = odd ? sK1 : sK0, *V = odd ? sV1 : sV0, *T = odd ? sT1 : sT0;
-    if ((tt + 1) * TS <= g.M) {
+    if ((tt + 1) * TS <= g.M && G == 1) {
       // a whole tile below M: the score products of every sub-tile first, so
       // that each sub-tile's vector work overlaps the matrix core's work on
       // the next sub-tile (and on the previous one's accumulation)
@@ -253,25 +270,29 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gq_mfma(
         for (int c = 0; c < KD; c++) {
           const bf16x8 kf = K[(2 * c + hi) * TS + 32 * sub + l32];
           const bf16x8 vf = V[(2 * c + hi) * TS + 32 * sub + l32];
-          s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], c == 0 ? zero16 : s[sub], 0, 0, 0);
-          dp[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[c], c == 0 ? zero16 : dp[sub], 0, 0, 0);
+          s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0][c], c == 0 ? zero16 : s[sub], 0, 0, 0);
+          dp[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[0][c], c == 0 ? zero16 : dp[sub], 0, 0, 0);
         }
 #pragma unroll
       for (int sub = 0; sub < NSUB; sub++) {
         bf16x8 tf[2];
 #pragma unroll
         for (int j = 0; j < 16; j++)
-          tf[j >> 3][j & 7] = (bf16)(__builtin_amdgcn_exp2f(s[sub][j] - lq) * (dp[sub][j] - dq));
+          tf[j >> 3][j & 7] =
+              (bf16)(__builtin_amdgcn_exp2f(s[sub][j] - lq[0]) * (dp[sub][j] - dq[0]));
 #pragma unroll
         for (int t = 0; t < DT; t++) {
           const int d = min(32 * t + l32, D - 1);
 #pragma unroll
           for (int c2 = 0; c2 < 2; c2++) {
             const bf16x8 kf = T[(4 * sub + 2 * c2 + hi) * D + d];
-            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, tf[c2], acc[t], 0, 0, 0);
+            acc[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, tf[c2], acc[0][t], 0, 0, 0);
           }
         }
       }
+    } else if ((tt + 1) * TS <= g.M) {
+#pragma unroll
+      for (int sub = 0; sub < NSUB; sub++) sub_step(K, V, T, sub, 0, std::false_type{});
     } else {
 #pragma unroll
       for (int sub = 0; sub < NSUB; sub++) {
@@ -287,21 +308,24 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gq_mfma(
     __syncthreads();
   }
   // lane: query site p (column l32), rows d = 32t + 8jj + 4hi + u
-  const int i = p < g.N ? tok[(int64_t)b * Np + p] : -1;
-  if (i < 0) return;
-  float *orow = dqg + (((int64_t)b * g.N + i) * g.H + h) * D;
 #pragma unroll
-  for (int t = 0; t < DT; t++)
+  for (int gi = 0; gi < G; gi++) {
+    const int i = p[gi] < g.N ? tok[(int64_t)b * Np + p[gi]] : -1;
+    if (i < 0) continue;
+    float *orow = dqg + (((int64_t)b * g.N + i) * g.H + h) * D;
 #pragma unroll
-    for (int jj = 0; jj < 4; jj++) {
-      const int d = 32 * t + 8 * jj + 4 * hi;
-      if (d < D) {
-        f32x4 o4;
+    for (int t = 0; t < DT; t++)
 #pragma unroll
-        for (int u = 0; u < 4; u++) o4[u] = g.scale * acc[t][4 * jj + u];
-        *reinterpret_cast<f32x4 *>(orow + d) = o4;
+      for (int jj = 0; jj < 4; jj++) {
+        const int d = 32 * t + 8 * jj + 4 * hi;
+        if (d < D) {
+          f32x4 o4;
+#pragma unroll
+          for (int u = 0; u < 4; u++) o4[u] = g.scale * acc[gi][t][4 * jj + u];
+          *reinterpret_cast<f32x4 *>(orow + d) = o4;
+        }
       }
-    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -480,7 +504,7 @@ __global__ void k_bwd_split_sum(int64_t n, int nsplit, const float *__restrict__
 
 // ---------------------------------------------------------------------------
 namespace {
-template <int D, int TS, int TQ, int NWQ, int NWK>
+template <int D, int TS, int TQ, int NWQ, int GQ, int NWK>
 hipError_t run_bwd_global_mfma(const Geo &g, const BwdArgs &a, const BwdMfmaArgs &m,
                                hipStream_t s) {
   const int Np = (g.N + kSiteAlign - 1) / kSiteAlign * kSiteAlign, Mp = (g.M + 31) / 32 * 32;
@@ -500,8 +524,8 @@ hipError_t run_bwd_global_mfma(const Geo &g, const BwdArgs &a, const BwdMfmaArgs
     if (hipError_t e = hipGetLastError()) return e;
   }
   {
-    const int ntiles = Np / (NWQ * 32);
-    hipLaunchKernelGGL((k_bwd_gq_mfma<D, TS, NWQ>), dim3((unsigned)(ntiles * g.B * g.H)), dim3(64 * NWQ), 0, s,
+    const int ntiles = Np / (NWQ * 32 * GQ);
+    hipLaunchKernelGGL((k_bwd_gq_mfma<D, TS, NWQ, GQ>), dim3((unsigned)(ntiles * g.B * g.H)), dim3(64 * NWQ), 0, s,
                        g, m.qn, m.dn, m.lse_p, m.dl_p, m.tok, static_cast<const bf16 *>(a.ks), m.vk,
                        m.kt, a.dqg, Np, ntiles);
     if (hipError_t e = hipGetLastError()) return e;
@@ -529,8 +553,8 @@ bool bwd_global_mfma_supported(const Geo &g, int dtype) {
 
 hipError_t launch_bwd_global_mfma(const Geo &g, const BwdArgs &a, const BwdMfmaArgs &m,
                                   hipStream_t s) {
-  if (g.D == 48) return run_bwd_global_mfma<48, 64, 64, 4, 4>(g, a, m, s);
-  return run_bwd_global_mfma<96, 64, 32, 4, 4>(g, a, m, s);
+  if (g.D == 48) return run_bwd_global_mfma<48, 64, 64, 4, 1, 4>(g, a, m, s);
+  return run_bwd_global_mfma<96, 64, 32, 4, 1, 4>(g, a, m, s);
 }
 
 }  // namespace pk
