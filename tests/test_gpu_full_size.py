@@ -89,3 +89,46 @@ MILLION = pi.workload(6)
 def test_million_tokens_sampled_rows_and_repack():
     test_full_size_sampled_rows(MILLION)
     test_full_size_repack_bitwise(MILLION)
+
+
+BWD_FULL = [pi.workload(3), pi.workload(5)]
+
+
+def _train_step(w, packing):
+    import geometry_aware_sparse_amd as gas
+    coords, q, k, v, g = inputs(w, packing=packing)
+    dout = pi.pack_fields((pi.make_dout(w),), coords, w.grid)[0]
+    d, _ = desc_pair(w)
+    dt = tdtype(w)
+    dev = [to_dev(coords, torch.int32)] + [to_dev(x, dt) for x in (q, k, v, g)]
+    ws = torch.empty(gas.pack3d_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    bws = torch.empty(gas.pack3d_backward_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    o, saved = gas.pack3d_forward_train(d, *dev, workspace=ws)
+    ddo = to_dev(dout, dt)
+    grads = gas.pack3d_backward(d, *dev, saved, ddo, workspace=bws)
+    again = gas.pack3d_backward(d, *dev, saved, ddo, workspace=bws)
+    return coords, ddo, grads, again
+
+
+@pytest.mark.parametrize("w", BWD_FULL, ids=[w.name for w in BWD_FULL])
+def test_full_size_backward_repack_determinism_and_value_conservation(w):
+    """The backward at full size, in the configuration bench.py --backward
+    times: every gradient permutes bit for bit under a repack, a second call
+    gives the same bits, and the value gradients conserve the output
+    gradient (every softmax row sums to one in both branches, and the pooling
+    hands each summary's gradient back to its members over their count):
+    sum_j dv_j = sum over the KV head's query heads of sum_i dO_i."""
+    ca, dout, ga, again = _train_step(w, w.packing)
+    for x, y in zip(ga, again):
+        assert torch.equal(x, y)
+        assert torch.isfinite(x.float()).all()
+    cb, _, gb, _ = _train_step(w, w.repack)
+    p = torch.from_numpy(pi.order_between(ca, cb, w.grid)).to("cuda")
+    for x, y in zip(ga, gb):
+        assert torch.equal(x, y[:, p])
+    G = w.H // w.kv_heads
+    dv = ga[2].double()
+    lhs = dv.sum(dim=1)                                             # [B, Hkv, D]
+    rhs = dout.double().view(w.B, w.N, w.kv_heads, G, w.D).sum(dim=(1, 3))
+    mass = dv.abs().sum(dim=1)
+    assert ((lhs - rhs).abs() <= 1e-2 * mass).all()
