@@ -140,8 +140,9 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_bwd_local_q_pair(
   const int qs = ((tz + 1) * HY + (ty + 1)) * HX + (tx + 1);
   const int i = sSlot[qs];
   const int wbase = __builtin_amdgcn_readfirstlane(threadIdx.x & ~63);
-  // all global loads first: raw K chunks, V straight to LDS, this lane's q,
-  // dO, O_glob, dq~_glob slices and the gate
+  // global loads first: raw K chunks, V straight to LDS, this lane's q and dO
+  // slices and the gate (O_glob and dq~_glob, needed only at the end, are
+  // loaded after the neighbour loop so they hold no registers through it)
   bf16x8 kraw[RS];
 #pragma unroll
   for (int r = 0; r < RS; r++) {
@@ -153,16 +154,12 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_bwd_local_q_pair(
   }
   const int64_t row = (bN + max(i, 0)) * g.H + h;
   const int64_t off = row * D + hh * DH;
-  bf16x8 qraw[DH / 8], draw[DH / 8], oraw[DH / 8];
-  f32x4 gq[DH / 4];
+  bf16x8 qraw[DH / 8], draw[DH / 8];
 #pragma unroll
   for (int c8 = 0; c8 < DH / 8; c8++) {
     qraw[c8] = *reinterpret_cast<const bf16x8 *>(q + off + 8 * c8);
     draw[c8] = *reinterpret_cast<const bf16x8 *>(dout + off + 8 * c8);
-    oraw[c8] = *reinterpret_cast<const bf16x8 *>(oglob + off + 8 * c8);
   }
-#pragma unroll
-  for (int c4 = 0; c4 < DH / 4; c4++) gq[c4] = *reinterpret_cast<const f32x4 *>(dqg + off + 4 * c4);
   const float gl = (float)gate[row];
   // rotate the staged keys at their own coordinates, as the forward does
 #pragma unroll
@@ -220,6 +217,9 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_bwd_local_q_pair(
     uu[kk] = lane_sum<LPQ>(a1);
     lg[kk] = sSlot[hs] >= 0 ? a0 : -INFINITY;
     mx = fmaxf(mx, lg[kk]);
+    // a compiler-only fence every three neighbours: the rows of the next
+    // ones are not loaded early, which would hold dozens of registers
+    if (kk % 3 == 2) asm volatile("" ::: "memory");
   }
   float den = 0.f;
 #pragma unroll
@@ -249,8 +249,15 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_bwd_local_q_pair(
     const float w1 = kp < 13 ? lg[k1] * (omg * uu[k1] - delta) : 0.f;
     pair_accumulate<DH>(acc, w0, w1, sK + (qs + halo_offset(k0, HY, HX)) * D + hh * DH,
                         sK + (qs + halo_offset(k1, HY, HX)) * D + hh * DH);
+    asm volatile("" ::: "memory");
   }
   // dq = R^T (s dq~_loc + dq~_glob); dG = g (1 - g) (<dO, O_glob> - <dO, O_loc>)
+  bf16x8 oraw[DH / 8];
+  f32x4 gq[DH / 4];
+#pragma unroll
+  for (int c8 = 0; c8 < DH / 8; c8++) oraw[c8] = *reinterpret_cast<const bf16x8 *>(oglob + off + 8 * c8);
+#pragma unroll
+  for (int c4 = 0; c4 < DH / 4; c4++) gq[c4] = *reinterpret_cast<const f32x4 *>(dqg + off + 4 * c4);
   float dgo = 0.f;
   bf16x8 outv[DH / 8];
 #pragma unroll
@@ -408,6 +415,7 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_bwd_local_kv_pair(
       const float pr = valid ? __builtin_amdgcn_exp2f(a0 - sL[hs]) : 0.f;
       pw[kk] = pr * sOmg[hs];
       dsw[kk] = pr * (sOmg[hs] * a1 - sDl[hs]);
+      if (kk % 3 == 2) asm volatile("" ::: "memory");  // as on the query side
     }
     asm volatile("" ::: "memory");  // the next phase re-reads its rows from LDS
 #pragma unroll
@@ -417,6 +425,7 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_bwd_local_kv_pair(
       const float c1 = kp2 < 13 ? 1.f : 0.f;
       pair_accumulate<DH>(adk, dsw[k0], c1 * dsw[k1], sQ + hs0 * D + hh * DH, sQ + hs1 * D + hh * DH);
       pair_accumulate<DH>(adv, pw[k0], c1 * pw[k1], sO + hs0 * D + hh * DH, sO + hs1 * D + hh * DH);
+      asm volatile("" ::: "memory");
     }
   }
   if (j < 0) return;
