@@ -45,6 +45,11 @@ CASES = [
        "raster"), "token", 2),
     (W(128, "bf16_d48_mha", (8, 12, 16), 2, 4, 48, (2, 2, 2), "bf16", "iid", "block", "random"),
      "token", 0),
+    # 72 summaries: the matrix-core query side's last 64-summary tile is half full
+    (W(129, "bf16_d48_m72_half_tile", (6, 8, 12), 1, 2, 48, (2, 2, 2), "bf16", "iid", "random",
+       "raster"), "token", 0),
+    (W(130, "bf16_d48_single_site", (1, 1, 1), 1, 2, 48, (1, 1, 1), "bf16", "iid", "raster",
+       "raster", Hkv=1), "token", 0),
 ]
 IDS = [f"{w.name}-{sr}" for w, sr, _ in CASES]
 
