@@ -1,5 +1,6 @@
 /*
- * pack3d.h -- C ABI of the PACK3D local-global attention forward on gfx950.
+ * pack3d.h -- C ABI of PACK3D local-global attention on gfx950: the forward
+ * pass, its stages one by one, and the backward pass.
  *
  * The operator (Geometry Matters in Packed 3D Attention; "project page" =
  * the Pack3D site, "paper summary" = the arXiv 2610.38694 abstract page):
@@ -11,7 +12,9 @@
  * coordinate neighbourhood (Contract 1) and to every block summary, built by
  * rotating keys first and mean-pooling them per contiguous 3D block
  * (Contract 2 and "Rotate first, then pool"; paper summary §3.2, §B.5). A
- * tokenwise gate mixes the two branches (paper summary §3.3).
+ * tokenwise gate mixes the two branches (paper summary §3.3). The operator is
+ * trained end to end (paper summary §1, §3.4): pack3d_forward_train and
+ * pack3d_backward give the gradients with respect to q, k, v and the gate.
  *
  * Conventions shared by every entry point
  *  - Pointers named q, k, v, gate, o, x, k_sum, v_sum, geom, coords, ws and
@@ -78,7 +81,7 @@ typedef enum pack3d_status {
   PACK3D_OK = 0,
   PACK3D_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad enum */
   PACK3D_ERR_SHAPE = -2,       /* N != Z*Y*X, D % 6, block < 1, H % kv_heads, overflow */
-  PACK3D_ERR_WORKSPACE = -3,   /* workspace smaller than pack3d_workspace_bytes */
+  PACK3D_ERR_WORKSPACE = -3,   /* workspace or saved buffer smaller than required  */
   PACK3D_ERR_UNSUPPORTED = -4, /* dtype / D / exclusion combination not built */
   PACK3D_ERR_HIP = -5,         /* a HIP launch or runtime call failed */
   PACK3D_ERR_COORDS = -6       /* coordinate off the grid or duplicated (VALIDATE only) */
