@@ -109,3 +109,42 @@ def test_binding_refuses_host_tensors(gas):
     with pytest.raises(ValueError, match="GPU"):
         gas.pack3d_rope_coords(d, torch.zeros((512, 3), dtype=torch.int32),
                                torch.zeros((1, 512, 2, 48), dtype=torch.bfloat16))
+
+
+def test_training_entry_points_check_arguments_on_the_host(gas):
+    # every failure below is decided before anything is enqueued
+    lib = gas.library()
+    d = _desc(gas)
+    fake = C.c_void_p(16)
+    n, sb, bn = C.c_size_t(), C.c_size_t(), C.c_size_t()
+    assert lib.pack3d_workspace_bytes(C.byref(d), C.byref(n)) == 0
+    assert lib.pack3d_saved_bytes(C.byref(d), C.byref(sb)) == 0
+    assert lib.pack3d_backward_workspace_bytes(C.byref(d), C.byref(bn)) == 0
+    # saved = O_glob [B,N,H,D] bf16 then lse [B,N,H] fp32, each 256-aligned
+    rows = 1 * 512 * 2
+    assert sb.value == (rows * 48 * 2 + 255) // 256 * 256 + (rows * 4 + 255) // 256 * 256
+    assert bn.value > n.value
+    # training forward: missing saved buffer, too small a saved buffer
+    assert lib.pack3d_forward_train(C.byref(d), fake, fake, fake, fake, fake, fake, None,
+                                    C.c_size_t(sb.value), fake, C.c_size_t(n.value), None,
+                                    None) == -1
+    assert lib.pack3d_forward_train(C.byref(d), fake, fake, fake, fake, fake, fake, fake,
+                                    C.c_size_t(sb.value - 1), fake, C.c_size_t(n.value), None,
+                                    None) == -3
+    # backward: null gradient pointer, small saved buffer, small workspace, bad descriptor
+    args = [fake] * 6
+    assert lib.pack3d_backward(C.byref(d), *args, C.c_size_t(sb.value), fake, None, fake, fake,
+                               fake, fake, C.c_size_t(bn.value), None, None) == -1
+    assert lib.pack3d_backward(C.byref(d), *args, C.c_size_t(sb.value - 1), fake, fake, fake,
+                               fake, fake, fake, C.c_size_t(bn.value), None, None) == -3
+    assert lib.pack3d_backward(C.byref(d), *args, C.c_size_t(sb.value), fake, fake, fake, fake,
+                               fake, fake, C.c_size_t(bn.value - 1), None, None) == -3
+    bad = _desc(gas, N=500)
+    assert lib.pack3d_backward(C.byref(bad), *args, C.c_size_t(sb.value), fake, fake, fake, fake,
+                               fake, fake, C.c_size_t(bn.value), None, None) == -2
+    # unsupported head dim
+    d18 = _desc(gas, D=18)
+    assert lib.pack3d_backward_workspace_bytes(C.byref(d18), C.byref(bn)) == 0
+    assert lib.pack3d_saved_bytes(C.byref(d18), C.byref(sb)) == 0
+    assert lib.pack3d_backward(C.byref(d18), *args, C.c_size_t(sb.value), fake, fake, fake, fake,
+                               fake, fake, C.c_size_t(bn.value), None, None) == -4
