@@ -13,9 +13,12 @@
 //            (the centre variant routes the key part through R(centre)^T)
 //   RoPE     dx = R(c)^T dx~
 //
-// The kernels here are the generic vector-unit path (every dtype and head
-// dim); every reduction runs in a fixed order, so results are reproducible
-// and a repack of the tokens permutes the gradients bit for bit.
+// The kernels here are the generic vector-unit path (every dtype, head dim
+// and exclusion reading). launch_backward sends bf16 rows of 48 or 96
+// channels to the matrix-core global branch (backward_mfma.hip, without
+// exclusion) and the pair-lane local branch (local_bwd.hip) instead. Every
+// reduction runs in a fixed order, so results are reproducible and a repack
+// of the tokens permutes the gradients bit for bit.
 //
 //   k_bwd_prep       per (token, query head): rotated query, dO_glob = g dO,
 //                    Delta_glob = <dO_glob, O_glob>
@@ -550,36 +553,30 @@ __global__ __launch_bounds__(TZ *TY *TX) void k_bwd_local_kv(
 // ---------------------------------------------------------------------------
 namespace {
 
-template <typename T, int D, int TZ, int TY, int TX>
-hipError_t run_backward_t(const Geo &g, const BwdArgs &a, hipStream_t s) {
+// Global branch on the vector units: prep, query side, summary side.
+template <typename T, int D>
+hipError_t run_global_bwd_valu(const Geo &g, const BwdArgs &a, hipStream_t s) {
   const int64_t rows = (int64_t)g.B * g.N * g.H;
-  if (a.mfma) {
-    if (hipError_t e = launch_bwd_global_mfma(g, a, *a.mfma, s)) return e;
-  } else {
   hipLaunchKernelGGL((k_bwd_prep<T, D>), dim3((unsigned)((rows + kNT - 1) / kNT)), dim3(kNT), 0, s,
                      g, a.geom, a.coords, static_cast<const T *>(a.q), static_cast<const T *>(a.gate),
                      static_cast<const T *>(a.dout), static_cast<const T *>(a.oglob), a.qr, a.dog,
                      a.delta_g);
   if (hipError_t e = hipGetLastError()) return e;
-  {
-    const int ntiles = (g.N + kNT - 1) / kNT;
-    hipLaunchKernelGGL((k_bwd_global_q<T, D>), dim3((unsigned)(ntiles * g.B * g.H)), dim3(kNT), 0, s,
-                       g, a.coords, a.qr, a.dog, a.lse_g, a.delta_g,
-                       static_cast<const T *>(a.ks), static_cast<const T *>(a.vs), a.dqg, ntiles);
-    if (hipError_t e = hipGetLastError()) return e;
-    const int mtiles = (g.M + 63) / 64;
-    hipLaunchKernelGGL((k_bwd_global_kv<D>), dim3((unsigned)(mtiles * g.B * g.Hkv)), dim3(64), 0, s, g,
-                       a.geom, a.qr, a.dog, a.lse_g, a.delta_g, a.ks, a.vs,
-                       (int)(sizeof(T) == 2), a.dks, a.dvs, mtiles);
-    if (hipError_t e = hipGetLastError()) return e;
-  }
-  }
-  if (a.events) {
-    if (hipError_t e = hipEventRecord(static_cast<hipEvent_t>(a.events[3]), s)) return e;
-    if (hipError_t e = hipEventRecord(static_cast<hipEvent_t>(a.events[4]), s)) return e;
-  }
-  if (bwd_local_pair_supported(g, sizeof(T) == 2 ? PACK3D_BF16 : PACK3D_F32))
-    return launch_bwd_local_pair(g, a, s);
+  const int ntiles = (g.N + kNT - 1) / kNT;
+  hipLaunchKernelGGL((k_bwd_global_q<T, D>), dim3((unsigned)(ntiles * g.B * g.H)), dim3(kNT), 0, s,
+                     g, a.coords, a.qr, a.dog, a.lse_g, a.delta_g, static_cast<const T *>(a.ks),
+                     static_cast<const T *>(a.vs), a.dqg, ntiles);
+  if (hipError_t e = hipGetLastError()) return e;
+  const int mtiles = (g.M + 63) / 64;
+  hipLaunchKernelGGL((k_bwd_global_kv<D>), dim3((unsigned)(mtiles * g.B * g.Hkv)), dim3(64), 0, s, g,
+                     a.geom, a.qr, a.dog, a.lse_g, a.delta_g, a.ks, a.vs, (int)(sizeof(T) == 2),
+                     a.dks, a.dvs, mtiles);
+  return hipGetLastError();
+}
+
+// Local branch on the vector units: query side, then key side.
+template <typename T, int D, int TZ, int TY, int TX>
+hipError_t run_local_bwd_valu(const Geo &g, const BwdArgs &a, hipStream_t s) {
   const int ntz = (g.Z + TZ - 1) / TZ, nty = (g.Y + TY - 1) / TY, ntx = (g.X + TX - 1) / TX;
   hipLaunchKernelGGL((k_bwd_local_q<T, D, TZ, TY, TX>), dim3((unsigned)(g.B * ntz * nty * ntx * g.H)),
                      dim3(TZ * TY * TX), 0, s, g, a.geom, static_cast<const T *>(a.q),
@@ -596,6 +593,23 @@ hipError_t run_backward_t(const Geo &g, const BwdArgs &a, hipStream_t s) {
                      static_cast<const T *>(a.dout), a.lse_l, a.delta_l, a.dks, a.dvs,
                      static_cast<T *>(a.dk), static_cast<T *>(a.dv), ntz, nty, ntx);
   return hipGetLastError();
+}
+
+// The whole backward after the geometry and the summaries: global branch
+// (matrix cores when prepared for, else vector units), then local branch
+// (pair lanes for bf16 rows of 48 or 96 channels, else vector units).
+template <typename T, int D, int TZ, int TY, int TX>
+hipError_t run_backward_t(const Geo &g, const BwdArgs &a, hipStream_t s) {
+  if (hipError_t e = a.mfma ? launch_bwd_global_mfma(g, a, *a.mfma, s)
+                            : run_global_bwd_valu<T, D>(g, a, s))
+    return e;
+  if (a.events) {
+    if (hipError_t e = hipEventRecord(static_cast<hipEvent_t>(a.events[3]), s)) return e;
+    if (hipError_t e = hipEventRecord(static_cast<hipEvent_t>(a.events[4]), s)) return e;
+  }
+  if (bwd_local_pair_supported(g, sizeof(T) == 2 ? PACK3D_BF16 : PACK3D_F32))
+    return launch_bwd_local_pair(g, a, s);
+  return run_local_bwd_valu<T, D, TZ, TY, TX>(g, a, s);
 }
 
 }  // namespace
