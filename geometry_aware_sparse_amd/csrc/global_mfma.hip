@@ -52,31 +52,40 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = 4;
 
-// 16 bytes of bf16 ones: the source of the value-tile row that makes the
-// matrix core return the softmax denominator. Read-only.
-__device__ __attribute__((aligned(16))) uint32_t g_ones[4] = {0x3F803F80u, 0x3F803F80u,
-                                                                 0x3F803F80u, 0x3F803F80u};
+// Word 3 of a raw buffer resource (32-bit data format, no swizzle): the
+// tile loads are buffer loads into LDS rather than flat ones. With a flat
+// LDS load in flight the compiler waits for every outstanding LDS read
+// before any use of one; with buffer loads it counts them in order, which
+// is what lets the fragment reads run a step ahead.
+constexpr int kBufWord3 = 0x00020000;
 
 __device__ __forceinline__ int swap23(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
-// Scheduling hint for one pipeline step: the LDS fragment reads first, a
-// few vector instructions while they land, then one matrix instruction
-// followed by PER vector instructions (exp2 and bf16 packs), so that a wave
-// keeps issuing vector work while its own products run (a wave issues in
-// order; a run of matrix instructions would otherwise stall it on the busy
-// matrix pipe).
-template <int NDS, int NMF, int NVA>
+// Scheduling hint for one pipeline step: a few vector instructions, then
+// the score products, each matrix instruction followed by PER vector
+// instructions (exp2 and bf16 packs), then the LDS reads of the next step's
+// key fragments, the value products interleaved the same way, and last the
+// reads of the next step's value fragments. A wave issues in order: the
+// vector work keeps it busy while its own products run, and every fragment
+// is read one product group ahead of its use, so no product waits on LDS.
+template <int NK, int NV, int NMK, int NMV, int NVA>
 __device__ __forceinline__ void sched_step() {
-  constexpr int PER = NVA / NMF, LEAD = NVA - NMF * PER;
-  __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+  constexpr int NMF = NMK + NMV, PER = NVA / NMF, LEAD = NVA - NMF * PER;
   if constexpr (LEAD > 0) __builtin_amdgcn_sched_group_barrier(0x002, LEAD, 0);
 #pragma unroll
-  for (int i = 0; i < NMF; i++) {
+  for (int i = 0; i < NMK; i++) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);
   }
+  __builtin_amdgcn_sched_group_barrier(0x100, NK, 0);
+#pragma unroll
+  for (int i = 0; i < NMV; i++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, NV, 0);
 }
 }  // namespace
 
@@ -119,6 +128,11 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
   const int64_t bk = (int64_t)b * g.Hkv + h / g.G;         // the KV head query head h reads
   const int64_t kbase = bk * M32;                          // k_sum [B,Hkv,M32,D/8,32,8]
   const int64_t vbase = bk * M32 * 4;                      // v_sum [B,Hkv,Mp/8,D,8]
+  // this KV head's summaries as two buffers (byte sizes checked on the host)
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16 *>(ks + kbase * NCH * 256), 0, M32 * NCH * 512, kBufWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16 *>(vsb + vbase * D * 8), 0, M32 * 4 * D * 16, kBufWord3);
 
   // Query fragments: lane holds channels 16c + 8*hi .. +7 of its query,
   // rotated at the token's own coordinate, scaled, rounded to bf16. A token
@@ -180,17 +194,24 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
   }
   const f32x16 zero16 = {};
 
-  // S^T = Ksum * Q~^T for the 32 summaries at row offset 32*pos of a k_sum tile
-  auto scores_from = [&](const bf16x8 *K, int pos, f32x16 *s) {
-    bf16x8 kf[KD];
+  // k_sum fragments of the 32 summaries at row offset 32*pos of a k_sum tile
+  auto read_k = [&](const bf16x8 *K, int pos, bf16x8 *kf) {
 #pragma unroll
     for (int c = 0; c < KD; c++) kf[c] = K[(2 * c + hi) * TS + 32 * pos + l32];
+  };
+  // S^T = Ksum * Q~^T from k_sum fragments
+  auto scores_of = [&](const bf16x8 *kf, f32x16 *s) {
 #pragma unroll
     for (int c = 0; c < KD; c++)
 #pragma unroll
       for (int gi = 0; gi < G; gi++)
         s[gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c], qf[gi][c], c == 0 ? zero16 : s[gi], 0,
                                                         0, 0);
+  };
+  auto scores_from = [&](const bf16x8 *K, int pos, f32x16 *s) {
+    bf16x8 kf[KD];
+    read_k(K, pos, kf);
+    scores_of(kf, s);
   };
 
   // Scores of summaries at or past M take no part (-inf); a select, so
@@ -239,12 +260,15 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
     // staging registers), double-buffered: key tile k in buffer k&1, value
     // tile v in buffer (v+1)&1. A key tile holds the NSUB
     // sub-tiles [NSUB*k, NSUB*k + NSUB); a value tile is shifted two
-    // sub-tiles back, [NSUB*v - 2, NSUB*v + NSUB - 2), so that both switch
-    // tiles at the same step: the step j with (j + 2) % NSUB == 0 first reads
-    // key tile (j+2)/NSUB and value tile (j+2)/NSUB. One barrier at that
-    // step makes both visible, and at that point no wave reads the key and
-    // value tiles before them any more, so the loads of the following tiles
-    // go into those buffers right after it (NSUB steps ahead of their use).
+    // sub-tiles back, [NSUB*v - 2, NSUB*v + NSUB - 2). Fragments are read
+    // from LDS one step ahead of their products: step j reads the key
+    // fragments of sub-tile j+3 and the value fragments of sub-tile j+1, so
+    // both switch tiles at the same step: the step j with
+    // (j + 3) % NSUB == 0 first reads key tile (j+3)/NSUB and value tile
+    // (j+3)/NSUB. One barrier at the start of that step makes both visible,
+    // and by then no wave reads the key and value tiles before them any
+    // more, so the loads of the following tiles go into those buffers right
+    // after it (NSUB steps ahead of their use).
     const int S = (g.M + 31) / 32;                 // sub-tiles with summaries
     const int IT = (S + 2 * NSUB - 1) / (2 * NSUB);  // iterations of 2*NSUB steps
     // Every lane of every load is active, so the loads need no branches:
@@ -260,22 +284,17 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
         const int i = wv + kWaves * r;
         const int ch = i / KPARTS, part = i % KPARTS;
         const int g32 = min(kt * NSUB + 2 * part + hi, M32 - 1);
-        __builtin_amdgcn_global_load_lds(ks + (((kbase + g32) * NCH + ch) * 32 + swap23(l32)) * 8,
-                                         (lds_ptr)&dK[ch * TS + part * 64], 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rk, (lds_ptr)&dK[ch * TS + part * 64], 16,
+            (uint32_t)(((g32 * NCH + ch) * 32 + swap23(l32)) * 16), 0, 0, 0);
       }
     };
     // v_sum tile vt: LDS chunk (j8, d) = channel d of summaries 8*j8.. of the
-    // tile. Row D is all ones when it carries the denominator (from a 16-byte
-    // constant); the other rows past D repeat channel D-1 and only feed
-    // output rows that are dropped.
-    // The lane that loads row D takes the ones instead; the choice is a bit
-    // mask built once and kept opaque to the compiler, which would otherwise
-    // turn it into a branch around the loads.
+    // tile. Rows past D-1 repeat channel D-1 and only feed output rows that
+    // are dropped -- except row D when it carries the denominator: once a
+    // wave's loads have landed it overwrites row D of the groups it loaded
+    // with bf16 ones, before the barrier that publishes the tile.
     static_assert(!ONES || VPARTS == 1, "the denominator row is in the first part");
-    uint32_t keep = (ONES && lane == D) ? 0u : ~0u;
-    asm volatile("" : "+v"(keep));
-    const uint64_t keep64 = ((uint64_t)keep << 32) | keep;
-    const uint64_t ones_bits = reinterpret_cast<uint64_t>(g_ones) & ~keep64;
     auto issue_v = [&](int vt, bf16x8 *dV) {
       const int g8base = 4 * (vt * NSUB - 2);
 #pragma unroll
@@ -284,22 +303,41 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
         const int j8 = i / VPARTS, part = i % VPARTS;
         const int d = part * 64 + lane;
         const int g8 = min(max(g8base + j8, 0), 4 * M32 - 1);
-        const bf16 *src = vsb + ((vbase + g8) * D + min(d, D - 1)) * 8;
-        if constexpr (ONES)
-          src = reinterpret_cast<const bf16 *>((reinterpret_cast<uint64_t>(src) & keep64) | ones_bits);
-        __builtin_amdgcn_global_load_lds(src, (lds_ptr)&dV[j8 * VROWS + part * 64], 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)&dV[j8 * VROWS + part * 64], 16,
+                                                 (uint32_t)((g8 * D + min(d, D - 1)) * 16), 0, 0,
+                                                 0);
+      }
+    };
+    // after this wave's loads landed: row D of its groups j8 = wv + kWaves*r
+    // (every lane writes; lanes that share a group write the same value)
+    auto ones_rows = [&](bf16x8 *dV) {
+      if constexpr (ONES) {
+        bf16x8 one8;
+#pragma unroll
+        for (int e = 0; e < 8; e++) one8[e] = (bf16)1.0f;
+        dV[(wv + kWaves * (lane % (NVI / kWaves))) * VROWS + D] = one8;
       }
     };
 
     issue_k(0, sK0);
     issue_v(0, sV1);  // sub-tiles -2 .. NSUB-3 (only 0, 1 exist for NSUB = 4)
     __builtin_amdgcn_s_waitcnt(0);
+    ones_rows(sV1);
     __syncthreads();
     issue_k(1, sK1);
     issue_v(1, sV0);
 
     f32x16 s[2][G];        // scores of sub-tiles j+1, j+2 (by parity)
     bf16x8 pf[2][G][2];    // probabilities of sub-tiles j, j+1 (by parity)
+    bf16x8 kf[KD];         // key fragments of sub-tile j+2
+    bf16x8 vf[DT][2];      // value fragments of sub-tile j
+    // value fragments of sub-tile j at position pos of a value tile
+    auto read_v = [&](const bf16x8 *V, int pos) {
+#pragma unroll
+      for (int t = 0; t < DT; t++)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; c2++) vf[t][c2] = V[(4 * pos + 2 * c2 + hi) * VROWS + 32 * t + l32];
+    };
     scores_from(sK0, 0, s[0]);
     mask_tail(s[0], 0);
     scores_from(sK0, 1, s[1]);
@@ -308,32 +346,44 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
 #pragma unroll
       for (int j = 0; j < 16; j++) pf[0][gi][j >> 3][j & 7] = (bf16)__builtin_amdgcn_exp2f(s[0][gi][j]);
     if constexpr (!ONES) sum_bf16(pf[0], lsum);
+    // The prologue is step -1: it reads key sub-tile 2 and value sub-tile 0,
+    // both in tile 2/NSUB. With two sub-tiles per tile that is tile 1, so
+    // this is a tile-switch step like the ones in the loop.
+    if constexpr (NSUB == 2) {
+      __builtin_amdgcn_s_waitcnt(0);
+      ones_rows(sV0);
+      __syncthreads();
+      issue_k(2, sK0);
+      issue_v(2, sV1);
+      read_k(sK1, 0, kf);
+      read_v(sV0, 0);
+    } else {
+      read_k(sK0, 2, kf);  // key tile 0
+      read_v(sV1, 2);      // value tile 0, which starts at sub-tile -2
+    }
 
     // one step; JJ = position in the 2*NSUB-step iteration (compile time)
     auto step = [&](int it, auto jc, auto mc) {
       constexpr int JJ = decltype(jc)::value;
       constexpr bool MASK = decltype(mc)::value;  // some summary of sub-tile j+1 may be past M
-      constexpr int KT = (JJ + 2) / NSUB;  // key tile of sub-tile j+2, from 2*it
+      constexpr int KT = (JJ + 3) / NSUB;  // key tile of sub-tile j+3, from 2*it
       constexpr int KB = KT & 1;
-      constexpr int VB = (KT + 1) & 1;     // value tile of sub-tile j: 2*it + KT
-      constexpr int POS = (JJ + 2) % NSUB;
+      constexpr int VB = (KT + 1) & 1;     // value tile of sub-tile j+1: 2*it + KT
+      constexpr int POS = (JJ + 3) % NSUB;
       constexpr int P = JJ & 1;
-      const bf16x8 *cK = KB ? sK1 : sK0;
-      const bf16x8 *cV = VB ? sV1 : sV0;
+      const bf16x8 *nK = KB ? sK1 : sK0;
+      bf16x8 *nV = VB ? sV1 : sV0;
       const int j = 2 * NSUB * it + JJ;
       if constexpr (POS == 0) {
         __builtin_amdgcn_s_waitcnt(0);  // this wave's loads landed, LDS reads done
+        ones_rows(nV);
         __syncthreads();
         issue_k(2 * it + KT + 1, KB ? sK0 : sK1);
         issue_v(2 * it + KT + 1, KB ? sV1 : sV0);
       }
       if constexpr (MASK) mask_tail(s[P ^ 1], 32 * (j + 1));
-      bf16x8 vf[DT][2];
-#pragma unroll
-      for (int t = 0; t < DT; t++)
-#pragma unroll
-        for (int c2 = 0; c2 < 2; c2++) vf[t][c2] = cV[(4 * POS + 2 * c2 + hi) * VROWS + 32 * t + l32];
-      scores_from(cK, POS, s[P]);
+      scores_of(kf, s[P]);  // sub-tile j+2
+      read_k(nK, POS, kf);  // sub-tile j+3, for the next step
 #pragma unroll
       for (int gi = 0; gi < G; gi++)
 #pragma unroll
@@ -348,7 +398,8 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
           for (int c2 = 0; c2 < 2; c2++)
             acc[gi][t] =
                 __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t][c2], pf[P][gi][c2], acc[gi][t], 0, 0, 0);
-      sched_step<KD + 2 * DT, G * (KD + 2 * DT), G * (ONES ? 24 : 32)>();
+      read_v(nV, POS);  // sub-tile j+1, for the next step
+      sched_step<KD, 2 * DT, G * KD, G * 2 * DT, G * (ONES ? 24 : 32)>();
     };
     // Iterations before IT_CLEAN only see sub-tiles that lie wholly below M,
     // so their steps carry no mask (and no branch that would split a step's
@@ -537,7 +588,10 @@ hipError_t run_global_mfma(const Geo &g, const void *geom, const int32_t *coords
 hipError_t launch_global(const Geo &g, int dtype, const void *geom, const int32_t *coords,
                          const void *q, const void *ks, const void *vs, void *out, float *lse,
                          hipStream_t s, bool *supported) {
-  if (dtype == PACK3D_BF16 && g.excl == PACK3D_EXCL_NONE) {
+  // the matrix-core path addresses one KV head's summaries with 32-bit byte
+  // offsets
+  const int64_t head_bytes = (int64_t)((g.M + 31) / 32) * 32 * g.D * 2;
+  if (dtype == PACK3D_BF16 && g.excl == PACK3D_EXCL_NONE && head_bytes <= INT32_MAX) {
     *supported = true;
     if (g.D == 48) return run_global_mfma<48, 2, 128>(g, geom, coords, q, ks, vs, out, lse, s);
     if (g.D == 96) return run_global_mfma<96, 1, 64>(g, geom, coords, q, ks, vs, out, lse, s);
