@@ -192,22 +192,26 @@ __global__ __launch_bounds__(64 * NW, G == 1 ? 2 : 1) void k_bwd_gq_mfma(
     rt_j8[r] = e / D;
     rt_d[r] = e % D;
   }
+  // this KV head's k_sum, V-in-key-layout and K-in-value-layout slices
+  const __amdgpu_buffer_rsrc_t rks = buffer_rsrc(ks + bk * M32 * (NCH * 256), M32 * NCH * 512);
+  const __amdgpu_buffer_rsrc_t rvk = buffer_rsrc(vk + bk * M32 * (NCH * 256), M32 * NCH * 512);
+  const __amdgpu_buffer_rsrc_t rkt = buffer_rsrc(kt + bk * 4 * M32 * D * 8, 4 * M32 * D * 16);
   auto issue = [&](int tt, bf16x8 *dK, bf16x8 *dV, bf16x8 *dT) {
 #pragma unroll
     for (int r = 0; r < RK; r++) {
       if (NTH * r + 64 * wv < NKC) {  // wave-uniform
         const int m32 = min(tt * NSUB + rk_sub[r], M32 - 1);
-        const int64_t o = (bk * M32 + m32) * (NCH * 256) + rk_in[r];
-        __builtin_amdgcn_global_load_lds(ks + o, (lds_ptr)&dK[NTH * r + 64 * wv], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vk + o, (lds_ptr)&dV[NTH * r + 64 * wv], 16, 0, 0);
+        const uint32_t o = (uint32_t)(m32 * (NCH * 256) + rk_in[r]) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, (lds_ptr)&dK[NTH * r + 64 * wv], 16, o, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rvk, (lds_ptr)&dV[NTH * r + 64 * wv], 16, o, 0, 0, 0);
       }
     }
 #pragma unroll
     for (int r = 0; r < RT; r++) {
       if (NTH * r + 64 * wv < NTC) {
         const int g8 = min(tt * NJ8 + rt_j8[r], 4 * M32 - 1);
-        const int64_t o = ((bk * 4 * M32 + g8) * D + rt_d[r]) * 8;
-        __builtin_amdgcn_global_load_lds(kt + o, (lds_ptr)&dT[NTH * r + 64 * wv], 16, 0, 0);
+        const uint32_t o = (uint32_t)(g8 * D + rt_d[r]) * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rkt, (lds_ptr)&dT[NTH * r + 64 * wv], 16, o, 0, 0, 0);
       }
     }
   };
@@ -392,26 +396,33 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gk_mfma(
                    float *dDl) {
     const int h = hk * g.G + it / nq, qtile = qt0 + it % nq;
     const int64_t bh = (int64_t)b * g.H + h;
+    // this head's slices: both query layouts are Np * D elements per head
+    const int32_t bytes = Np * D * 2;
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(qn + bh * Np * D, bytes);
+    const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(dn + bh * Np * D, bytes);
+    const __amdgpu_buffer_rsrc_t rqt = buffer_rsrc(qt + bh * Np * D, bytes);
+    const __amdgpu_buffer_rsrc_t rdt = buffer_rsrc(dt + bh * Np * D, bytes);
 #pragma unroll
     for (int r = 0; r < RN; r++) {
       if (NTH * r + 64 * wv < NNC) {
-        const int64_t o = (bh * (Np / 32) + qtile * NSUB + rn_sub[r]) * (NCH * 256) + rn_in[r];
-        __builtin_amdgcn_global_load_lds(qn + o, (lds_ptr)&dQ[NTH * r + 64 * wv], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(dn + o, (lds_ptr)&dD[NTH * r + 64 * wv], 16, 0, 0);
+        const uint32_t o = (uint32_t)((qtile * NSUB + rn_sub[r]) * (NCH * 256) + rn_in[r]) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_ptr)&dQ[NTH * r + 64 * wv], 16, o, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_ptr)&dD[NTH * r + 64 * wv], 16, o, 0, 0, 0);
       }
     }
 #pragma unroll
     for (int r = 0; r < RTT; r++) {
       if (NTH * r + 64 * wv < NTC) {
-        const int64_t o = ((bh * (Np / 8) + qtile * NJ8 + rt_j8[r]) * D + rt_d[r]) * 8;
-        __builtin_amdgcn_global_load_lds(qt + o, (lds_ptr)&dQT[NTH * r + 64 * wv], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(dt + o, (lds_ptr)&dDT[NTH * r + 64 * wv], 16, 0, 0);
+        const uint32_t o = (uint32_t)((qtile * NJ8 + rt_j8[r]) * D + rt_d[r]) * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rqt, (lds_ptr)&dQT[NTH * r + 64 * wv], 16, o, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rdt, (lds_ptr)&dDT[NTH * r + 64 * wv], 16, o, 0, 0, 0);
       }
     }
     // per-site statistics: wave 0 the log-sum-exp, wave 1 Delta (4 bytes a lane)
     if (wv < 2) {
-      const float *src = (wv == 0 ? lse_p : dl_p) + bh * Np + qtile * TQ + min(lane, TQ - 1);
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr)(wv == 0 ? dL : dDl), 4, 0, 0);
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc((wv == 0 ? lse_p : dl_p) + bh * Np, Np * 4);
+      const uint32_t o = (uint32_t)(qtile * TQ + min(lane, TQ - 1)) * 4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(wv == 0 ? dL : dDl), 4, o, 0, 0, 0);
     }
   };
   if (ntile > 0) issue(0, sQ0, sD0, sQT0, sDT0, sL0, sDl0);
@@ -548,7 +559,12 @@ hipError_t run_bwd_global_mfma(const Geo &g, const BwdArgs &a, const BwdMfmaArgs
 }  // namespace
 
 bool bwd_global_mfma_supported(const Geo &g, int dtype) {
-  return dtype == PACK3D_BF16 && g.excl == PACK3D_EXCL_NONE && (g.D == 48 || g.D == 96);
+  // one head's query slice and one KV head's summaries are addressed with
+  // 32-bit byte offsets
+  const int64_t Np = ((int64_t)g.N + kSiteAlign - 1) / kSiteAlign * kSiteAlign;
+  const int64_t Mp = ((int64_t)g.M + 31) / 32 * 32;
+  return dtype == PACK3D_BF16 && g.excl == PACK3D_EXCL_NONE && (g.D == 48 || g.D == 96) &&
+         Np * g.D * 2 <= INT32_MAX && Mp * g.D * 2 <= INT32_MAX;
 }
 
 hipError_t launch_bwd_global_mfma(const Geo &g, const BwdArgs &a, const BwdMfmaArgs &m,

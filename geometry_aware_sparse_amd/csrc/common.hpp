@@ -15,6 +15,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // LDS destination of a direct global->LDS load
 typedef __attribute__((address_space(3))) void *lds_ptr;
 
+// Raw buffer resource over [p, p + bytes) (32-bit data format, no swizzle),
+// for buffer loads into LDS. The tiled matrix-core kernels stage through
+// buffer loads rather than flat global->LDS loads: while a flat LDS load is
+// in flight the compiler cannot count LDS reads in order, and waits for all
+// of them before any use of one; with buffer loads it waits for each read
+// alone. Offsets are 32-bit bytes, so callers check that a slice fits.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, 0x00020000);
+}
+
 // Problem geometry, derived once on the host from pack3d_desc and passed to
 // kernels by value.
 struct Geo {

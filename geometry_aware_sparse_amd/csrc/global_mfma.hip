@@ -52,12 +52,6 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = 4;
 
-// Word 3 of a raw buffer resource (32-bit data format, no swizzle): the
-// tile loads are buffer loads into LDS rather than flat ones. With a flat
-// LDS load in flight the compiler waits for every outstanding LDS read
-// before any use of one; with buffer loads it counts them in order, which
-// is what lets the fragment reads run a step ahead.
-constexpr int kBufWord3 = 0x00020000;
 
 __device__ __forceinline__ int swap23(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
@@ -128,11 +122,11 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
   const int64_t bk = (int64_t)b * g.Hkv + h / g.G;         // the KV head query head h reads
   const int64_t kbase = bk * M32;                          // k_sum [B,Hkv,M32,D/8,32,8]
   const int64_t vbase = bk * M32 * 4;                      // v_sum [B,Hkv,Mp/8,D,8]
-  // this KV head's summaries as two buffers (byte sizes checked on the host)
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16 *>(ks + kbase * NCH * 256), 0, M32 * NCH * 512, kBufWord3);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16 *>(vsb + vbase * D * 8), 0, M32 * 4 * D * 16, kBufWord3);
+  // this KV head's summaries as two buffers (byte sizes checked on the
+  // host); buffer loads keep the LDS reads countable in order, which lets
+  // the fragment reads run a step ahead
+  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(ks + kbase * NCH * 256, M32 * NCH * 512);
+  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vsb + vbase * D * 8, M32 * 4 * D * 16);
 
   // Query fragments: lane holds channels 16c + 8*hi .. +7 of its query,
   // rotated at the token's own coordinate, scaled, rounded to bf16. A token
