@@ -217,6 +217,36 @@ def copy_calibration(nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def attainable_peaks(reps=20):
+    """Attainable, not spec, peaks of this GPU: the HBM rate of a plain
+    1 GiB device-to-device copy (read + write bytes over time) and the dense
+    bf16 rate of a large library GEMM (the vendor BLAS on the matrix cores).
+    Context for the roofline fractions, which stay against the spec peaks."""
+    import torch
+    out = {}
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    n = 8192
+    x = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    y = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for name, fn, work in (("hbm_copy", lambda: b.copy_(a), 2.0 * a.numel()),
+                           ("bf16_gemm", lambda: torch.mm(x, y), 2.0 * n * n * n)):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3 / reps
+        out[name] = round(work / sec * 1e-9 if name == "hbm_copy" else work / sec * 1e-12, 1)
+    out["units"] = {"hbm_copy": "GB/s (read + write)", "bf16_gemm": "TFLOP/s (8192^3 torch.mm)"}
+    print(json.dumps({"attainable_peaks": out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,6 +255,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--peaks", action="store_true",
+                    help="measure attainable HBM copy and bf16 GEMM rates on this GPU")
     ap.add_argument("--summary-centre", action="store_true",
                     help="summary-centre variant: pool unrotated keys, rotate at the block centre")
     ap.add_argument("--backward", action="store_true",
@@ -244,6 +276,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.peaks:
+        attainable_peaks()
         return
 
     import geometry_aware_sparse_amd as gas
