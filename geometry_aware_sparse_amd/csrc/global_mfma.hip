@@ -9,8 +9,8 @@
 // Layout of the work. A workgroup of 4 waves owns 64*G*4 consecutive tokens
 // (packed order) of one (batch, head); a wave owns 32*G of them as G groups
 // of 32 that share every LDS fragment read. Summary tiles stream through
-// double-buffered LDS by direct global->LDS loads (16 bytes per lane, no
-// staging registers, no branches), one barrier per tile, the next tile in
+// double-buffered LDS by buffer loads straight into LDS (16 bytes per lane,
+// no staging registers, no branches), one barrier per tile, the next tile in
 // flight while the current one is used. Both tiles are stored chunk-major --
 // a 16-byte chunk is 8 channels of one k_sum row, or one channel of 8
 // consecutive v_sum rows -- laid out so that every fragment read of a
@@ -22,9 +22,10 @@
 // 2 and 3 swapped, which makes the score registers come out exactly in the
 // operand order of the next product O^T += Vsum^T * P^T: probabilities go
 // from registers straight into the matrix core. The sub-tiles run as a
-// three-stage software pipeline -- value products of sub-tile j, exp2 of
-// j+1, score products of j+2 in one step -- so that within a step no matrix
-// instruction waits on a vector one and the two units overlap.
+// three-stage software pipeline -- score products of sub-tile j+2, exp2 of
+// j+1, value products of j in one step -- so that within a step no matrix
+// instruction waits on a vector one and the two units overlap; each step
+// also reads the next step's LDS fragments once its own have been used.
 //
 // Softmax details. Scores are in log2 units (the query is pre-multiplied by
 // scale*log2(e)). Subtracting a running maximum only guards exp against
