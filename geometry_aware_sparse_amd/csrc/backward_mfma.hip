@@ -128,8 +128,8 @@ __global__ void k_bwd_relayout(int64_t n, int Mp, const bf16 *__restrict__ ks,
 // ---------------------------------------------------------------------------
 // Query side. Workgroup: NW waves, each owning G groups of 32 query sites of
 // one (b, h) that share every LDS fragment read; summary tiles of TS (NSUB
-// 32-summary sub-tiles) double-buffered in LDS, filled by direct
-// global->LDS loads (16 bytes per lane, offsets computed once): the loads of
+// 32-summary sub-tiles) double-buffered in LDS, filled by buffer loads
+// straight into LDS (16 bytes per lane, offsets computed once): the loads of
 // tile t+1 go out while tile t is used, one barrier per tile. With G = 2 one
 // group's vector work runs while the matrix core works on the other's.
 template <int D, int TS, int NW, int G>
@@ -335,8 +335,8 @@ __global__ __launch_bounds__(64 * NW, G == 1 ? 2 : 1) void k_bwd_gq_mfma(
 // ---------------------------------------------------------------------------
 // Summary side. Workgroup: 4 waves x 32 summaries of one (b, hk), one split
 // of the query sites of every head of the group; query tiles of TQ sites
-// double-buffered in LDS by direct global->LDS loads (Np is a multiple of
-// 128, so every tile is whole). Writes the split's partial sums.
+// double-buffered in LDS by buffer loads straight into LDS (Np is a multiple
+// of 256, so every tile is whole). Writes the split's partial sums.
 template <int D, int TQ, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gk_mfma(
     Geo g, const bf16 *__restrict__ qn, const bf16 *__restrict__ qt, const bf16 *__restrict__ dn,

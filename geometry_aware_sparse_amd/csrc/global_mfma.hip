@@ -106,8 +106,8 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
   static_assert(D % 16 == 0 && DA % 8 == 0 && (NSUB == 2 || NSUB == 4), "shape");
   static_assert(NKI % kWaves == 0 && NVI % kWaves == 0, "loads split evenly over the waves");
   // Two LDS buffers per operand, as distinct objects: the compiler can then
-  // tell the in-flight global->LDS loads into one buffer from the reads of
-  // the other and does not wait for the loads before every read.
+  // tell the in-flight loads into one buffer from the reads of the other
+  // and does not wait for the loads before every read.
   __shared__ bf16x8 sK0[NCH * TS], sK1[NCH * TS];    // chunk (ch, pos): channels 8ch.., row at pos
   __shared__ bf16x8 sV0[NJ8 * VROWS], sV1[NJ8 * VROWS];  // chunk (j8, d): channel d of rows 8j8..+7
 
@@ -251,8 +251,8 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
     // a step depend on none of its vector instructions, so the two streams
     // interleave freely within one wave.
     //
-    // Summaries reach LDS by direct global->LDS loads (16 bytes per lane, no
-    // staging registers), double-buffered: key tile k in buffer k&1, value
+    // Summaries reach LDS by buffer loads straight into LDS (16 bytes per
+    // lane, no staging registers), double-buffered: key tile k in buffer k&1, value
     // tile v in buffer (v+1)&1. A key tile holds the NSUB
     // sub-tiles [NSUB*k, NSUB*k + NSUB); a value tile is shifted two
     // sub-tiles back, [NSUB*v - 2, NSUB*v + NSUB - 2). Fragments are read
