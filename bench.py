@@ -132,9 +132,12 @@ def backward_bench(args, w, dt, es):
     import geometry_aware_sparse_amd as gas
     import pack3d_inputs as pi
 
+    t_in = time.perf_counter()
     coords = pi.packing_coords(w.grid, w.packing, block=w.block, seed=w.seed("perm"))
     q, k, v, g = pi.pack_fields(pi.make_fields(w), coords, w.grid)
     dout = pi.pack_fields((pi.make_dout(w),), coords, w.grid)[0]
+    print(f"{w.name}: host inputs ready in {time.perf_counter() - t_in:.1f} s", file=sys.stderr,
+          flush=True)
     dev = torch.device("cuda:0")
     dc = torch.from_numpy(coords).to(dev)
     dq, dk, dv, dg, ddo = (torch.from_numpy(a).to(dev).to(dt).contiguous()
@@ -292,8 +295,11 @@ def main():
     if args.backward:
         backward_bench(args, w, dt, es)
         return
+    t_in = time.perf_counter()
     coords = pi.packing_coords(w.grid, w.packing, block=w.block, seed=w.seed("perm"))
     q, k, v, g = pi.pack_fields(pi.make_fields(w), coords, w.grid)
+    print(f"{w.name}: host inputs ready in {time.perf_counter() - t_in:.1f} s", file=sys.stderr,
+          flush=True)
     dev = torch.device("cuda:0")
     dc = torch.from_numpy(coords).to(dev)
     dq, dk, dv, dg = (torch.from_numpy(a).to(dev).to(dt).contiguous() for a in (q, k, v, g))

@@ -60,6 +60,9 @@ WORKLOADS = {
     # tokens per 4x8x8 block), and 2^22 tokens at the same block volume
     6: Workload(6, "grid64x128x128_bf16_1m", (64, 128, 128), 1, 8, 48, (4, 8, 8), "bf16", "iid", "block", "random"),
     7: Workload(7, "grid128x128x256_bf16_4m", (128, 128, 256), 1, 8, 48, (4, 8, 8), "bf16", "iid", "block", "random"),
+    # 2^23 tokens, 32,768 summaries per head: a token tensor holds 3.2e9
+    # elements, past 32-bit element offsets
+    8: Workload(8, "grid128x256x256_bf16_8m", (128, 256, 256), 1, 8, 48, (4, 8, 8), "bf16", "iid", "block", "random"),
 }
 
 

@@ -6,17 +6,29 @@ with a separable Gaussian (sigma 2 tokens, radius 8, reflect boundary) along
 z, y and x and standardises each channel, to give peaked attention. bf16
 workloads draw in fp32 and round to bf16 (round to nearest even).
 """
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 
-def round_bf16(a):
-    """Round fp32 values to the nearest bf16 (ties to even); returns fp32."""
+def round_bf16(a, chunk=1 << 26):
+    """Round fp32 values to the nearest bf16 (ties to even); returns fp32.
+
+    Works in uint32 and in chunks, so that multi-GB fields need little extra
+    memory: for every non-NaN pattern u <= 0xFF800000 the sum u + 0x8000
+    cannot wrap, and NaNs are restored explicitly."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)
-    out = r.view(np.float32).copy()
-    nan = np.isnan(a)
-    out[nan] = np.nan
+    out = np.empty_like(a)
+    src = a.reshape(-1).view(np.uint32)
+    dst = out.reshape(-1).view(np.uint32)
+    for s0 in range(0, src.size, chunk):
+        u = src[s0:s0 + chunk]
+        r = u + np.uint32(0x7FFF)
+        r += (u >> np.uint32(16)) & np.uint32(1)
+        r &= np.uint32(0xFFFF0000)
+        nan = ((u & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000))
+        r[nan] = np.uint32(0x7FC00000)
+        dst[s0:s0 + chunk] = r
     return out
 
 
@@ -60,16 +72,21 @@ def make_fields(w, values=None, shape_override=None):
     values = values or w.values
     B, H, D = w.B, w.H, w.D
     N = w.N
-    out = []
-    for name in ("q", "k", "v"):
+
+    def field(name):
+        # each field has its own seeded stream, so the fields can be drawn
+        # concurrently (numpy releases the GIL while filling) with the same
+        # values as one after the other
         rng = np.random.Generator(np.random.PCG64(w.seed(name)))
-        heads = H if name == "q" else w.kv_heads
-        out.append(_draw(rng, (B, N, heads, D), values, w.grid))
-    rng = np.random.Generator(np.random.PCG64(w.seed("g")))
-    out.append(rng.standard_normal((B, N, H), dtype=np.float32))
-    if w.dtype == "bf16":
-        out = [round_bf16(a) for a in out]
-    return tuple(out)
+        if name == "g":
+            a = rng.standard_normal((B, N, H), dtype=np.float32)
+        else:
+            heads = H if name == "q" else w.kv_heads
+            a = _draw(rng, (B, N, heads, D), values, w.grid)
+        return round_bf16(a) if w.dtype == "bf16" else a
+
+    with ThreadPoolExecutor(max_workers=4) as pool:
+        return tuple(pool.map(field, ("q", "k", "v", "g")))
 
 
 def make_dout(w):
