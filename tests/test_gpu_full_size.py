@@ -132,3 +132,76 @@ def test_full_size_backward_repack_determinism_and_value_conservation(w):
     rhs = dout.double().view(w.B, w.N, w.kv_heads, G, w.D).sum(dim=(1, 3))
     mass = dv.abs().sum(dim=1)
     assert ((lhs - rhs).abs() <= 1e-2 * mass).all()
+
+
+def test_2pow23_tokens_repack_equivariance():
+    """2^23 tokens (128x256x256, 8 heads, head dim 48, 32,768 summaries per
+    head): a token tensor holds 3.2e9 elements, past 32-bit element offsets.
+    The forward under two packings (block-contiguous and uniform random) must
+    give the same bits for every token; an offset that wraps would corrupt
+    whichever tokens sit high in memory, and those differ between the two
+    packings. The oracle's cost at this size rules out a direct comparison
+    (the other tests pin the values); inputs are drawn on the GPU, seeded,
+    N(0,1) rounded to bf16, in site order, then gathered into each packing."""
+    import geometry_aware_sparse_amd as gas
+    w = pi.workload(8)
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed("q"))
+    site = [torch.randn((w.B, w.N, w.H, w.D), generator=gen, device=dev).to(torch.bfloat16)
+            for _ in range(3)]
+    site.append(torch.randn((w.B, w.N, w.H), generator=gen, device=dev).to(torch.bfloat16))
+    d = gas.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block, dtype=torch.bfloat16)
+    ws = torch.empty(gas.pack3d_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    outs = []
+    for kind, seed in ((w.packing, w.seed("perm")), (w.repack, w.seed("perm2"))):
+        coords = pi.packing_coords(w.grid, kind, block=w.block, seed=seed)
+        sites = torch.from_numpy(pi.coords_to_sites(coords, w.grid)).to(dev)
+        q, k, v, g = (x.index_select(1, sites) for x in site)
+        out = gas.pack3d_forward(d, torch.from_numpy(coords).to(dev), q, k, v, g, workspace=ws)
+        del q, k, v, g
+        back = torch.empty_like(out)
+        back[:, sites] = out  # row i of this packing is site sites[i]
+        del out
+        outs.append(back)
+    torch.cuda.synchronize()
+    assert torch.isfinite(outs[0]).all()
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_2pow23_tokens_backward_repack_equivariance():
+    """The training step at 2^23 tokens, the same way: every gradient, taken
+    back to site order, has the same bits under both packings (the backward's
+    reductions run in grid-site order, so a repack only permutes them)."""
+    import geometry_aware_sparse_amd as gas
+    w = pi.workload(8)
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed("dout"))
+    site = [torch.randn((w.B, w.N, w.H, w.D), generator=gen, device=dev).to(torch.bfloat16)
+            for _ in range(4)]  # q, k, v, dO
+    site.insert(3, torch.randn((w.B, w.N, w.H), generator=gen, device=dev).to(torch.bfloat16))
+    d = gas.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block, dtype=torch.bfloat16)
+    ws = torch.empty(gas.pack3d_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    bws = torch.empty(gas.pack3d_backward_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    results = []
+    for kind, seed in ((w.packing, w.seed("perm")), (w.repack, w.seed("perm2"))):
+        coords = pi.packing_coords(w.grid, kind, block=w.block, seed=seed)
+        sites = torch.from_numpy(pi.coords_to_sites(coords, w.grid)).to(dev)
+        dc = torch.from_numpy(coords).to(dev)
+        q, k, v, g, do = (x.index_select(1, sites) for x in site)
+        out, saved = gas.pack3d_forward_train(d, dc, q, k, v, g, workspace=ws)
+        del out
+        grads = gas.pack3d_backward(d, dc, q, k, v, g, saved, do, workspace=bws)
+        del q, k, v, g, do, saved
+        back = []
+        for x in grads:
+            b = torch.empty_like(x)
+            b[:, sites] = x
+            back.append(b)
+        del grads
+        results.append(back)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv", "dgate"), results[0], results[1]):
+        assert torch.isfinite(a).all(), name
+        assert torch.equal(a, b), name
