@@ -134,6 +134,31 @@ def test_full_size_backward_repack_determinism_and_value_conservation(w):
     assert ((lhs - rhs).abs() <= 1e-2 * mass).all()
 
 
+# The summary-centre variant and grouped KV heads at the headline shape
+VARIANTS = [(pi.workload(3), "centre"),
+            (pi.Workload(33, "grid32x32x64_bf16_gqa2", (32, 32, 64), 1, 8, 48, (2, 2, 2), "bf16",
+                         "iid", "block", "group", Hkv=2), "token")]
+
+
+@pytest.mark.parametrize("w,sr", VARIANTS, ids=["centre_" + VARIANTS[0][0].name,
+                                                 VARIANTS[1][0].name])
+def test_full_size_variants_sampled_rows(w, sr):
+    import geometry_aware_sparse_amd as gas
+    coords, q, k, v, g = inputs(w)
+    _, od = desc_pair(w)
+    d = gas.make_desc(w.B, w.N, w.H, w.D, w.grid, w.block, dtype=gas.PACK3D_BF16,
+                      rope_base=w.rope_base, summary_centre=(sr == "centre"),
+                      kv_heads=w.kv_heads)
+    dt = tdtype(w)
+    ws = torch.empty(gas.pack3d_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    out = gas.pack3d_forward(d, to_dev(coords, torch.int32), to_dev(q, dt), to_dev(k, dt),
+                             to_dev(v, dt), to_dev(g, dt), workspace=ws)
+    rows = _sample_rows(w, coords)
+    ref = oracle.forward(od, coords, q, k, v, g, rows=rows, summary_rope=sr)
+    got = host(out[:, torch.from_numpy(rows).long().to("cuda")])
+    assert_close(w, got, ref, f"{w.name} ({sr} summaries) sampled rows")
+
+
 def test_2pow23_tokens_repack_equivariance():
     """2^23 tokens (128x256x256, 8 heads, head dim 48, 32,768 summaries per
     head): a token tensor holds 3.2e9 elements, past 32-bit element offsets.
