@@ -253,7 +253,7 @@ int forward_impl(const pack3d_desc *desc, const int32_t *coords, const void *q, 
   void *ksum = base + gbytes;
   void *vsum = base + gbytes + kbytes;
   auto mark = [&](int idx) -> int {
-    if (!stage_events) return PACK3D_OK;
+    if (!stage_events || !stage_events[idx]) return PACK3D_OK;  // NULL entries are skipped
     return hip_status(hipEventRecord(static_cast<hipEvent_t>(stage_events[idx]), s));
   };
   bool ok = true;
@@ -389,7 +389,7 @@ int pack3d_backward(const pack3d_desc *desc, const int32_t *coords, const void *
   hipStream_t s = static_cast<hipStream_t>(stream);
   char *base = static_cast<char *>(ws);
   auto mark = [&](int idx) -> int {
-    if (!stage_events) return PACK3D_OK;
+    if (!stage_events || !stage_events[idx]) return PACK3D_OK;  // NULL entries are skipped
     return hip_status(hipEventRecord(static_cast<hipEvent_t>(stage_events[idx]), s));
   };
   BwdArgs a;

@@ -603,9 +603,11 @@ hipError_t run_backward_t(const Geo &g, const BwdArgs &a, hipStream_t s) {
   if (hipError_t e = a.mfma ? launch_bwd_global_mfma(g, a, *a.mfma, s)
                             : run_global_bwd_valu<T, D>(g, a, s))
     return e;
-  if (a.events) {
-    if (hipError_t e = hipEventRecord(static_cast<hipEvent_t>(a.events[3]), s)) return e;
-    if (hipError_t e = hipEventRecord(static_cast<hipEvent_t>(a.events[4]), s)) return e;
+  if (a.events) {  // NULL entries are skipped
+    if (a.events[3])
+      if (hipError_t e = hipEventRecord(static_cast<hipEvent_t>(a.events[3]), s)) return e;
+    if (a.events[4])
+      if (hipError_t e = hipEventRecord(static_cast<hipEvent_t>(a.events[4]), s)) return e;
   }
   if (bwd_local_pair_supported(g, sizeof(T) == 2 ? PACK3D_BF16 : PACK3D_F32))
     return launch_bwd_local_pair(g, a, s);

@@ -231,7 +231,8 @@ def pack3d_mix(desc, gate, o_local, o_global, out=None):
 
 def pack3d_forward(desc, coords, q, k, v, gate, out=None, workspace=None, stage_events=None):
     """The whole operator. stage_events: None or a list of
-    2*PACK3D_NUM_STAGES torch.cuda.Event(enable_timing=True) objects."""
+    2*PACK3D_NUM_STAGES torch.cuda.Event(enable_timing=True) objects (a None
+    entry skips that mark; every recorded event adds stream time)."""
     _need(coords, "coords", desc, (desc.N, 3), torch.int32)
     _need(q, "q", desc, _bnhd(desc))
     _need(k, "k", desc, _bnkd(desc))
@@ -243,11 +244,7 @@ def pack3d_forward(desc, coords, q, k, v, gate, out=None, workspace=None, stage_
     if workspace is None:
         workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
-    ev = None
-    if stage_events is not None:
-        if len(stage_events) != 2 * PACK3D_NUM_STAGES:
-            raise ValueError("stage_events needs 2*PACK3D_NUM_STAGES events")
-        ev = (C.c_void_p * len(stage_events))(*[C.c_void_p(e.cuda_event) for e in stage_events])
+    ev = _events(stage_events, PACK3D_NUM_STAGES)
     _check(library().pack3d_forward(C.byref(desc), _ptr(coords), _ptr(q), _ptr(k), _ptr(v),
                                     _ptr(gate), _ptr(out), _ptr(workspace), C.c_size_t(ws_bytes),
                                     _stream(), ev), "pack3d_forward")
@@ -259,7 +256,8 @@ def _events(stage_events, n):
         return None
     if len(stage_events) != 2 * n:
         raise ValueError(f"stage_events needs {2 * n} events")
-    return (C.c_void_p * len(stage_events))(*[C.c_void_p(e.cuda_event) for e in stage_events])
+    return (C.c_void_p * len(stage_events))(
+        *[C.c_void_p(None if e is None else e.cuda_event) for e in stage_events])
 
 
 def pack3d_saved_bytes(desc):

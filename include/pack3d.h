@@ -230,7 +230,8 @@ int pack3d_workspace_bytes(const pack3d_desc *desc, size_t *bytes);
  * (ws_bytes says how large it is). stage_events: NULL, or an array of
  * 2*PACK3D_NUM_STAGES hipEvent_t (as void*) that are recorded on stream
  * before and after each stage (index, summarize, global, local+mix), for
- * timing. */
+ * timing; a NULL entry is skipped. Each recorded event costs a few
+ * microseconds of stream time, so time a stage with its own two only. */
 #define PACK3D_NUM_STAGES 4
 int pack3d_forward(const pack3d_desc *desc, const int32_t *coords, const void *q, const void *k,
                    const void *v, const void *gate, void *o, void *ws, size_t ws_bytes,
@@ -258,7 +259,8 @@ int pack3d_forward(const pack3d_desc *desc, const int32_t *coords, const void *q
  * deterministic, and a repack of the tokens permutes every gradient bit for
  * bit. ws: device workspace of at least pack3d_backward_workspace_bytes
  * bytes. stage_events: NULL or 2*PACK3D_NUM_BWD_STAGES hipEvent_t recorded
- * around each stage (geometry + summaries, global branch, local branch).
+ * around each stage (geometry + summaries, global branch, local branch);
+ * a NULL entry is skipped.
  * None of the outputs may alias an input. */
 int pack3d_saved_bytes(const pack3d_desc *desc, size_t *bytes);
 int pack3d_forward_train(const pack3d_desc *desc, const int32_t *coords, const void *q,

@@ -73,3 +73,57 @@ def test_validate_passes_valid_coordinates(w):
     dv, _ = desc_pair(w, validate=True)
     dn, _ = desc_pair(w)
     assert torch.equal(gas.pack3d_forward(dv, *dev), gas.pack3d_forward(dn, *dev))
+
+
+def test_stage_events_with_skipped_marks():
+    """stage_events entries may be None (NULL in the C ABI): those marks are
+    skipped, the others recorded; the result does not depend on them."""
+    import geometry_aware_sparse_amd as gas
+    w = pi.workload(2)
+    coords, q, k, v, g = inputs(w)
+    d, _ = desc_pair(w)
+    dt = tdtype(w)
+    dev = [to_dev(coords, torch.int32)] + [to_dev(a, dt) for a in (q, k, v, g)]
+    ref = gas.pack3d_forward(d, *dev)
+    n = 2 * gas.PACK3D_NUM_STAGES
+    for only in (None, 2):  # every mark, then the global stage's two only
+        evs = [torch.cuda.Event(enable_timing=True) if only is None or j // 2 == only else None
+               for j in range(n)]
+        for e in evs:
+            if e is not None:
+                e.record()
+        out = gas.pack3d_forward(d, *dev, stage_events=evs)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        for s in range(gas.PACK3D_NUM_STAGES):
+            if evs[2 * s] is not None:
+                assert evs[2 * s].elapsed_time(evs[2 * s + 1]) > 0
+
+
+def test_backward_stage_events_with_skipped_marks():
+    """The same for pack3d_backward: marks whose entries are None are
+    skipped, including the two the global-branch dispatch records itself."""
+    import geometry_aware_sparse_amd as gas
+    w = pi.workload(2)
+    coords, q, k, v, g = inputs(w)
+    dout = pi.pack_fields((pi.make_dout(w),), coords, w.grid)[0]
+    d, _ = desc_pair(w)
+    dt = tdtype(w)
+    dev = [to_dev(coords, torch.int32)] + [to_dev(a, dt) for a in (q, k, v, g)]
+    ddo = to_dev(dout, dt)
+    _, saved = gas.pack3d_forward_train(d, *dev)
+    ref = gas.pack3d_backward(d, *dev, saved, ddo)
+    n = 2 * gas.PACK3D_NUM_BWD_STAGES
+    for only in (None, 0, 1, 2):
+        evs = [torch.cuda.Event(enable_timing=True) if only is None or j // 2 == only else None
+               for j in range(n)]
+        for e in evs:
+            if e is not None:
+                e.record()
+        grads = gas.pack3d_backward(d, *dev, saved, ddo, stage_events=evs)
+        torch.cuda.synchronize()
+        for a, b in zip(grads, ref):
+            assert torch.equal(a, b)
+        for s in range(gas.PACK3D_NUM_BWD_STAGES):
+            if evs[2 * s] is not None:
+                assert evs[2 * s].elapsed_time(evs[2 * s + 1]) > 0
