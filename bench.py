@@ -163,9 +163,10 @@ def backward_bench(args, w, dt, es):
                     e.record()
         return evs
 
-    # the timed steps record only the two events around the global backward
-    # (its roofline); the per-stage breakdown comes from extra steps after
+    # the timed steps time the global backward (its roofline) on every
+    # SAMPLE-th step only; the per-stage breakdown comes from extra steps after
     stage_passes = min(args.steps, 10)
+    sample = max(1, args.steps // 10)
     tev = make_events(nb, args.steps, only=gi)
     fev = make_events(nf, stage_passes)
     bev = make_events(nb, stage_passes)
@@ -184,12 +185,13 @@ def backward_bench(args, w, dt, es):
     t0 = time.perf_counter()
     start.record()
     for s_ in range(args.steps):
-        step(None, tev[s_])
+        step(None, tev[s_] if s_ % sample == 0 else None)
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(stop) / args.steps
-    global_ms = float(np.mean([e[2 * gi].elapsed_time(e[2 * gi + 1]) for e in tev]))
+    global_ms = float(np.mean([tev[s_][2 * gi].elapsed_time(tev[s_][2 * gi + 1])
+                               for s_ in range(0, args.steps, sample)]))
     for s_ in range(stage_passes):
         step(fev[s_], bev[s_])
     torch.cuda.synchronize()
@@ -219,7 +221,8 @@ def backward_bench(args, w, dt, es):
                    "summaries": w.M, "tokens": w.tokens, "packing": w.packing,
                    "summary_rope": "centre" if args.summary_centre else "token"},
         "roofline": roofline, "stages": stages,
-        "stages_note": f"per-stage events from {stage_passes} extra steps after the timed ones",
+        "stages_note": (f"global backward timed on every {sample}th timed step; per-stage "
+                        f"events from {stage_passes} extra steps after the timed ones"),
         "wall_s_timed_region": round(wall, 4),
         "cpu_baseline": None,
     }
@@ -341,9 +344,11 @@ def main():
                     e.record()
         return evs
 
-    # Each recorded event costs a few microseconds of stream time, so the
-    # timed steps record only the two around the global kernel (for its
-    # roofline); the per-stage breakdown comes from a separate pass after.
+    # Each recorded event drains the stream and costs microseconds, so the
+    # timed steps time the global kernel (for its roofline) on every
+    # SAMPLE-th step only, with its two marks; the per-stage breakdown comes
+    # from a separate pass after the timed steps.
+    sample = max(1, args.steps // 10)
     timed_events = make_events(args.steps, only=gi)
     stage_passes = min(args.steps, 20)
     stage_events = make_events(stage_passes)
@@ -357,13 +362,14 @@ def main():
     start.record()
     for s in range(args.steps):
         gas.pack3d_forward(d, dc, dq, dk, dv, dg, out=out, workspace=ws,
-                           stage_events=timed_events[s])
+                           stage_events=timed_events[s] if s % sample == 0 else None)
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
-    global_ms = float(np.mean([evs[2 * gi].elapsed_time(evs[2 * gi + 1]) for evs in timed_events]))
+    global_ms = float(np.mean([timed_events[s][2 * gi].elapsed_time(timed_events[s][2 * gi + 1])
+                               for s in range(0, args.steps, sample)]))
     for s in range(stage_passes):
         gas.pack3d_forward(d, dc, dq, dk, dv, dg, out=out, workspace=ws,
                            stage_events=stage_events[s])
@@ -400,7 +406,8 @@ def main():
                    "summary_rope": "centre" if args.summary_centre else "token"},
         "roofline": roofline,
         "stages": stage_roof,
-        "stages_note": f"per-stage events from {stage_passes} extra steps after the timed ones",
+        "stages_note": (f"global kernel timed on every {sample}th timed step; per-stage events "
+                        f"from {stage_passes} extra steps after the timed ones"),
         "wall_s_timed_region": round(wall, 4),
     }
     if not args.no_cpu_baseline:
