@@ -147,11 +147,17 @@ __global__ __launch_bounds__(TZ *TY *TX) void k_local(Geo g, const void *geom, c
 }
 
 // bf16 variant for head dims that are multiples of 48: LPQ = D/24 lanes per
-// query, each owning 24 consecutive channels. Dot products use
-// v_dot2_f32_bf16 on packed pairs (the rotated, scaled query is rounded to
-// bf16) and the lanes of a query meet through DPP lane swaps; the value sum
-// pairs neighbours (k, k+1) so that one v_dot2 accumulates two neighbours
-// for one channel, the pairs being formed with v_perm_b32.
+// query; lane hh owns channels a*DA + 8hh .. +7 of each axis a (24 in all).
+// RoPE enters through relative angles: the logit of key j for query i is
+// <R(c_i) q, R(c_j) k> = <R(c_i - c_j) q, k>, the rotations being planar and
+// commuting, and every offset c_j - c_i in the neighbourhood is -1, 0 or +1
+// along each axis. So each lane rotates its query slice once by the three
+// relative angles of its axis and reads the keys unrotated: keys and values
+// both reach LDS by direct loads. Dot products use v_dot2_f32_bf16 on packed
+// pairs (the rotated, scaled query is rounded to bf16) and the lanes of a
+// query meet through DPP lane swaps; the value sum pairs neighbours (k, k+1)
+// so that one v_dot2 accumulates two neighbours for one channel, the pairs
+// being formed with v_perm_b32.
 template <int D, int TZ, int TY, int TX>
 __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_local_pair(
     Geo g, const void *geom, const bf16 *__restrict__ q, const bf16 *__restrict__ k,
@@ -160,10 +166,10 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_local_pair(
   constexpr int HZ = TZ + 2, HY = TY + 2, HX = TX + 2, NH = HZ * HY * HX, NQ = TZ * TY * TX;
   constexpr int LPQ = D / 24;          // lanes per query
   constexpr int NT = LPQ * NQ;
-  constexpr int DA = D / 3;
-  constexpr int DH = 24;               // channels per lane
+  constexpr int DA = D / 3;            // channels per axis
   constexpr int PITCH = D;             // LDS row pitch (elements), 16-byte aligned rows
   static_assert(D % 48 == 0 && (LPQ == 2 || LPQ == 4), "head dim 48 or 96");
+  static_assert(DA == 8 * LPQ, "each lane owns 8 channels (4 planes) of every axis");
   constexpr int CPS = D / 8;                // 16-byte chunks per staged row
   constexpr int NCK = NH * CPS;             // chunks per staged tensor
   constexpr int RS = (NCK + NT - 1) / NT;   // staging rounds per thread
@@ -173,7 +179,6 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_local_pair(
   __shared__ __attribute__((aligned(16))) bf16 sK[RS * NT * 8];
   __shared__ __attribute__((aligned(16))) bf16 sV[RS * NT * 8];
   __shared__ int sSlot[NH];
-  __shared__ float2 sCS[(HZ + HY + HX) * (D / 6)];  // (cos, sin) of the box's coordinates
 
   const int ntiles = ntz * nty * ntx;
   const int w = xcd_remap(blockIdx.x, gridDim.x);
@@ -184,31 +189,11 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_local_pair(
   const int32_t *slot = slot_map(geom, g);
   const float2 *tab = rope_table(geom, g);
   const int64_t bN = (int64_t)b * g.N;
-  constexpr int P = D / 6;
-  // local (cos, sin): axis a at box-relative coordinate rc (0 = one before the box)
-  auto cs_at = [&](int a, int rc, int p) {
-    const int base = a == 0 ? 0 : (a == 1 ? HZ : HZ + HY);
-    return sCS[(base + rc) * P + p];
-  };
-  // Rotation table rows of the box's coordinate range (clamped at the grid;
-  // off-grid rows are never used) and the slots of the halo sites (-1 off
-  // the grid): all loads first, then the LDS writes, one barrier.
+  // slots of the halo sites (-1 off the grid): all loads first, then the LDS
+  // writes, one barrier
   {
-    constexpr int NTAB = (HZ + HY + HX) * P;
-    constexpr int RT = (NTAB + NT - 1) / NT, RSL = (NH + NT - 1) / NT;
-    float2 tv[RT];
+    constexpr int RSL = (NH + NT - 1) / NT;
     int sv[RSL];
-#pragma unroll
-    for (int r = 0; r < RT; r++) {
-      const int e = (int)threadIdx.x + r * NT;
-      const int row = min(e, NTAB - 1) / P, p = min(e, NTAB - 1) % P;
-      int a, c;
-      if (row < HZ) { a = 0; c = z0 - 1 + row; }
-      else if (row < HZ + HY) { a = 1; c = y0 - 1 + row - HZ; }
-      else { a = 2; c = x0 - 1 + row - HZ - HY; }
-      const int dim = a == 0 ? g.Z : (a == 1 ? g.Y : g.X);
-      tv[r] = rope_cs(tab, g, a, min(max(c, 0), dim - 1), p);
-    }
 #pragma unroll
     for (int r = 0; r < RSL; r++) {
       const int hs = min((int)threadIdx.x + r * NT, NH - 1);
@@ -219,84 +204,72 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_local_pair(
       sv[r] = on ? j : -1;
     }
 #pragma unroll
-    for (int r = 0; r < RT; r++)
-      if ((int)threadIdx.x + r * NT < NTAB) sCS[threadIdx.x + r * NT] = tv[r];
-#pragma unroll
     for (int r = 0; r < RSL; r++)
       if ((int)threadIdx.x + r * NT < NH) sSlot[threadIdx.x + r * NT] = sv[r];
   }
   __syncthreads();
 
   // Every global load of the workgroup goes out before any is waited for:
-  // the raw K chunks into registers, the V chunks straight into LDS (16
-  // bytes per lane), this lane's query slice, and for the fused mix its
-  // slice of O_glob and the gate. A site off the grid reads token 0 instead:
-  // its logit is replaced by -inf and its weight is exactly 0, so only
-  // finiteness matters.
+  // the K and V chunks straight into LDS (16 bytes per lane), this lane's
+  // query slices, the (cos, sin) of one step along each of its planes, and
+  // for the fused mix its slices of O_glob and the gate. A site off the grid
+  // reads token 0 instead: its logit is replaced by -inf and its weight is
+  // exactly 0, so only finiteness matters.
   const int qn = threadIdx.x / LPQ, hh = threadIdx.x % LPQ;
   const int tz = qn / (TY * TX), ty = (qn / TX) % TY, tx = qn % TX;
   const int qs = ((tz + 1) * HY + (ty + 1)) * HX + (tx + 1);
   const int i = sSlot[qs];  // all lanes of a query see the same value
   const int wbase = __builtin_amdgcn_readfirstlane(threadIdx.x & ~63);
-  bf16x8 kraw[RS];
 #pragma unroll
   for (int r = 0; r < RS; r++) {
     const int e = min((int)threadIdx.x + r * NT, NCK - 1);
     const int hs = e / CPS, ch = e % CPS;
     const int64_t off = ((bN + max(sSlot[hs], 0)) * g.Hkv + h / g.G) * D + ch * 8;  // KV head of h
-    kraw[r] = *reinterpret_cast<const bf16x8 *>(k + off);
+    __builtin_amdgcn_global_load_lds(k + off, (lds_ptr)&sK[(wbase + r * NT) * 8], 16, 0, 0);
     __builtin_amdgcn_global_load_lds(v + off, (lds_ptr)&sV[(wbase + r * NT) * 8], 16, 0, 0);
   }
-  const int64_t off = ((bN + max(i, 0)) * g.H + h) * D + hh * DH;
-  bf16x8 qraw[DH / 8], ograw[DH / 8];
+  const int64_t row = ((bN + max(i, 0)) * g.H + h) * D;
+  bf16x8 qraw[3], ograw[3];
   float gl = 0.f;
 #pragma unroll
-  for (int c8 = 0; c8 < DH / 8; c8++) qraw[c8] = *reinterpret_cast<const bf16x8 *>(q + off + 8 * c8);
+  for (int a = 0; a < 3; a++) qraw[a] = *reinterpret_cast<const bf16x8 *>(q + row + a * DA + 8 * hh);
   if (gate) {
 #pragma unroll
-    for (int c8 = 0; c8 < DH / 8; c8++)
-      ograw[c8] = *reinterpret_cast<const bf16x8 *>(oglob + off + 8 * c8);
+    for (int a = 0; a < 3; a++)
+      ograw[a] = *reinterpret_cast<const bf16x8 *>(oglob + row + a * DA + 8 * hh);
     gl = (float)gate[(bN + max(i, 0)) * g.H + h];
   }
-  // rotate the staged keys at their own coordinates
+  // one unit step of plane 4hh+u of axis a: the table's row for coordinate 1
+  // (an axis one site long has no neighbour along it; its row 0 keeps the
+  // unused values finite)
+  float2 cs1[3][4];
 #pragma unroll
-  for (int r = 0; r < RS; r++) {
-    const int e = (int)threadIdx.x + r * NT;
-    const int ec = min(e, NCK - 1);
-    const int hs = ec / CPS, ch = ec % CPS;
-    const int rc3[3] = {hs / (HY * HX), (hs / HX) % HY, hs % HX};
-    const int a = (ch * 8) / DA, p0 = ((ch * 8) % DA) / 2;
-    bf16x8 ko;
+  for (int a = 0; a < 3; a++) {
+    const int dim = a == 0 ? g.Z : (a == 1 ? g.Y : g.X);
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-      float k0 = (float)kraw[r][2 * u], k1 = (float)kraw[r][2 * u + 1];
-      rotate(k0, k1, cs_at(a, rc3[a], p0 + u));
-      ko[2 * u] = (bf16)k0;
-      ko[2 * u + 1] = (bf16)k1;
-    }
-    *reinterpret_cast<bf16x8 *>(&sK[e * 8]) = ko;
+    for (int u = 0; u < 4; u++) cs1[a][u] = rope_cs(tab, g, a, min(1, dim - 1), 4 * hh + u);
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
   __syncthreads();
   if (i < 0) return;
   const float qscale = g.scale * kLog2e;
 
-  bf16x2 qp[DH / 2];
-  {
-    const int rc3[3] = {tz + 1, ty + 1, tx + 1};
+  // qv[a][d + 1]: the query slice of axis a rotated by the relative angle of
+  // a neighbour at offset d along a, R(-d theta), scaled and rounded to bf16
+  bf16x2 qv[3][3][4];
 #pragma unroll
-    for (int c8 = 0; c8 < DH / 8; c8++) {
-      const bf16x8 raw = qraw[c8];
-      const int d0 = hh * DH + 8 * c8, a = d0 / DA, p0 = (d0 % DA) / 2;
+  for (int a = 0; a < 3; a++)
 #pragma unroll
-      for (int u = 0; u < 4; u++) {
-        float x0v = (float)raw[2 * u], x1v = (float)raw[2 * u + 1];
-        rotate(x0v, x1v, cs_at(a, rc3[a], p0 + u));
-        qp[4 * c8 + u][0] = (bf16)(x0v * qscale);
-        qp[4 * c8 + u][1] = (bf16)(x1v * qscale);
+    for (int u = 0; u < 4; u++) {
+      const float x0v = (float)qraw[a][2 * u], x1v = (float)qraw[a][2 * u + 1];
+#pragma unroll
+      for (int d = -1; d <= 1; d++) {
+        float y0 = x0v, y1 = x1v;
+        if (d != 0) rotate(y0, y1, make_float2(cs1[a][u].x, d > 0 ? -cs1[a][u].y : cs1[a][u].y));
+        qv[a][d + 1][u][0] = (bf16)(y0 * qscale);
+        qv[a][d + 1][u][1] = (bf16)(y1 * qscale);
       }
     }
-  }
 
   // sum over the LPQ lanes of a query (adjacent lanes) with DPP swaps
   auto lane_sum = [&](float x) {
@@ -313,11 +286,15 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_local_pair(
   float mx = -INFINITY;
 #pragma unroll
   for (int kk = 0; kk < 27; kk++) {
-    const int hs = qs + ((kk / 9) - 1) * HY * HX + (((kk / 3) % 3) - 1) * HX + (kk % 3) - 1;
-    const bf16x2 *kr = reinterpret_cast<const bf16x2 *>(sK + hs * PITCH + hh * DH);
+    const int dd[3] = {kk / 9 - 1, (kk / 3) % 3 - 1, kk % 3 - 1};
+    const int hs = qs + dd[0] * HY * HX + dd[1] * HX + dd[2];
+    const bf16x2 *kr = reinterpret_cast<const bf16x2 *>(sK + hs * PITCH + 8 * hh);
     float acc = 0.f;
 #pragma unroll
-    for (int j = 0; j < DH / 2; j++) acc = __builtin_amdgcn_fdot2_f32_bf16(qp[j], kr[j], acc, false);
+    for (int a = 0; a < 3; a++)
+#pragma unroll
+      for (int u = 0; u < 4; u++)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(qv[a][dd[a] + 1][u], kr[a * (DA / 2) + u], acc, false);
     acc = lane_sum(acc);
     lg[kk] = sSlot[hs] >= 0 ? acc : -INFINITY;
     mx = fmaxf(mx, lg[kk]);
@@ -332,9 +309,9 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_local_pair(
   float den = 0.f;
   bf16x2 ones2;
   ones2[0] = ones2[1] = (bf16)1.0f;
-  float o[DH];
+  float o[24];  // channel a*DA + 8hh + c at o[8a + c]
 #pragma unroll
-  for (int d = 0; d < DH; d++) o[d] = 0.f;
+  for (int d = 0; d < 24; d++) o[d] = 0.f;
   // neighbours in pairs (2j, 2j+1); the last pair's second member has weight 0
 #pragma unroll
   for (int kp = 0; kp < 14; kp++) {
@@ -345,38 +322,41 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_local_pair(
     pp[0] = (bf16)pr[2 * kp];
     pp[1] = (bf16)pr[2 * kp + 1];
     den = __builtin_amdgcn_fdot2_f32_bf16(pp, ones2, den, false);
-    const uint32_t *A = reinterpret_cast<const uint32_t *>(sV + hs0 * PITCH + hh * DH);
-    const uint32_t *Bv = reinterpret_cast<const uint32_t *>(sV + hs1 * PITCH + hh * DH);
+    const uint32_t *A = reinterpret_cast<const uint32_t *>(sV + hs0 * PITCH + 8 * hh);
+    const uint32_t *Bv = reinterpret_cast<const uint32_t *>(sV + hs1 * PITCH + 8 * hh);
 #pragma unroll
-    for (int j = 0; j < DH / 2; j++) {
-      const uint32_t a = A[j], bb = Bv[j];
-      // (a.lo, b.lo) and (a.hi, b.hi)
-      const uint32_t lo = __builtin_amdgcn_perm(bb, a, 0x05040100u);
-      const uint32_t hi2 = __builtin_amdgcn_perm(bb, a, 0x07060302u);
-      o[2 * j] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2, lo), o[2 * j], false);
-      o[2 * j + 1] =
-          __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2, hi2), o[2 * j + 1], false);
-    }
+    for (int a = 0; a < 3; a++)
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const uint32_t aw = A[a * (DA / 2) + u], bw = Bv[a * (DA / 2) + u];
+        // (a.lo, b.lo) and (a.hi, b.hi)
+        const uint32_t lo = __builtin_amdgcn_perm(bw, aw, 0x05040100u);
+        const uint32_t hi2 = __builtin_amdgcn_perm(bw, aw, 0x07060302u);
+        o[8 * a + 2 * u] =
+            __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2, lo), o[8 * a + 2 * u], false);
+        o[8 * a + 2 * u + 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2, hi2),
+                                                               o[8 * a + 2 * u + 1], false);
+      }
   }
   const float inv = 1.0f / den;
   if (gate) {
     const float gg = 1.0f / (1.0f + expf(-gl));
 #pragma unroll
-    for (int c8 = 0; c8 < DH / 8; c8++) {
-      const bf16x8 og = ograw[c8];
+    for (int a = 0; a < 3; a++) {
+      const bf16x8 og = ograw[a];
       bf16x8 r;
 #pragma unroll
       for (int u = 0; u < 8; u++)
-        r[u] = (bf16)((1.0f - gg) * (o[8 * c8 + u] * inv) + gg * (float)og[u]);
-      *reinterpret_cast<bf16x8 *>(out + off + 8 * c8) = r;
+        r[u] = (bf16)((1.0f - gg) * (o[8 * a + u] * inv) + gg * (float)og[u]);
+      *reinterpret_cast<bf16x8 *>(out + row + a * DA + 8 * hh) = r;
     }
   } else {
 #pragma unroll
-    for (int c8 = 0; c8 < DH / 8; c8++) {
+    for (int a = 0; a < 3; a++) {
       bf16x8 r;
 #pragma unroll
-      for (int u = 0; u < 8; u++) r[u] = (bf16)(o[8 * c8 + u] * inv);
-      *reinterpret_cast<bf16x8 *>(out + off + 8 * c8) = r;
+      for (int u = 0; u < 8; u++) r[u] = (bf16)(o[8 * a + u] * inv);
+      *reinterpret_cast<bf16x8 *>(out + row + a * DA + 8 * hh) = r;
     }
   }
 }
