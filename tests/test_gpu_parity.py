@@ -26,6 +26,9 @@ CASES = [
     W(105, "f32_d96", (4, 5, 6), 1, 1, 96, (2, 2, 2), "f32", "iid", "random", "raster"),
     W(106, "bf16_d24_peaked", (6, 6, 6), 1, 2, 24, (3, 3, 3), "bf16", "smooth", "block", "raster"),
     W(107, "single_site", (1, 1, 1), 1, 1, 48, (1, 1, 1), "bf16", "iid", "raster", "raster"),
+    # one axis a single site long: no neighbour along it, no rotation step
+    W(114, "slab_z1_bf16_d48", (1, 12, 21), 1, 2, 48, (1, 2, 2), "bf16", "iid", "random", "raster"),
+    W(115, "slab_y1_bf16_d96", (5, 1, 17), 1, 2, 96, (2, 1, 3), "bf16", "smooth", "block", "random"),
     # grouped key/value heads (GQA, MQA): query head h reads KV head h // (H // Hkv)
     W(110, "gqa4x2_bf16_d48", (10, 13, 19), 1, 4, 48, (2, 2, 2), "bf16", "iid", "random", "morton",
       Hkv=2),
