@@ -64,8 +64,23 @@ __device__ __forceinline__ void pair_accumulate(float *o, float w0, float w1, co
   }
 }
 
-__device__ __forceinline__ int halo_offset(int kk, int HY, int HX) {
-  return ((kk / 9) - 1) * HY * HX + (((kk / 3) % 3) - 1) * HX + (kk % 3) - 1;
+// An empty asm that takes the N accumulators as read-write operands: the
+// products feeding them are issued before it, so a loop that calls this
+// after each step keeps only that step's operands live (without it the
+// scheduler hoists every step's LDS reads and byte permutes ahead of the
+// accumulation and runs out of registers).
+template <int N>
+__device__ __forceinline__ void pin(float *a) {
+#pragma unroll
+  for (int d = 0; d < N; d++) asm volatile("" : "+v"(a[d]));
+}
+
+// Halo index of neighbour kk (canonical order: dz outermost, dx innermost)
+// counted from the site's (-1, -1, -1) corner, never negative: addresses
+// formed from one corner base then differ by constants that fit the LDS
+// instructions' unsigned offset field, so they need no register each.
+__device__ __forceinline__ int halo_from_corner(int kk, int HY, int HX) {
+  return (kk / 9) * HY * HX + ((kk / 3) % 3) * HX + kk % 3;
 }
 }  // namespace
 
@@ -108,7 +123,7 @@ __device__ __forceinline__ void stage_box(const Geo &g, const int32_t *slot, con
 
 // ---------------------------------------------------------------------------
 template <int D, int TZ, int TY, int TX>
-__global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_bwd_local_q_pair(
+__global__ __launch_bounds__((D / 24) * TZ *TY *TX, 2) void k_bwd_local_q_pair(
     Geo g, const void *geom, const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const bf16 *__restrict__ v, const bf16 *__restrict__ gate, const bf16 *__restrict__ dout,
     const bf16 *__restrict__ oglob, const float *__restrict__ dqg, bf16 *dq, bf16 *dgate,
@@ -138,6 +153,7 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_bwd_local_q_pair(
   const int qn = threadIdx.x / LPQ, hh = threadIdx.x % LPQ;
   const int tz = qn / (TY * TX), ty = (qn / TX) % TY, tx = qn % TX;
   const int qs = ((tz + 1) * HY + (ty + 1)) * HX + (tx + 1);
+  const int qc = (tz * HY + ty) * HX + tx;  // the query's (-1, -1, -1) corner
   const int i = sSlot[qs];
   const int wbase = __builtin_amdgcn_readfirstlane(threadIdx.x & ~63);
   // global loads first: raw K chunks, V straight to LDS, this lane's q and dO
@@ -204,7 +220,7 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_bwd_local_q_pair(
   float mx = -INFINITY;
 #pragma unroll
   for (int kk = 0; kk < 27; kk++) {
-    const int hs = qs + halo_offset(kk, HY, HX);
+    const int hs = qc + halo_from_corner(kk, HY, HX);
     const bf16x2 *kr = reinterpret_cast<const bf16x2 *>(sK + hs * D + hh * DH);
     const bf16x2 *vr = reinterpret_cast<const bf16x2 *>(sV + hs * D + hh * DH);
     float a0 = 0.f, a1 = 0.f;
@@ -219,7 +235,7 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_bwd_local_q_pair(
     mx = fmaxf(mx, lg[kk]);
     // a compiler-only fence every three neighbours: the rows of the next
     // ones are not loaded early, which would hold dozens of registers
-    if (kk % 3 == 2) asm volatile("" ::: "memory");
+    asm volatile("" ::: "memory");
   }
   float den = 0.f;
 #pragma unroll
@@ -247,8 +263,9 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_bwd_local_q_pair(
     const int k0 = 2 * kp, k1 = kp < 13 ? 2 * kp + 1 : 2 * kp;
     const float w0 = lg[k0] * (omg * uu[k0] - delta);
     const float w1 = kp < 13 ? lg[k1] * (omg * uu[k1] - delta) : 0.f;
-    pair_accumulate<DH>(acc, w0, w1, sK + (qs + halo_offset(k0, HY, HX)) * D + hh * DH,
-                        sK + (qs + halo_offset(k1, HY, HX)) * D + hh * DH);
+    pair_accumulate<DH>(acc, w0, w1, sK + (qc + halo_from_corner(k0, HY, HX)) * D + hh * DH,
+                        sK + (qc + halo_from_corner(k1, HY, HX)) * D + hh * DH);
+    pin<DH>(acc);
     asm volatile("" ::: "memory");
   }
   // dq = R^T (s dq~_loc + dq~_glob); dG = g (1 - g) (<dO, O_glob> - <dO, O_loc>)
@@ -287,7 +304,7 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_bwd_local_q_pair(
 
 // ---------------------------------------------------------------------------
 template <int D, int TZ, int TY, int TX, bool CENTRE>
-__global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_bwd_local_kv_pair(
+__global__ __launch_bounds__((D / 24) * TZ *TY *TX, 2) void k_bwd_local_kv_pair(
     Geo g, const void *geom, const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const bf16 *__restrict__ v, const bf16 *__restrict__ gate, const bf16 *__restrict__ dout,
     const float *__restrict__ lse_l, const float *__restrict__ delta_l,
@@ -396,11 +413,16 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_bwd_local_kv_pair(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (j < 0) continue;
+    // the key's corner index, opaque to the compiler within this head: the
+    // 27 neighbour addresses derived from it are formed here rather than
+    // hoisted out of the head loop, where they would hold ~100 registers
+    int ksh = ((tz * HY) + ty) * HX + tx;  // the key's (-1, -1, -1) corner
+    asm volatile("" : "+v"(ksh));
     // logits (the query side's, bit for bit) and u_ij = <dO_i, v_j>
     float pw[27], dsw[27];
 #pragma unroll
     for (int kk = 0; kk < 27; kk++) {
-      const int hs = ks_ + halo_offset(kk, HY, HX);
+      const int hs = ksh + halo_from_corner(kk, HY, HX);
       const bf16x2 *qr = reinterpret_cast<const bf16x2 *>(sQ + hs * D + hh * DH);
       const bf16x2 *orr = reinterpret_cast<const bf16x2 *>(sO + hs * D + hh * DH);
       float a0 = 0.f, a1 = 0.f;
@@ -415,16 +437,29 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_bwd_local_kv_pair(
       const float pr = valid ? __builtin_amdgcn_exp2f(a0 - sL[hs]) : 0.f;
       pw[kk] = pr * sOmg[hs];
       dsw[kk] = pr * (sOmg[hs] * a1 - sDl[hs]);
-      if (kk % 3 == 2) asm volatile("" ::: "memory");  // as on the query side
+      pin<1>(&pw[kk]);
+      pin<1>(&dsw[kk]);
+      asm volatile("" ::: "memory");  // as on the query side
     }
     asm volatile("" ::: "memory");  // the next phase re-reads its rows from LDS
+    // dk~ over the staged queries, then dv over the staged dO: one row pair
+    // in flight at a time
 #pragma unroll
     for (int kp2 = 0; kp2 < 14; kp2++) {
       const int k0 = 2 * kp2, k1 = kp2 < 13 ? 2 * kp2 + 1 : 2 * kp2;
-      const int hs0 = ks_ + halo_offset(k0, HY, HX), hs1 = ks_ + halo_offset(k1, HY, HX);
+      const int hs0 = ksh + halo_from_corner(k0, HY, HX), hs1 = ksh + halo_from_corner(k1, HY, HX);
       const float c1 = kp2 < 13 ? 1.f : 0.f;
       pair_accumulate<DH>(adk, dsw[k0], c1 * dsw[k1], sQ + hs0 * D + hh * DH, sQ + hs1 * D + hh * DH);
+      pin<DH>(adk);
+      asm volatile("" ::: "memory");
+    }
+#pragma unroll
+    for (int kp2 = 0; kp2 < 14; kp2++) {
+      const int k0 = 2 * kp2, k1 = kp2 < 13 ? 2 * kp2 + 1 : 2 * kp2;
+      const int hs0 = ksh + halo_from_corner(k0, HY, HX), hs1 = ksh + halo_from_corner(k1, HY, HX);
+      const float c1 = kp2 < 13 ? 1.f : 0.f;
       pair_accumulate<DH>(adv, pw[k0], c1 * pw[k1], sO + hs0 * D + hh * DH, sO + hs1 * D + hh * DH);
+      pin<DH>(adv);
       asm volatile("" ::: "memory");
     }
   }
