@@ -176,8 +176,10 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_local_pair(
   // rows are PITCH = D apart, so chunk e of the halo is at element 8e; the
   // arrays are padded to whole rounds so that every lane of every round has
   // a place to write
+  // one LDS buffer holds the keys for the logits, then the values for the
+  // sums, so that the workgroup needs half the LDS and more of them fit a CU
   __shared__ __attribute__((aligned(16))) bf16 sK[RS * NT * 8];
-  __shared__ __attribute__((aligned(16))) bf16 sV[RS * NT * 8];
+  const bf16 *sV = sK;
   __shared__ int sSlot[NH];
 
   const int ntiles = ntz * nty * ntx;
@@ -220,13 +222,14 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_local_pair(
   const int qs = ((tz + 1) * HY + (ty + 1)) * HX + (tx + 1);
   const int i = sSlot[qs];  // all lanes of a query see the same value
   const int wbase = __builtin_amdgcn_readfirstlane(threadIdx.x & ~63);
+  bf16x8 vraw[RS];  // value chunks, held until the keys have been used
 #pragma unroll
   for (int r = 0; r < RS; r++) {
     const int e = min((int)threadIdx.x + r * NT, NCK - 1);
     const int hs = e / CPS, ch = e % CPS;
     const int64_t off = ((bN + max(sSlot[hs], 0)) * g.Hkv + h / g.G) * D + ch * 8;  // KV head of h
     __builtin_amdgcn_global_load_lds(k + off, (lds_ptr)&sK[(wbase + r * NT) * 8], 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(v + off, (lds_ptr)&sV[(wbase + r * NT) * 8], 16, 0, 0);
+    vraw[r] = *reinterpret_cast<const bf16x8 *>(v + off);
   }
   const int64_t row = ((bN + max(i, 0)) * g.H + h) * D;
   bf16x8 qraw[3], ograw[3];
@@ -249,9 +252,10 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_local_pair(
 #pragma unroll
     for (int u = 0; u < 4; u++) cs1[a][u] = rope_cs(tab, g, a, min(1, dim - 1), 4 * hh + u);
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have landed
   __syncthreads();
-  if (i < 0) return;
+  // every lane runs to the end (the barriers below need the whole
+  // workgroup); a query site off the grid stores nothing
   const float qscale = g.scale * kLog2e;
 
   // qv[a][d + 1]: the query slice of axis a rotated by the relative angle of
@@ -299,11 +303,17 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_local_pair(
     lg[kk] = sSlot[hs] >= 0 ? acc : -INFINITY;
     mx = fmaxf(mx, lg[kk]);
   }
+  // the keys are no longer read: the buffer takes the values
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < RS; r++)
+    *reinterpret_cast<bf16x8 *>(&sK[((int)threadIdx.x + r * NT) * 8]) = vraw[r];
   float pr[28];
 #pragma unroll
   for (int kk = 0; kk < 27; kk++)
     pr[kk] = __builtin_amdgcn_exp2f(lg[kk] - mx);  // exactly 0 for an invalid neighbour
   pr[27] = 0.f;
+  __syncthreads();
   // the weights are rounded to bf16 for the value products; the denominator
   // sums the same rounded weights, so the weights used sum to one
   float den = 0.f;
@@ -339,6 +349,7 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_local_pair(
       }
   }
   const float inv = 1.0f / den;
+  if (i < 0) return;
   if (gate) {
     const float gg = 1.0f / (1.0f + expf(-gl));
 #pragma unroll
