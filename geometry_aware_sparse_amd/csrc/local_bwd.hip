@@ -123,7 +123,7 @@ __device__ __forceinline__ void stage_box(const Geo &g, const int32_t *slot, con
 
 // ---------------------------------------------------------------------------
 template <int D, int TZ, int TY, int TX>
-__global__ __launch_bounds__((D / 24) * TZ *TY *TX, 2) void k_bwd_local_q_pair(
+__global__ __launch_bounds__((D / 24) * TZ *TY *TX, D == 48 ? 3 : 2) void k_bwd_local_q_pair(
     Geo g, const void *geom, const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const bf16 *__restrict__ v, const bf16 *__restrict__ gate, const bf16 *__restrict__ dout,
     const bf16 *__restrict__ oglob, const float *__restrict__ dqg, bf16 *dq, bf16 *dgate,
@@ -132,8 +132,10 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX, 2) void k_bwd_local_q_pair(
   constexpr int LPQ = D / 24, NT = LPQ * NQ, DA = D / 3, DH = 24, P = D / 6;
   constexpr int CPS = D / 8, NCK = NH * CPS, RS = (NCK + NT - 1) / NT;
   static_assert(D % 48 == 0 && (LPQ == 2 || LPQ == 4), "head dim 48 or 96");
+  // one LDS buffer holds the values for u_j = <dO, v_j>, then the rotated
+  // keys for the logits and dq, so that more workgroups fit a CU
   __shared__ __attribute__((aligned(16))) bf16 sK[RS * NT * 8];
-  __shared__ __attribute__((aligned(16))) bf16 sV[RS * NT * 8];
+  const bf16 *sV = sK;
   __shared__ int sSlot[NH];
   __shared__ float2 sCS[(HZ + HY + HX) * P];
 
@@ -166,7 +168,7 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX, 2) void k_bwd_local_q_pair(
     const int hs = e / CPS, ch = e % CPS;
     const int64_t off = ((bN + max(sSlot[hs], 0)) * g.Hkv + hk) * D + ch * 8;
     kraw[r] = *reinterpret_cast<const bf16x8 *>(k + off);
-    __builtin_amdgcn_global_load_lds(v + off, (lds_ptr)&sV[(wbase + r * NT) * 8], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(v + off, (lds_ptr)&sK[(wbase + r * NT) * 8], 16, 0, 0);
   }
   const int64_t row = (bN + max(i, 0)) * g.H + h;
   const int64_t off = row * D + hh * DH;
@@ -177,6 +179,42 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX, 2) void k_bwd_local_q_pair(
     draw[c8] = *reinterpret_cast<const bf16x8 *>(dout + off + 8 * c8);
   }
   const float gl = (float)gate[row];
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // every lane runs to the end (the barriers below need the whole
+  // workgroup); a query site off the grid stores nothing
+  const float qscale = g.scale * kLog2e;
+  const int rc3[3] = {tz + 1, ty + 1, tx + 1};
+
+  bf16x2 qp[DH / 2], dp[DH / 2];
+#pragma unroll
+  for (int c8 = 0; c8 < DH / 8; c8++) {
+    const int d0 = hh * DH + 8 * c8, a = d0 / DA, p0 = (d0 % DA) / 2;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      float x0 = (float)qraw[c8][2 * u], x1 = (float)qraw[c8][2 * u + 1];
+      rotate(x0, x1, cs_at(a, rc3[a], p0 + u));
+      qp[4 * c8 + u][0] = (bf16)(x0 * qscale);
+      qp[4 * c8 + u][1] = (bf16)(x1 * qscale);
+      dp[4 * c8 + u][0] = draw[c8][2 * u];
+      dp[4 * c8 + u][1] = draw[c8][2 * u + 1];
+    }
+  }
+  // u_j = <dO, v_j>, canonical offset order, from the staged values
+  float lg[27], uu[27];
+#pragma unroll
+  for (int kk = 0; kk < 27; kk++) {
+    const int hs = qc + halo_from_corner(kk, HY, HX);
+    const bf16x2 *vr = reinterpret_cast<const bf16x2 *>(sV + hs * D + hh * DH);
+    float a1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < DH / 2; j++) a1 = __builtin_amdgcn_fdot2_f32_bf16(dp[j], vr[j], a1, false);
+    uu[kk] = lane_sum<LPQ>(a1);
+    // a compiler-only fence per neighbour: the rows of the next ones are not
+    // loaded early, which would hold dozens of registers
+    asm volatile("" ::: "memory");
+  }
+  __syncthreads();  // the values are no longer read: the buffer takes the keys
   // rotate the staged keys at their own coordinates, as the forward does
 #pragma unroll
   for (int r = 0; r < RS; r++) {
@@ -195,46 +233,19 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX, 2) void k_bwd_local_q_pair(
     }
     *reinterpret_cast<bf16x8 *>(&sK[e * 8]) = ko;
   }
-  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (i < 0) return;
-  const float qscale = g.scale * kLog2e;
-  const int rc3[3] = {tz + 1, ty + 1, tx + 1};
-
-  bf16x2 qp[DH / 2], dp[DH / 2];
-#pragma unroll
-  for (int c8 = 0; c8 < DH / 8; c8++) {
-    const int d0 = hh * DH + 8 * c8, a = d0 / DA, p0 = (d0 % DA) / 2;
-#pragma unroll
-    for (int u = 0; u < 4; u++) {
-      float x0 = (float)qraw[c8][2 * u], x1 = (float)qraw[c8][2 * u + 1];
-      rotate(x0, x1, cs_at(a, rc3[a], p0 + u));
-      qp[4 * c8 + u][0] = (bf16)(x0 * qscale);
-      qp[4 * c8 + u][1] = (bf16)(x1 * qscale);
-      dp[4 * c8 + u][0] = draw[c8][2 * u];
-      dp[4 * c8 + u][1] = draw[c8][2 * u + 1];
-    }
-  }
-  // logits (log2 units) and u_j = <dO, v_j>, canonical offset order
-  float lg[27], uu[27];
+  // logits (log2 units), canonical offset order
   float mx = -INFINITY;
 #pragma unroll
   for (int kk = 0; kk < 27; kk++) {
     const int hs = qc + halo_from_corner(kk, HY, HX);
     const bf16x2 *kr = reinterpret_cast<const bf16x2 *>(sK + hs * D + hh * DH);
-    const bf16x2 *vr = reinterpret_cast<const bf16x2 *>(sV + hs * D + hh * DH);
-    float a0 = 0.f, a1 = 0.f;
+    float a0 = 0.f;
 #pragma unroll
-    for (int j = 0; j < DH / 2; j++) {
-      a0 = __builtin_amdgcn_fdot2_f32_bf16(qp[j], kr[j], a0, false);
-      a1 = __builtin_amdgcn_fdot2_f32_bf16(dp[j], vr[j], a1, false);
-    }
+    for (int j = 0; j < DH / 2; j++) a0 = __builtin_amdgcn_fdot2_f32_bf16(qp[j], kr[j], a0, false);
     a0 = lane_sum<LPQ>(a0);
-    uu[kk] = lane_sum<LPQ>(a1);
     lg[kk] = sSlot[hs] >= 0 ? a0 : -INFINITY;
     mx = fmaxf(mx, lg[kk]);
-    // a compiler-only fence every three neighbours: the rows of the next
-    // ones are not loaded early, which would hold dozens of registers
     asm volatile("" ::: "memory");
   }
   float den = 0.f;
@@ -268,6 +279,7 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX, 2) void k_bwd_local_q_pair(
     pin<DH>(acc);
     asm volatile("" ::: "memory");
   }
+  if (i < 0) return;
   // dq = R^T (s dq~_loc + dq~_glob); dG = g (1 - g) (<dO, O_glob> - <dO, O_loc>)
   bf16x8 oraw[DH / 8];
   f32x4 gq[DH / 4];
