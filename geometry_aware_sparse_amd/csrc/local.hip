@@ -158,8 +158,10 @@ __global__ __launch_bounds__(TZ *TY *TX) void k_local(Geo g, const void *geom, c
 // query meet through DPP lane swaps; the value sum pairs neighbours (k, k+1)
 // so that one v_dot2 accumulates two neighbours for one channel, the pairs
 // being formed with v_perm_b32.
+// D = 96 workgroups are 8 waves with 74 KB of LDS: asking for four waves per
+// SIMD (128 VGPRs, a few values spilled) lets two of them share a CU
 template <int D, int TZ, int TY, int TX>
-__global__ __launch_bounds__((D / 24) * TZ *TY *TX) void k_local_pair(
+__global__ __launch_bounds__((D / 24) * TZ *TY *TX, D == 96 ? 4 : 1) void k_local_pair(
     Geo g, const void *geom, const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const bf16 *__restrict__ v, const bf16 *gate, const bf16 *oglob, bf16 *out, int ntz, int nty,
     int ntx) {
