@@ -214,9 +214,10 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX, D == 96 ? 4 : 1) void k_loca
   __syncthreads();
 
   // Every global load of the workgroup goes out before any is waited for:
-  // the K and V chunks straight into LDS (16 bytes per lane), this lane's
-  // query slices, the (cos, sin) of one step along each of its planes, and
-  // for the fused mix its slices of O_glob and the gate. A site off the grid
+  // the K chunks straight into LDS (16 bytes per lane), the V chunks into
+  // registers (they go into the same LDS buffer once the logits are done),
+  // this lane's query slices, the (cos, sin) of one step along each of its
+  // planes, and for the fused mix its slices of O_glob and the gate. A site off the grid
   // reads token 0 instead: its logit is replaced by -inf and its weight is
   // exactly 0, so only finiteness matters.
   const int qn = threadIdx.x / LPQ, hh = threadIdx.x % LPQ;
