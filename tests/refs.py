@@ -30,6 +30,29 @@ def rotation(coord, D, base=10000.0):
     return scipy.linalg.expm(generator(coord, D, base))
 
 
+def sequence_generator(pos, D, base=10000.0):
+    """Skew-symmetric D x D generator of 1-D RoPE at a packed sequence index
+    (the control of paper summary §B.4): plane p is the channel pair
+    (2p, 2p+1) over all D channels, angular rate theta_p = base^(-2p/D)."""
+    G = np.zeros((D, D))
+    for p in range(D // 2):
+        th = base ** (-2.0 * p / D)
+        G[2 * p + 1, 2 * p] += pos * th
+        G[2 * p, 2 * p + 1] -= pos * th
+    return G
+
+
+def sequence_rotate_all(x, base=10000.0):
+    """x: [B, N, H, D] -> the 1-D rotation at packed index i of row i, via
+    explicit matrices."""
+    D = x.shape[-1]
+    out = np.empty_like(x, dtype=np.float64)
+    for i in range(x.shape[1]):
+        R = scipy.linalg.expm(sequence_generator(i, D, base))
+        out[:, i] = x[:, i].astype(np.float64) @ R.T
+    return out
+
+
 def rotate_all(coords, x, base=10000.0):
     """x: [B, N, H, D] -> R(c_i) x_i via explicit matrices."""
     D = x.shape[-1]

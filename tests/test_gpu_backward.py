@@ -52,6 +52,16 @@ CASES = [
        "raster", Hkv=1), "token", 0),
 ]
 IDS = [f"{w.name}-{sr}" for w, sr, _ in CASES]
+BY_NAME = {w.name: (w, sr, excl) for w, sr, excl in CASES}
+assert len(BY_NAME) == len(CASES), "case names are unique"
+# gates saturated to one side: one grouped case per dtype, D = 96 multi-query,
+# the centre variant in both dtypes
+BRANCH_CASES = ["f32_d12_gqa", "bf16_d48_gqa", "bf16_d96_mqa", "f32_d48_centre",
+                "bf16_d24_centre"]
+REPACK_CASES = ["bf16_d48_gqa", "bf16_d24_centre"]
+assert any(BY_NAME[n][0].kv_heads < BY_NAME[n][0].H for n in BRANCH_CASES)
+assert {BY_NAME[n][1] for n in BRANCH_CASES} == {"token", "centre"}
+assert {BY_NAME[n][0].dtype for n in BRANCH_CASES} == {"f32", "bf16"}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -99,9 +109,9 @@ def test_backward_matches_oracle(w, sr, excl):
 
 
 @pytest.mark.parametrize("gate", [30.0, -30.0], ids=["global_only", "local_only"])
-@pytest.mark.parametrize("idx", [1, 2, 3, 4, 6], ids=[IDS[i] for i in (1, 2, 3, 4, 6)])
-def test_backward_each_branch_alone(idx, gate):
-    w, sr, excl = CASES[idx]
+@pytest.mark.parametrize("name", BRANCH_CASES)
+def test_backward_each_branch_alone(name, gate):
+    w, sr, excl = BY_NAME[name]
     gas, d, od, coords, (q, k, v, g, dout), dev, o, saved, grads = _run(w, sr, excl,
                                                                        gate_override=gate)
     ref = oracle.backward(od, coords, q, k, v, g, dout, summary_rope=sr)
@@ -110,7 +120,7 @@ def test_backward_each_branch_alone(idx, gate):
 
 def test_saved_lse_is_the_global_log_sum_exp():
     # lse = log2 sum_m exp2(t_m), t = <q~, k_sum_m> * scale * log2(e), per (b, i, h)
-    w, sr, excl = CASES[1]
+    w, sr, excl = BY_NAME["f32_d12_gqa"]
     gas, d, od, coords, (q, k, v, g, dout), dev, o, saved, grads = _run(w, sr, excl)
     _, lse = gas.saved_views(d, saved)
     slot, _, _ = oracle.index(od, coords)
@@ -122,9 +132,9 @@ def test_saved_lse_is_the_global_log_sum_exp():
     assert np.abs(lse.cpu().numpy() - ref).max() < 1e-4
 
 
-@pytest.mark.parametrize("idx", [2, 6], ids=[IDS[2], IDS[6]])
-def test_backward_repack_permutes_gradients_bitwise(idx):
-    w, sr, excl = CASES[idx]
+@pytest.mark.parametrize("name", REPACK_CASES)
+def test_backward_repack_permutes_gradients_bitwise(name):
+    w, sr, excl = BY_NAME[name]
     outs = []
     for packing in (w.packing, w.repack):
         gas, d, od, coords, _, dev, o, saved, grads = _run(w, sr, excl, packing=packing)
@@ -136,7 +146,7 @@ def test_backward_repack_permutes_gradients_bitwise(idx):
 
 def test_backward_is_deterministic():
     import geometry_aware_sparse_amd as gas
-    w, sr, excl = CASES[7]
+    w, sr, excl = BY_NAME["grid16_bf16"]
     _, d, _, _, (_, _, _, _, dout), dev, o, saved, grads = _run(w, sr, excl)
     again = gas.pack3d_backward(d, *dev, saved, to_dev(dout, tdtype(w)))
     for a, b in zip(grads, again):

@@ -31,6 +31,13 @@ SMALL = [
 ]
 
 
+BY_ID = {f"{w.name}-{a}-{b}": (w, a, b) for w, a, b in SMALL}
+assert len(BY_ID) == len(SMALL)
+CENTRE = ["grid8_fp32-raster-random", "ragged-random-block_morton", "gqa4x2-random-block_morton",
+          "mqa_f32-raster-random"]
+assert any(BY_ID[n][0].kv_heads < BY_ID[n][0].H for n in CENTRE)
+
+
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
     if not torch.cuda.is_available():
@@ -70,7 +77,7 @@ def test_repack_permutes_output_bitwise(w, a, b):
 
 def test_deterministic_replay():
     import geometry_aware_sparse_amd as gas
-    w = SMALL[4][0]
+    w = BY_ID["ragged-random-block_morton"][0]
     fields = pi.make_fields(w)
     coords = pi.packing_coords(w.grid, "random", seed=3)
     q, k, v, g = pi.pack_fields(fields, coords, w.grid)
@@ -82,6 +89,6 @@ def test_deterministic_replay():
     assert torch.equal(o1, o2)
 
 
-@pytest.mark.parametrize("w,a,b", [SMALL[1], SMALL[4]], ids=["grid8-centre", "ragged-centre"])
-def test_repack_permutes_output_bitwise_summary_centre(w, a, b):
-    _check(w, a, b, centre=True)
+@pytest.mark.parametrize("name", CENTRE)
+def test_repack_permutes_output_bitwise_summary_centre(name):
+    _check(*BY_ID[name], centre=True)

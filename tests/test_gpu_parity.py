@@ -39,6 +39,45 @@ CASES = [
       Hkv=2),
 ]
 IDS = [c.name for c in CASES]
+BY_NAME = {c.name: c for c in CASES}
+assert len(BY_NAME) == len(CASES), "case names are unique"
+
+
+def _pick(*names):
+    """Cases by name, so inserting a case never shifts a cross-cutting list."""
+    return [BY_NAME[n] for n in names]
+
+
+def _ids(cases):
+    return [c.name for c in cases]
+
+
+# every summary-exclusion reading, crossed with fp32 and bf16, ragged grids,
+# partial blocks and grouped KV heads (fp32 GQA with three KV heads included)
+EXCLUSION_CASES = _pick("grid8_fp32", "ragged_bf16_d48", "partial_blocks_f32_d48",
+                        "gqa4x2_bf16_d48", "gqa6x3_f32_d24", "gqa8x2_bf16_d48")
+# bf16 with head dim 48 or 96 and no exclusion: the matrix-core global kernel
+MFMA_CASES = _pick("grid16_bf16", "ragged_bf16_d48", "ragged_bf16_d96", "single_site",
+                   "slab_z1_bf16_d48", "slab_y1_bf16_d96", "gqa4x2_bf16_d48", "mqa4_bf16_d96",
+                   "gqa8x2_bf16_d48")
+# summary-centre variant: even, odd and clipped block extents, fp32 and bf16
+# (both pooling kernels), grouped KV heads in both dtypes
+CENTRE_CASES = _pick("grid8_fp32", "grid16_bf16", "ragged_bf16_d48", "ragged_bf16_d96",
+                     "partial_blocks_f32_d48", "small_bf16_d12", "gqa4x2_bf16_d48",
+                     "gqa6x3_f32_d24", "gqa8x2_bf16_d48")
+# grouped KV heads proper: more query heads than KV heads in every entry
+GQA_CASES = _pick("gqa4x2_bf16_d48", "mqa4_bf16_d96", "gqa6x3_f32_d24", "gqa8x2_bf16_d48")
+
+# each list's defining property, checked when the module is imported
+assert all(c.kv_heads < c.H for c in GQA_CASES)
+assert {c.kv_heads for c in GQA_CASES} >= {1, 2, 3} and any(c.dtype == "f32" for c in GQA_CASES)
+assert any(c.H // c.kv_heads == 4 for c in GQA_CASES)
+assert all(c.dtype == "bf16" and c.D in (48, 96) for c in MFMA_CASES)
+assert any(c.kv_heads < c.H for c in MFMA_CASES)
+assert any(c.kv_heads < c.H and c.dtype == "f32" for c in EXCLUSION_CASES)
+assert any(c.kv_heads < c.H and c.dtype == "f32" for c in CENTRE_CASES)
+assert {c.dtype for c in CENTRE_CASES} == {"f32", "bf16"}
+assert {c.dtype for c in EXCLUSION_CASES} == {"f32", "bf16"}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -177,8 +216,7 @@ def test_forward(w):
 
 
 @pytest.mark.parametrize("mode", [1, 2], ids=["own_block", "neighbourhood_blocks"])
-@pytest.mark.parametrize("w", [CASES[0], CASES[2], CASES[4], CASES[9], CASES[11]],
-                         ids=[IDS[0], IDS[2], IDS[4], IDS[9], IDS[11]])
+@pytest.mark.parametrize("w", EXCLUSION_CASES, ids=_ids(EXCLUSION_CASES))
 def test_global_exclusion_readings(w, mode):
     import geometry_aware_sparse_amd as gas
     coords, q, k, v, g = inputs(w)
@@ -203,10 +241,7 @@ def test_all_summaries_excluded_gives_local_only_mix():
     assert torch.count_nonzero(og).item() == 0
 
 
-MFMA_CASES = [CASES[1], CASES[2], CASES[3], CASES[8], CASES[9], CASES[10], CASES[12]]
-
-
-@pytest.mark.parametrize("w", MFMA_CASES, ids=[c.name for c in MFMA_CASES])
+@pytest.mark.parametrize("w", MFMA_CASES, ids=_ids(MFMA_CASES))
 def test_global_exact_softmax_flag(w):
     """Every query through the two-pass softmax (maximum first) matches the
     oracle, and so does the default path."""
@@ -240,7 +275,7 @@ def test_global_overflowing_scores_fall_back_per_query():
     two-pass row bit for bit; ordinary rows keep the one-pass result; nothing
     is non-finite."""
     import geometry_aware_sparse_amd as gas
-    w = CASES[2]
+    w = BY_NAME["ragged_bf16_d48"]
     coords, q, k, v, g = inputs(w)
     big = np.zeros(w.N, bool)
     big[::7] = True
@@ -272,7 +307,6 @@ def test_global_overflowing_scores_fall_back_per_query():
 # Summary-centre variant (paper summary §B.7, §B.8): keys pooled unrotated,
 # the mean rotated once at the block centre. Cases with even, odd and clipped
 # block extents, fp32 and bf16 (both pooling kernels).
-CENTRE_CASES = [CASES[0], CASES[1], CASES[2], CASES[3], CASES[4], CASES[5], CASES[9], CASES[11]]
 
 
 def _centre_pair(w):
@@ -285,7 +319,7 @@ def _centre_pair(w):
     return d, od
 
 
-@pytest.mark.parametrize("w", CENTRE_CASES, ids=[c.name for c in CENTRE_CASES])
+@pytest.mark.parametrize("w", CENTRE_CASES, ids=_ids(CENTRE_CASES))
 def test_block_summarize_centre(w):
     import geometry_aware_sparse_amd as gas
     coords, q, k, v, g = inputs(w)
@@ -305,7 +339,7 @@ def test_block_summarize_centre(w):
         assert not torch.equal(ks, ks_t)
 
 
-@pytest.mark.parametrize("w", CENTRE_CASES, ids=[c.name for c in CENTRE_CASES])
+@pytest.mark.parametrize("w", CENTRE_CASES, ids=_ids(CENTRE_CASES))
 def test_forward_centre(w):
     import geometry_aware_sparse_amd as gas
     coords, q, k, v, g = inputs(w)
@@ -317,10 +351,7 @@ def test_forward_centre(w):
     assert_close(w, host(o), ref, "centre forward")
 
 
-GQA_CASES = [CASES[9], CASES[10], CASES[11], CASES[12]]
-
-
-@pytest.mark.parametrize("w", GQA_CASES, ids=[c.name for c in GQA_CASES])
+@pytest.mark.parametrize("w", GQA_CASES, ids=_ids(GQA_CASES))
 @pytest.mark.parametrize("centre", [False, True], ids=["token", "centre"])
 def test_gqa_equals_mha_over_repeated_kv_bitwise(w, centre):
     """GQA through the library gives the same bits as multi-head attention

@@ -15,7 +15,7 @@ import pytest
 import oracle
 import pack3d_inputs as pi
 from refs import (block_ids, chebyshev_mask, dense_masked_attention, rotate_all, rotation,
-                  torch_sdpa)
+                  sequence_rotate_all, torch_sdpa)
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
                    "pack3d_oracle.c")
@@ -33,6 +33,13 @@ def _setup(grid=(4, 5, 6), block=(2, 2, 2), B=1, H=2, D=12, kind="random"):
 def pin_rope():
     d, c, q, _, _, _ = _setup()
     return np.allclose(oracle.rope_axial(d, c, q), rotate_all(c, q), atol=1e-12)
+
+
+def pin_rope_sequence():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((2, 30, 2, 24))
+    d = oracle.make_desc(2, 30, 2, 24, (2, 3, 5), (2, 2, 2))
+    return np.allclose(oracle.rope_sequence(d, x), sequence_rotate_all(x), rtol=0, atol=1e-10)
 
 
 def pin_neighbours():
@@ -152,6 +159,10 @@ MUTANTS = [
     ("rope_frequency", "pow(d->rope_base, -2.0 * p / (double)da)", "pow(d->rope_base, -2.0 * p / (double)D)", pin_rope),
     ("rope_axis_chunk", "int c0 = a * da + 2 * p;", "int c0 = a * 2 + 2 * p * 3;", pin_rope),
     ("rope_coord_axis", "double phi = (double)coords[3 * i + a] * theta;", "double phi = (double)coords[3 * i + (2 - a)] * theta;", pin_rope),
+    ("seq_rope_exponent", "double theta = pow(d->rope_base, -2.0 * p / (double)D);", "double theta = pow(d->rope_base, -1.0 * p / (double)D);", pin_rope_sequence),
+    ("seq_rope_axis_exponent", "double theta = pow(d->rope_base, -2.0 * p / (double)D);", "double theta = pow(d->rope_base, -2.0 * p / (double)(D / 3));", pin_rope_sequence),
+    ("seq_rope_sin_sign", "yr[2 * p + 1] = x0 * sn + x1 * cs;", "yr[2 * p + 1] = -x0 * sn + x1 * cs;", pin_rope_sequence),
+    ("seq_rope_row_index", "double phi = (double)i * theta;", "double phi = (double)(row % d->N) * theta;", pin_rope_sequence),
     ("neighbour_offset", "*dx = k % 3 - 1;", "*dx = k % 3;", pin_neighbours),
     ("neighbour_edge_wrap", "if (z < 0 || y < 0 || x < 0 || z >= d->grid[0] || y >= d->grid[1] || x >= d->grid[2])\n    return -1;", "if (z < 0 || y < 0 || x < 0 || z >= d->grid[0] || y >= d->grid[1] || x >= d->grid[2])\n    return slot[site_of(d, (z + d->grid[0]) % d->grid[0], (y + d->grid[1]) % d->grid[1], (x + d->grid[2]) % d->grid[2])];", pin_neighbours),
     ("local_no_scale", "logit[k] = s * dot(", "logit[k] = dot(", pin_local),
@@ -174,7 +185,7 @@ MUTANTS = [
 
 
 def test_unmodified_oracle_passes_every_pin():
-    for f in (pin_rope, pin_neighbours, pin_local, pin_summaries, pin_global, pin_mix,
+    for f in (pin_rope, pin_rope_sequence, pin_neighbours, pin_local, pin_summaries, pin_global, pin_mix,
               pin_summary_centre, pin_gqa, pin_backward):
         assert f(), f.__name__
 

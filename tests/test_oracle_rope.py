@@ -3,13 +3,15 @@
 The rotation is checked against the matrix exponential of its generator (an
 independent construction), against R(0) = I, norm preservation and the
 displacement identity <R(a)q, R(b)k> = <q, R(b-a)k> (paper summary §B.2).
+The sequence-index control (paper summary §B.4) is checked the same way,
+against the matrix exponential of its 1-D generator at the packed index.
 """
 import numpy as np
 import pytest
 
 import oracle
 import pack3d_inputs as pi
-from refs import rotation, rotate_all
+from refs import rotation, rotate_all, sequence_rotate_all
 
 
 def _desc(grid, D, H=2, B=1):
@@ -84,3 +86,30 @@ def test_sequence_control_is_an_actual_rotation():
     # and it is a rotation at the packed index: position 0 is the identity
     assert np.array_equal(qs[0, 0], q[0, 0])
     assert np.allclose(np.linalg.norm(qs, axis=-1), np.linalg.norm(q, axis=-1))
+
+
+@pytest.mark.parametrize("D", [6, 24, 48])
+def test_sequence_control_matches_matrix_exponential(D):
+    # 1-D RoPE at the packed index i over all D channels, theta_p = base^(-2p/D):
+    # the rotation of a generator that carries the index, built independently
+    N, H, B = 40, 2, 2
+    rng = np.random.default_rng(30 + D)
+    x = rng.standard_normal((B, N, H, D))
+    d = oracle.make_desc(B, N, H, D, (2, 4, 5), (2, 2, 2))
+    # expm of angles up to N rad carries ~1e-12 of its own error
+    assert np.allclose(oracle.rope_sequence(d, x), sequence_rotate_all(x), rtol=0, atol=1e-10)
+
+
+def test_sequence_control_relative_offset():
+    # the 1-D rotation is relative in the packed index: <R(i)q, R(j)k> depends
+    # on j - i only, so two pairs with the same index gap give the same logit
+    D, N = 24, 64
+    rng = np.random.default_rng(31)
+    q, k = rng.standard_normal(D), rng.standard_normal(D)
+    x = np.zeros((1, N, 2, D))
+    x[0, :, 0] = q
+    x[0, :, 1] = k
+    d = oracle.make_desc(1, N, 2, D, (4, 4, 4), (2, 2, 2))
+    y = oracle.rope_sequence(d, x)[0]
+    for i, j in [(0, 5), (17, 22), (58, 63)]:
+        assert abs(y[i, 0] @ y[j, 1] - y[0, 0] @ y[5, 1]) < 1e-10
