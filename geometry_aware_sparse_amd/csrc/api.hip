@@ -272,6 +272,16 @@ int forward_impl(const pack3d_desc *desc, const int32_t *coords, const void *q, 
   if ((rc = mark(6))) return rc;
   if ((rc = hip_status(launch_local(g, desc->dtype, geom, q, k, v, gate, oglob, o, s, &ok)))) return rc;
   if (!ok) return PACK3D_ERR_UNSUPPORTED;
+  if (oglob != o) {
+    // training: the global branch wrote into the saved buffer, so the rows of
+    // o that the local kernel does not reach (tokens taking no part) are
+    // zeroed here, as the global kernel zeroes them in the inference forward
+    void *rows[4] = {o, nullptr, nullptr, nullptr};
+    const int len[4] = {g.H * g.D, 0, 0, 0};
+    if ((rc = hip_status(launch_zero_absent(g, (int)elem_size(desc->dtype), geom, coords, rows,
+                                            len, s))))
+      return rc;
+  }
   return mark(7);
 }
 

@@ -609,9 +609,15 @@ hipError_t run_backward_t(const Geo &g, const BwdArgs &a, hipStream_t s) {
     if (a.events[4])
       if (hipError_t e = hipEventRecord(static_cast<hipEvent_t>(a.events[4]), s)) return e;
   }
-  if (bwd_local_pair_supported(g, sizeof(T) == 2 ? PACK3D_BF16 : PACK3D_F32))
-    return launch_bwd_local_pair(g, a, s);
-  return run_local_bwd_valu<T, D, TZ, TY, TX>(g, a, s);
+  if (hipError_t e = bwd_local_pair_supported(g, sizeof(T) == 2 ? PACK3D_BF16 : PACK3D_F32)
+                         ? launch_bwd_local_pair(g, a, s)
+                         : run_local_bwd_valu<T, D, TZ, TY, TX>(g, a, s))
+    return e;
+  // the kernels above reach tokens through the slot map only: the gradient
+  // rows of a token that takes no part are zero
+  void *rows[4] = {a.dq, a.dk, a.dv, a.dgate};
+  const int len[4] = {g.H * g.D, g.Hkv * g.D, g.Hkv * g.D, g.H};
+  return launch_zero_absent(g, (int)sizeof(T), a.geom, a.coords, rows, len, s);
 }
 
 }  // namespace

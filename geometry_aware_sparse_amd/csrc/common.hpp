@@ -94,6 +94,14 @@ __device__ __forceinline__ void rotate(float &x0, float &x1, float2 cs) {
 __device__ __forceinline__ int site_of(const Geo &g, int z, int y, int x) {
   return (z * g.Y + y) * g.X + x;
 }
+// Whether the token at memory position i, with coordinate (z, y, x), takes
+// part: its coordinate is on the grid and its site's slot names it (a
+// repeated coordinate leaves every token but the lowest index out).
+__device__ __forceinline__ bool takes_part(const Geo &g, const int32_t *slot, int i, int z, int y,
+                                           int x) {
+  if (z < 0 || y < 0 || x < 0 || z >= g.Z || y >= g.Y || x >= g.X) return false;
+  return slot[site_of(g, z, y, x)] == i;
+}
 __device__ __forceinline__ int block_of(const Geo &g, int z, int y, int x) {
   return ((z / g.bz) * g.My + (y / g.by)) * g.Mx + (x / g.bx);
 }

@@ -131,8 +131,9 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
 
   // Query fragments: lane holds channels 16c + 8*hi .. +7 of its query,
   // rotated at the token's own coordinate, scaled, rounded to bf16. A token
-  // whose coordinate is off the grid takes no part (zero query, zero output
-  // row; only reachable without PACK3D_VALIDATE).
+  // whose coordinate is off the grid, or whose site went to a lower memory
+  // index, takes no part (zero query, zero output row; only reachable without
+  // PACK3D_VALIDATE).
   bf16x8 qf[G][KD];
   bool active[G], cok[G];
   int qi[G];
@@ -149,8 +150,7 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
         c3[0] = coords[3 * (int64_t)qi[gi]];
         c3[1] = coords[3 * (int64_t)qi[gi] + 1];
         c3[2] = coords[3 * (int64_t)qi[gi] + 2];
-        cok[gi] = c3[0] >= 0 && c3[1] >= 0 && c3[2] >= 0 && c3[0] < g.Z && c3[1] < g.Y &&
-                  c3[2] < g.X;
+        cok[gi] = takes_part(g, slot_map(geom, g), qi[gi], c3[0], c3[1], c3[2]);
         if (!cok[gi]) c3[0] = c3[1] = c3[2] = 0;
       }
       const int64_t off = (((int64_t)b * g.N + qi[gi]) * g.H + h) * D;

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(kNT) void k_global_valu(Geo g, const void *geom,
   const int h = bh % g.H, b = bh / g.H;
   const int i = tile * kNT + threadIdx.x;
   const bool active = i < g.N;
-  bool cok = false;  // off-grid coordinate: zero query, zero output row
+  bool cok = false;  // a token that takes no part: zero query, zero output row
   const float2 *tab = rope_table(geom, g);
   const int Mp = (g.M + 31) / 32 * 32;
   const int64_t bk = (int64_t)b * g.Hkv + h / g.G;           // the KV head query head h reads
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kNT) void k_global_valu(Geo g, const void *geom,
     c3[0] = coords[3 * (int64_t)i];
     c3[1] = coords[3 * (int64_t)i + 1];
     c3[2] = coords[3 * (int64_t)i + 2];
-    cok = c3[0] >= 0 && c3[1] >= 0 && c3[2] >= 0 && c3[0] < g.Z && c3[1] < g.Y && c3[2] < g.X;
+    cok = takes_part(g, slot_map(geom, g), i, c3[0], c3[1], c3[2]);
   }
   if (cok) {
     const int64_t off = (((int64_t)b * g.N + i) * g.H + h) * D;

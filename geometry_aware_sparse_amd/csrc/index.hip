@@ -25,7 +25,10 @@ __global__ void k_geom_init(Geo g, int32_t *status, int32_t *slot, float2 *tab) 
 }
 
 // slot[site(c_i)] = i; bit 0 of the status word marks an off-grid
-// coordinate, bit 1 a site claimed twice (the first claim stays).
+// coordinate, bit 1 a site claimed twice. A site claimed by several tokens
+// keeps the lowest memory index whatever order the claims arrive in: the
+// empty slot (-1) is the largest value as an unsigned word, so an unsigned
+// atomic minimum takes the first claim and every lower index after it.
 __global__ void k_geom_scatter(Geo g, const int32_t *coords, int32_t *status, int32_t *slot) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= g.N) return;
@@ -34,8 +37,8 @@ __global__ void k_geom_scatter(Geo g, const int32_t *coords, int32_t *status, in
     atomicOr(status, 1);
     return;
   }
-  int old = atomicCAS(&slot[site_of(g, z, y, x)], -1, i);
-  if (old != -1) atomicOr(status, 2);
+  unsigned old = atomicMin(reinterpret_cast<unsigned *>(&slot[site_of(g, z, y, x)]), (unsigned)i);
+  if (old != 0xFFFFFFFFu) atomicOr(status, 2);
 }
 
 __global__ void k_geom_export(Geo g, const int32_t *coords, const int32_t *slot, int32_t *nbr,
@@ -53,6 +56,35 @@ __global__ void k_geom_export(Geo g, const int32_t *coords, const int32_t *slot,
       nbr[(int64_t)i * 27 + k] = ok ? slot[site_of(g, zz, yy, xx)] : -1;
     }
   }
+}
+
+// Zeroes, for every token that takes no part (coordinate off the grid, or a
+// site that went to a lower memory index), its row in each of up to four
+// [B, N, len] tensors of es-byte elements (a null pointer is skipped). The
+// kernels that reach tokens through the slot map never write those rows.
+__global__ void k_zero_absent(Geo g, const void *geom, const int32_t *__restrict__ coords,
+                              char *r0, char *r1, char *r2, char *r3, int b0, int b1, int b2,
+                              int b3) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (int64_t)g.B * g.N) return;
+  const int i = (int)(t % g.N);
+  const int z = coords[3 * (int64_t)i], y = coords[3 * (int64_t)i + 1], x = coords[3 * (int64_t)i + 2];
+  if (takes_part(g, slot_map(geom, g), i, z, y, x)) return;
+  char *rows[4] = {r0, r1, r2, r3};
+  const int bytes[4] = {b0, b1, b2, b3};
+  for (int k = 0; k < 4; k++)
+    if (rows[k])
+      for (int e = 0; e < bytes[k]; e++) rows[k][t * bytes[k] + e] = 0;
+}
+
+hipError_t launch_zero_absent(const Geo &g, int es, const void *geom, const int32_t *coords,
+                              void *const *rows, const int *len, hipStream_t s) {
+  const int64_t n = (int64_t)g.B * g.N;
+  hipLaunchKernelGGL(k_zero_absent, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, g, geom,
+                     coords, static_cast<char *>(rows[0]), static_cast<char *>(rows[1]),
+                     static_cast<char *>(rows[2]), static_cast<char *>(rows[3]), len[0] * es,
+                     len[1] * es, len[2] * es, len[3] * es);
+  return hipGetLastError();
 }
 
 hipError_t launch_index(const Geo &g, const int32_t *coords, void *geom, int32_t *nbr,

@@ -9,6 +9,10 @@ namespace pk {
 
 hipError_t launch_index(const Geo &g, const int32_t *coords, void *geom, int32_t *nbr,
                         int32_t *blk, int32_t *rank, hipStream_t s);
+// Zeroes the rows of tokens that take no part in up to four [B, N, len[k]]
+// tensors of es-byte elements (null entries skipped).
+hipError_t launch_zero_absent(const Geo &g, int es, const void *geom, const int32_t *coords,
+                              void *const *rows, const int *len, hipStream_t s);
 hipError_t launch_rope(const Geo &g, int dtype, const int32_t *coords, const void *x, void *y,
                        hipStream_t s);
 hipError_t launch_summarize(const Geo &g, int dtype, const void *geom, const void *k,

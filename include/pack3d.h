@@ -51,9 +51,18 @@
  *  - Return value: PACK3D_OK or a negative pack3d_status. Argument checks run
  *    on the host before anything is enqueued; nothing is launched when they
  *    fail. Coordinate errors are detected on the device: kernels never read
- *    out of bounds (an off-grid or empty site simply takes no part), and the
- *    error is reported to the host only when desc->flags has PACK3D_VALIDATE
- *    (the call then synchronises the stream).
+ *    out of bounds, and the error is reported to the host only when
+ *    desc->flags has PACK3D_VALIDATE (the call then synchronises the stream).
+ *  - Without PACK3D_VALIDATE a bad coordinate is resolved deterministically.
+ *    A token whose coordinate is off the grid takes no part. A site claimed
+ *    by several tokens goes to the lowest memory index among them, and the
+ *    others take no part. A token that takes no part is nobody's neighbour
+ *    and no block's member; its output row from pack3d_global_attn,
+ *    pack3d_forward and pack3d_forward_train is zero, its saved log-sum-exp
+ *    is -inf, and its dq, dk, dv and dgate rows from pack3d_backward are
+ *    zero. pack3d_local_attn visits grid sites only, so it leaves that row of
+ *    o_local unwritten. A grid site with no token is skipped by every
+ *    kernel.
  *
  * Readings taken where the pages are silent (their formulas did not survive):
  * RoPE channels are three contiguous chunks of D/3 for z, y, x; plane p of a
@@ -145,7 +154,9 @@ int64_t pack3d_num_summaries(const pack3d_desc *desc);
  *   [0, 256)               int32 status word (bit 0: coordinate off the grid,
  *                          bit 1: coordinate duplicated), then padding
  *   [slot_offset, ...)     int32 slot map [Z*Y*X]: slot[(z*Y + y)*X + x] =
- *                          memory position of the token at (z,y,x), -1 if none
+ *                          memory position of the token at (z,y,x) (the
+ *                          lowest one when several claim the site), -1 if
+ *                          none
  *   [table_offset, ...)    float32 RoPE table [(Z+Y+X+1) * (D/6)][2]: entry
  *                          (axis_start + c)*(D/6) + p holds (cos, sin) of
  *                          c * base^(-2p/(D/3)), evaluated in double and
@@ -223,10 +234,14 @@ int pack3d_mix(const pack3d_desc *desc, const void *gate, const void *o_local,
  * k_sum and v_sum, each 256-byte aligned. */
 int pack3d_workspace_bytes(const pack3d_desc *desc, size_t *bytes);
 
-/* The whole forward, stream-ordered: index build, summaries, global branch
- * (written into o), then local branch fused with the mix (reads o, writes
- * o). Equivalent to the staged calls above; o must not alias q, k, v or
- * gate. ws: device workspace of at least pack3d_workspace_bytes bytes
+/* The whole PACK3D operator (project page Ch. 3, Contracts 1-3 and "Rotate
+ * first, then pool"; paper summary §3.2, §3.3, §3.5): for each token i and
+ * head h, O = (1-g)*O_local + g*O_global with g = sigmoid(gate), where the
+ * two branches are those of pack3d_local_attn and pack3d_global_attn over the
+ * summaries of pack3d_block_summarize, all from UNROTATED q and k. Stream-
+ * ordered: index build, summaries, global branch (written into o), then
+ * local branch fused with the mix (reads o, writes o). Equivalent to the
+ * staged calls above; o must not alias q, k, v or gate. ws: device workspace of at least pack3d_workspace_bytes bytes
  * (ws_bytes says how large it is). stage_events: NULL, or an array of
  * 2*PACK3D_NUM_STAGES hipEvent_t (as void*) that are recorded on stream
  * before and after each stage (index, summarize, global, local+mix), for

@@ -65,6 +65,45 @@ def test_validate_reports_coordinate_errors(w, kind, bit):
 
 
 @pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
+def test_repeated_coordinate_lowest_index_wins(w):
+    """Without validation a site claimed twice goes to the lowest memory index,
+    whatever order the claims arrive in, and the other token takes no part:
+    its output and gradient rows are zero, and the whole result is bit for bit
+    that of the same tokens with the loser moved off the grid."""
+    import geometry_aware_sparse_amd as gas
+    coords, q, k, v, g = inputs(w)
+    dup = _bad(coords, "duplicate")         # token 5 takes token 9's site
+    off = dup.copy()
+    off[9] = [off[9][0], off[9][1], 10_000]  # the same, with token 9 off the grid
+    dt = tdtype(w)
+    dn, _ = desc_pair(w)
+    vals = [to_dev(x, dt) for x in (q, k, v, g)]
+    dout = to_dev(pi.pack_fields((pi.make_dout(w),), coords, w.grid)[0], dt)
+    results = []
+    for c in (dup, off, dup):
+        dc = to_dev(c, torch.int32)
+        geom, _, _, _ = gas.pack3d_index_build(dn, dc)
+        slot = gas.slot_map_view(dn, geom).cpu().numpy()
+        o, saved = gas.pack3d_forward_train(dn, dc, *vals)
+        grads = gas.pack3d_backward(dn, dc, *vals, saved, dout)
+        torch.cuda.synchronize()
+        results.append((slot, o, grads))
+    Z, Y, X = w.grid
+    z, y, x = coords[9]
+    assert results[0][0][(z * Y + y) * X + x] == 5
+    assert np.array_equal(results[0][0], results[1][0])
+    for slot, o, grads in results:
+        assert torch.count_nonzero(o[:, 9]).item() == 0
+        for gr in grads:
+            assert torch.count_nonzero(gr[:, 9]).item() == 0
+        assert torch.isfinite(o.float()).all()
+    for a, b in ((results[0], results[1]), (results[0], results[2])):
+        assert torch.equal(a[1], b[1])
+        for ga, gb in zip(a[2], b[2]):
+            assert torch.equal(ga, gb)
+
+
+@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
 def test_validate_passes_valid_coordinates(w):
     import geometry_aware_sparse_amd as gas
     coords, q, k, v, g = inputs(w)
