@@ -15,6 +15,7 @@ PACK3D_EXACT_SOFTMAX = 0x2
 PACK3D_SUMMARY_CENTRE = 0x4
 PACK3D_NUM_STAGES = 4
 PACK3D_NUM_BWD_STAGES = 3
+PACK3D_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 STATUS = {0: "PACK3D_OK", -1: "PACK3D_ERR_INVALID_ARG", -2: "PACK3D_ERR_SHAPE",
           -3: "PACK3D_ERR_WORKSPACE", -4: "PACK3D_ERR_UNSUPPORTED", -5: "PACK3D_ERR_HIP",
@@ -56,6 +57,7 @@ _SIGS = {
     "pack3d_mix": (C.c_int, [_P, _P, _P, _P, _P, _P]),
     "pack3d_workspace_bytes": (C.c_int, [_P, C.POINTER(C.c_size_t)]),
     "pack3d_forward": (C.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P, _P]),
+    "pack3d_forward_noalloc": (C.c_int, [_P, _P, _P, _P, _P, _P, _P, _P]),
     "pack3d_saved_bytes": (C.c_int, [_P, C.POINTER(C.c_size_t)]),
     "pack3d_forward_train": (C.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P, C.c_size_t,
                                        _P, _P]),

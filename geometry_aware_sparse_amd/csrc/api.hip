@@ -3,6 +3,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string.h>
 
 #include "launch.hpp"
@@ -348,6 +349,66 @@ int pack3d_forward(const pack3d_desc *desc, const int32_t *coords, const void *q
                    void *stream, void *const *stage_events) {
   return forward_impl(desc, coords, q, k, v, gate, o, o, nullptr, ws, ws_bytes, stream,
                       stage_events);
+}
+
+}  // extern "C"
+
+// Scratch of pack3d_forward_noalloc: the forward's workspace (geometry
+// metadata, k_sum, v_sum) in a device array of fixed size, one copy per GPU,
+// held until the process ends. In host code `scratch` names a host-side
+// stand-in, never the device memory: its address on a device is taken once
+// per device with hipGetSymbolAddress (that device current) and only that
+// address is handed to kernels.
+static __device__ __align__(256) char scratch[PACK3D_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag scratch_once[kMaxDevices];
+void *scratch_ptr[kMaxDevices];
+hipError_t scratch_err[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up on the
+// first call there.
+int device_scratch(hipStream_t s, void **ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PACK3D_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return PACK3D_ERR_UNSUPPORTED;
+  if (s) {  // the stream must belong to the current device
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess) return PACK3D_ERR_HIP;
+    if (sdev != dev) return PACK3D_ERR_INVALID_ARG;
+  }
+  std::call_once(scratch_once[dev], [dev] {
+    void *p = nullptr;
+    scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    scratch_ptr[dev] = scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (scratch_err[dev] != hipSuccess || !scratch_ptr[dev]) return PACK3D_ERR_HIP;
+  *ptr = scratch_ptr[dev];
+  return PACK3D_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pack3d_forward_noalloc(const pack3d_desc *desc, const int32_t *coords, const void *q,
+                           const void *k, const void *v, const void *gate, void *o,
+                           void *stream) {
+  size_t need = 0;
+  int rc = pack3d_workspace_bytes(desc, &need);
+  if (rc) return rc;
+  if (need > (size_t)PACK3D_NOALLOC_SCRATCH_BYTES) return PACK3D_ERR_WORKSPACE;
+  if (!coords || !q || !k || !v || !gate || !o) return PACK3D_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void *ws = nullptr;
+  if ((rc = device_scratch(s, &ws))) return rc;
+  // every byte the forward reads from its workspace is written by it first
+  // (status word, slot map, RoPE table, summaries with their padding), so
+  // nothing left by an earlier call needs clearing
+  return forward_impl(desc, coords, q, k, v, gate, o, o, nullptr, ws,
+                      (size_t)PACK3D_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int pack3d_saved_bytes(const pack3d_desc *desc, size_t *bytes) {

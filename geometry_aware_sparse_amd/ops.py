@@ -251,6 +251,21 @@ def pack3d_forward(desc, coords, q, k, v, gate, out=None, workspace=None, stage_
     return out
 
 
+def pack3d_forward_noalloc(desc, coords, q, k, v, gate, out):
+    """The whole operator with the library's own per-GPU scratch array as the
+    workspace: the C call allocates nothing (out is the caller's)."""
+    _need(coords, "coords", desc, (desc.N, 3), torch.int32)
+    _need(q, "q", desc, _bnhd(desc))
+    _need(k, "k", desc, _bnkd(desc))
+    _need(v, "v", desc, _bnkd(desc))
+    _need(gate, "gate", desc, (desc.B, desc.N, desc.H))
+    _need(out, "out", desc, _bnhd(desc))
+    _check(library().pack3d_forward_noalloc(C.byref(desc), _ptr(coords), _ptr(q), _ptr(k),
+                                            _ptr(v), _ptr(gate), _ptr(out), _stream()),
+           "pack3d_forward_noalloc")
+    return out
+
+
 def _events(stage_events, n):
     if stage_events is None:
         return None

@@ -19,7 +19,8 @@
  * Conventions shared by every entry point
  *  - Pointers named q, k, v, gate, o, x, k_sum, v_sum, geom, coords, ws and
  *    the *_out arrays are DEVICE pointers owned by the caller; the library
- *    never allocates, frees or retains device memory.
+ *    never allocates, frees or retains device memory (pack3d_forward_noalloc
+ *    uses a fixed device array inside the library instead of a workspace).
  *  - Layouts (row-major, C order), with Hkv = desc->kv_heads (H when 0):
  *      q, o, o_local, o_global, x       : [B, N, H, D] in packed memory order
  *      k, v                             : [B, N, Hkv, D], same packing
@@ -47,7 +48,7 @@
  *  - stream is a hipStream_t passed as void* (NULL = default stream). Every
  *    call only enqueues work on it and returns; results are ready when the
  *    stream reaches that point. Calls are reentrant: the library keeps no
- *    mutable global state.
+ *    mutable global state, except pack3d_forward_noalloc's per-GPU array.
  *  - Return value: PACK3D_OK or a negative pack3d_status. Argument checks run
  *    on the host before anything is enqueued; nothing is launched when they
  *    fail. Coordinate errors are detected on the device: kernels never read
@@ -251,6 +252,23 @@ int pack3d_workspace_bytes(const pack3d_desc *desc, size_t *bytes);
 int pack3d_forward(const pack3d_desc *desc, const int32_t *coords, const void *q, const void *k,
                    const void *v, const void *gate, void *o, void *ws, size_t ws_bytes,
                    void *stream, void *const *stage_events);
+
+/* pack3d_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same operator, kernels and results (bit for bit) as pack3d_forward, but
+ * the workspace is a device array inside the library of
+ * PACK3D_NOALLOC_SCRATCH_BYTES bytes, one per GPU, kept until the process
+ * ends; the call itself allocates nothing. It runs on the current device, and
+ * stream (NULL = default stream) must belong to it (else
+ * PACK3D_ERR_INVALID_ARG). Returns PACK3D_ERR_WORKSPACE, with nothing
+ * launched, when pack3d_workspace_bytes(desc) exceeds the array. Every call
+ * on one GPU shares that GPU's array: calls that may overlap on one GPU
+ * (different streams, or host threads) race and must be serialised by the
+ * caller. The first call on a device looks up the array's device address. */
+#define PACK3D_NOALLOC_SCRATCH_BYTES (32u << 20)
+int pack3d_forward_noalloc(const pack3d_desc *desc, const int32_t *coords, const void *q,
+                           const void *k, const void *v, const void *gate, void *o,
+                           void *stream);
 
 /* ---------------------------------------------------------------------------
  * Training (paper summary §1, §3.4: the operator is trained end to end, with
