@@ -58,30 +58,6 @@ __device__ __forceinline__ int swap23(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
-// Scheduling hint for one pipeline step: a few vector instructions, then
-// the score products, each matrix instruction followed by PER vector
-// instructions (exp2 and bf16 packs), then the LDS reads of the next step's
-// key fragments, the value products interleaved the same way, and last the
-// reads of the next step's value fragments. A wave issues in order: the
-// vector work keeps it busy while its own products run, and every fragment
-// is read one product group ahead of its use, so no product waits on LDS.
-template <int NK, int NV, int NMK, int NMV, int NVA>
-__device__ __forceinline__ void sched_step() {
-  constexpr int NMF = NMK + NMV, PER = NVA / NMF, LEAD = NVA - NMF * PER;
-  if constexpr (LEAD > 0) __builtin_amdgcn_sched_group_barrier(0x002, LEAD, 0);
-#pragma unroll
-  for (int i = 0; i < NMK; i++) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x100, NK, 0);
-#pragma unroll
-  for (int i = 0; i < NMV; i++) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x100, NV, 0);
-}
 }  // namespace
 
 // G = 32-query groups per wave; TS = summaries per LDS tile.
@@ -285,10 +261,11 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
       }
     };
     // v_sum tile vt: LDS chunk (j8, d) = channel d of summaries 8*j8.. of the
-    // tile. Rows past D-1 repeat channel D-1 and only feed output rows that
-    // are dropped -- except row D when it carries the denominator: once a
-    // wave's loads have landed it overwrites row D of the groups it loaded
-    // with bf16 ones, before the barrier that publishes the tile.
+    // tile. Only rows d < D are loaded (the lanes of the other rows are
+    // masked off). Rows D.. of both buffers are written once, below, and
+    // never overwritten: all zeros, except row D when it carries the
+    // denominator (bf16 ones), so the padding output rows stay finite and
+    // the spare row sums the weights.
     static_assert(!ONES || VPARTS == 1, "the denominator row is in the first part");
     auto issue_v = [&](int vt, bf16x8 *dV) {
       const int g8base = 4 * (vt * NSUB - 2);
@@ -298,26 +275,25 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
         const int j8 = i / VPARTS, part = i % VPARTS;
         const int d = part * 64 + lane;
         const int g8 = min(max(g8base + j8, 0), 4 * M32 - 1);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)&dV[j8 * VROWS + part * 64], 16,
-                                                 (uint32_t)((g8 * D + min(d, D - 1)) * 16), 0, 0,
-                                                 0);
+        if (part * 64 + 64 <= D || d < D)  // the first test is known at compile time
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)&dV[j8 * VROWS + part * 64], 16,
+                                                   (uint32_t)((g8 * D + d) * 16), 0, 0, 0);
       }
     };
-    // after this wave's loads landed: row D of its groups j8 = wv + kWaves*r
-    // (every lane writes; lanes that share a group write the same value)
-    auto ones_rows = [&](bf16x8 *dV) {
-      if constexpr (ONES) {
-        bf16x8 one8;
+    {
+      constexpr int NCR = VROWS - D;  // constant rows per 8-summary group
+      for (int e = threadIdx.x; e < 2 * NJ8 * NCR; e += 256) {
+        const int buf = e / (NJ8 * NCR), j8 = (e / NCR) % NJ8, row = D + e % NCR;
+        bf16x8 c;
 #pragma unroll
-        for (int e = 0; e < 8; e++) one8[e] = (bf16)1.0f;
-        dV[(wv + kWaves * (lane % (NVI / kWaves))) * VROWS + D] = one8;
+        for (int u = 0; u < 8; u++) c[u] = (bf16)((ONES && row == D) ? 1.0f : 0.0f);
+        (buf ? sV1 : sV0)[j8 * VROWS + row] = c;
       }
-    };
+    }
 
     issue_k(0, sK0);
     issue_v(0, sV1);  // sub-tiles -2 .. NSUB-3 (only 0, 1 exist for NSUB = 4)
     __builtin_amdgcn_s_waitcnt(0);
-    ones_rows(sV1);
     __syncthreads();
     issue_k(1, sK1);
     issue_v(1, sV0);
@@ -346,7 +322,6 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
     // this is a tile-switch step like the ones in the loop.
     if constexpr (NSUB == 2) {
       __builtin_amdgcn_s_waitcnt(0);
-      ones_rows(sV0);
       __syncthreads();
       issue_k(2, sK0);
       issue_v(2, sV1);
@@ -369,9 +344,12 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
       const bf16x8 *nK = KB ? sK1 : sK0;
       bf16x8 *nV = VB ? sV1 : sV0;
       const int j = 2 * NSUB * it + JJ;
+      // each step is its own scheduling region: the compiler may not pull the
+      // next step's exp2 of the scores just issued into this one, where it
+      // would wait for those products to drain
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (POS == 0) {
         __builtin_amdgcn_s_waitcnt(0);  // this wave's loads landed, LDS reads done
-        ones_rows(nV);
         __syncthreads();
         issue_k(2 * it + KT + 1, KB ? sK0 : sK1);
         issue_v(2 * it + KT + 1, KB ? sV1 : sV0);
@@ -394,7 +372,7 @@ __global__ __launch_bounds__(256, 2) void k_global_mfma(
             acc[gi][t] =
                 __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t][c2], pf[P][gi][c2], acc[gi][t], 0, 0, 0);
       read_v(nV, POS);  // sub-tile j+1, for the next step
-      sched_step<KD, 2 * DT, G * KD, G * 2 * DT, G * (ONES ? 24 : 32)>();
+      __builtin_amdgcn_sched_barrier(0);
     };
     // Iterations before IT_CLEAN only see sub-tiles that lie wholly below M,
     // so their steps carry no mask (and no branch that would split a step's

@@ -261,20 +261,20 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX, D == 96 ? 4 : 1) void k_loca
   // workgroup); a query site off the grid stores nothing
   const float qscale = g.scale * kLog2e;
 
-  // qv[a][d + 1]: the query slice of axis a rotated by the relative angle of
-  // a neighbour at offset d along a, R(-d theta), scaled and rounded to bf16
+  // qv[a][d + 1]: the query slice of axis a, scaled, rotated by the relative
+  // angle of a neighbour at offset d along a, R(-d theta), rounded to bf16
   bf16x2 qv[3][3][4];
 #pragma unroll
   for (int a = 0; a < 3; a++)
 #pragma unroll
     for (int u = 0; u < 4; u++) {
-      const float x0v = (float)qraw[a][2 * u], x1v = (float)qraw[a][2 * u + 1];
+      const float x0v = (float)qraw[a][2 * u] * qscale, x1v = (float)qraw[a][2 * u + 1] * qscale;
 #pragma unroll
       for (int d = -1; d <= 1; d++) {
         float y0 = x0v, y1 = x1v;
         if (d != 0) rotate(y0, y1, make_float2(cs1[a][u].x, d > 0 ? -cs1[a][u].y : cs1[a][u].y));
-        qv[a][d + 1][u][0] = (bf16)(y0 * qscale);
-        qv[a][d + 1][u][1] = (bf16)(y1 * qscale);
+        qv[a][d + 1][u][0] = (bf16)y0;
+        qv[a][d + 1][u][1] = (bf16)y1;
       }
     }
 
