@@ -51,6 +51,9 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 
+// Byte offset, in the geometry buffer's header, of 64 zero bytes.
+constexpr int kZeroOff = 64;
+
 __device__ __forceinline__ const int32_t *slot_map(const void *geom, const Geo &g) {
   return reinterpret_cast<const int32_t *>(static_cast<const char *>(geom) + g.slot_off);
 }

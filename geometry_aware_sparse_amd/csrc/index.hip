@@ -13,6 +13,7 @@ __global__ void k_geom_init(Geo g, int32_t *status, int32_t *slot, float2 *tab) 
   int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int64_t S = (int64_t)g.Z * g.Y * g.X;
   if (t == 0) status[0] = 0;
+  if (t < 16) status[kZeroOff / 4 + t] = 0;  // the header's zero bytes
   if (t < S) slot[t] = -1;
   const int rows = g.Z + g.Y + g.X;
   int64_t T = (int64_t)(rows + 1) * g.P;

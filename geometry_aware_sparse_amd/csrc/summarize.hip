@@ -173,21 +173,29 @@ __global__ __launch_bounds__(512) void k_summarize(Geo g, const void *geom, cons
 }
 
 // bf16 rows whose head dim is a multiple of 8: the same summaries (same
-// members, same order, same fp32 arithmetic), arranged so that memory
-// latency is paid a few times per workgroup instead of once per member.
+// members, same order, fp32 sums; the rotation is folded into the sums'
+// fused multiply-adds, so the last bits may differ from k_summarize),
+// arranged so that memory latency is paid a few times per workgroup instead
+// of once per member.
 //   1. The members' slots and the RoPE rows of the 8 blocks' coordinate
 //      ranges are staged in LDS (one round of loads, one barrier).
 //   2. A thread owns one block and one 16-byte chunk of the token row; it
-//      issues the K and V loads of up to 8 members at once, then adds them
-//      up in within-block-slot order. A member that is absent reads token 0
-//      and contributes +0 through a select, which leaves the sum unchanged
-//      bit for bit.
-//   3. The value means are transposed through LDS with an odd row pitch, so
+//      issues the K and V loads of kBatch members at once, then adds them
+//      up in within-block-slot order: keys through fused multiply-adds with
+//      their (cos, sin), values through v_dot2 with weights (1, 0), (0, 1).
+//      A member that is absent reads a zero chunk of the geometry buffer
+//      instead, so it contributes exact zeros with no select.
+//   3. The means take one reciprocal per block and a residual correction.
+//   4. The value means are transposed through LDS with an odd row pitch, so
 //      the writes of a wave fall in distinct banks.
-constexpr int kBatch = 8;  // members whose loads are in flight together
+// Members whose loads are in flight together. Four, with five waves per
+// SIMD asked of the compiler (93 VGPRs): three 6-wave workgroups share a CU
+// instead of two, and the 65,536-token volume's pass takes 24.7 us instead
+// of 29.0 us with eight members at 122 VGPRs.
+constexpr int kBatch = 4;
 
 template <bool CENTRE>
-__global__ __launch_bounds__(512) void k_summarize_b8(Geo g, const void *geom, const bf16 *k,
+__global__ __launch_bounds__(512, 5) void k_summarize_b8(Geo g, const void *geom, const bf16 *k,
                                                        const bf16 *v, bf16 *ks, bf16 *vsb,
                                                        int nrow) {
   extern __shared__ float s_dyn[];
@@ -245,6 +253,17 @@ __global__ __launch_bounds__(512) void k_summarize_b8(Geo g, const void *geom, c
     for (int ss = 0; ss < 8; ss++) s_cs[(ss * nrow + row) * P + pp] = cs[ss];
   }
   const int rowbase = a == 0 ? 0 : (a == 1 ? g.bz : g.bz + g.by);
+  // an absent member reads this 16-byte zero chunk of the geometry buffer
+  // instead of a token, so its terms are exact zeros without a select
+  const bf16 *zero16 = reinterpret_cast<const bf16 *>(static_cast<const char *>(geom) + kZeroOff);
+  // value sums on v_dot2 with weights (1, 0) and (0, 1): one instruction
+  // per channel, exactly the fp32 sum of the bf16 values. The weights are
+  // kept in registers (the empty asm hides their value): as an inline
+  // constant the compiler would encode (1, 0) as the 32-bit constant 1.0,
+  // which the instruction reads as the pair (0, 1).
+  uint32_t w0 = 0x00003F80u, w1 = 0x3F800000u;  // bf16 pairs (1, 0) and (0, 1)
+  asm volatile("" : "+v"(w0), "+v"(w1));
+  const bf16x2 e0 = __builtin_bit_cast(bf16x2, w0), e1 = __builtin_bit_cast(bf16x2, w1);
   float ka[8], va[8];
 #pragma unroll
   for (int u = 0; u < 8; u++) ka[u] = va[u] = 0.f;
@@ -278,32 +297,51 @@ __global__ __launch_bounds__(512) void k_summarize_b8(Geo g, const void *geom, c
       for (int t = 0; t < kBatch; t++) {
         jj[t] = q0 + t < nr ? s_slot[s * nr + q0 + t] : -1;
         const int64_t off = ((rowoff + max(jj[t], 0)) * g.Hkv + h) * g.D + d0;
-        kr[t] = *reinterpret_cast<const bf16x8 *>(k + off);
-        vr[t] = *reinterpret_cast<const bf16x8 *>(v + off);
+        const bool on = jj[t] >= 0;
+        kr[t] = *reinterpret_cast<const bf16x8 *>(on ? k + off : zero16);
+        vr[t] = *reinterpret_cast<const bf16x8 *>(on ? v + off : zero16);
       }
 #pragma unroll
       for (int t = 0; t < kBatch; t++) {
-        const bool on = jj[t] >= 0;
-        cnt += on ? 1 : 0;
+        cnt += jj[t] >= 0 ? 1 : 0;
         const int lcp = s_lc[min(q0 + t, nr - 1)];
         const int lc = (lcp >> (10 * a)) & 1023;
         const float2 *cs = s_cs + ((s * nrow) + rowbase + lc) * P + p0;
 #pragma unroll
         for (int u = 0; u < 4; u++) {
-          float x0 = (float)kr[t][2 * u], x1 = (float)kr[t][2 * u + 1];
-          if constexpr (!CENTRE) rotate(x0, x1, cs[u]);
-          ka[2 * u] += on ? x0 : 0.0f;
-          ka[2 * u + 1] += on ? x1 : 0.0f;
-          va[2 * u] += on ? (float)vr[t][2 * u] : 0.0f;
-          va[2 * u + 1] += on ? (float)vr[t][2 * u + 1] : 0.0f;
+          bf16x2 kp, vp;
+          kp[0] = kr[t][2 * u];
+          kp[1] = kr[t][2 * u + 1];
+          vp[0] = vr[t][2 * u];
+          vp[1] = vr[t][2 * u + 1];
+          if constexpr (CENTRE) {
+            ka[2 * u] = __builtin_amdgcn_fdot2_f32_bf16(kp, e0, ka[2 * u], false);
+            ka[2 * u + 1] = __builtin_amdgcn_fdot2_f32_bf16(kp, e1, ka[2 * u + 1], false);
+          } else {
+            // the rotated pair accumulated term by term:
+            // (x0 c - x1 s, x0 s + x1 c)
+            const float x0 = (float)kp[0], x1 = (float)kp[1];
+            const float2 r = cs[u];
+            ka[2 * u] = fmaf(-x1, r.y, fmaf(x0, r.x, ka[2 * u]));
+            ka[2 * u + 1] = fmaf(x1, r.x, fmaf(x0, r.y, ka[2 * u + 1]));
+          }
+          va[2 * u] = __builtin_amdgcn_fdot2_f32_bf16(vp, e0, va[2 * u], false);
+          va[2 * u + 1] = __builtin_amdgcn_fdot2_f32_bf16(vp, e1, va[2 * u + 1], false);
         }
       }
     }
   }
-  // mean = sum / count (a division, as in the definition); empty -> 0
+  // mean = sum / count: one reciprocal per block, then the quotient with
+  // one residual correction (exact for a power-of-two count); empty -> 0
+  const float fc = (float)cnt;
+  const float rc = cnt > 0 ? 1.0f / fc : 0.0f;
+  auto mean = [&](float x) {
+    const float q = x * rc;
+    return fmaf(fmaf(-q, fc, x), rc, q);
+  };
   float km[8];
 #pragma unroll
-  for (int u = 0; u < 8; u++) km[u] = cnt > 0 ? ka[u] / (float)cnt : 0.0f;
+  for (int u = 0; u < 8; u++) km[u] = mean(ka[u]);
   if (CENTRE && m < g.M)  // padding slots stay 0 (and have no extent)
     rotate_at_centre<8>(g, m, a, p0, tab,
                         [&](int l, int p) { return s_cs[(s * nrow + rowbase + l) * P + p]; }, km);
@@ -311,7 +349,7 @@ __global__ __launch_bounds__(512) void k_summarize_b8(Geo g, const void *geom, c
 #pragma unroll
   for (int u = 0; u < 8; u++) {
     ko[u] = (bf16)km[u];
-    s_vt[(u * NC + c) * 9 + s] = cnt > 0 ? va[u] / (float)cnt : 0.0f;
+    s_vt[(u * NC + c) * 9 + s] = mean(va[u]);
   }
   {  // m < Mp always: the grid covers Mp / 8 groups
     const int64_t bh = (int64_t)b * g.Hkv + h;

@@ -153,7 +153,9 @@ int64_t pack3d_num_summaries(const pack3d_desc *desc);
  * Ch. 4, Prop. 2). It lives in one caller buffer `geom` of
  * pack3d_geometry_bytes() bytes, 256-byte aligned, laid out as:
  *   [0, 256)               int32 status word (bit 0: coordinate off the grid,
- *                          bit 1: coordinate duplicated), then padding
+ *                          bit 1: coordinate duplicated); bytes [64, 128)
+ *                          are zero (read in place of an absent block
+ *                          member); the rest is padding
  *   [slot_offset, ...)     int32 slot map [Z*Y*X]: slot[(z*Y + y)*X + x] =
  *                          memory position of the token at (z,y,x) (the
  *                          lowest one when several claim the site), -1 if
