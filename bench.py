@@ -13,7 +13,7 @@ launch time, timed with HIP events recorded by pack3d_forward on the launch
 stream), per-stage times and HBM-roofline fractions, and the CPU oracle
 timed on a bounded sample of the same workload on this host's cores.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--block bz,by,bx]
   python bench.py --copy-calibration    # plain device copy, for counter scaling
 """
 import argparse
@@ -290,6 +290,8 @@ def main():
                          "then the backward) instead of the inference forward")
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="grouped key/value heads (GQA/MQA) for the workload; 0 keeps H")
+    ap.add_argument("--block", type=str, default="",
+                    help="summary block shape 'bz,by,bx' in place of the workload's own")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the PACK3D "
@@ -313,6 +315,11 @@ def main():
     w = pi.workload(args.workload)
     if args.kv_heads:
         w = dataclasses.replace(w, Hkv=args.kv_heads)
+    if args.block:
+        blk = tuple(int(x) for x in args.block.split(","))
+        if len(blk) != 3 or any(b < 1 or n % b for b, n in zip(blk, w.grid)):
+            sys.exit(f"--block {args.block}: need three extents that divide the grid {w.grid}")
+        w = dataclasses.replace(w, block=blk)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     es = 2 if w.dtype == "bf16" else 4
     if args.backward:

@@ -75,4 +75,36 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
   return base + idx;
 }
 
+// (batch, head, box) of the local kernels' work item w, over nh heads: heads
+// innermost (the heads of one token are adjacent in memory, so the workgroups
+// of one box share cache lines), then the boxes in cubes of S x S x S boxes
+// (the last cube of each axis may be cut short), each cube in z, y, x order.
+// With the XCD-contiguous dealing above, one XCD holds a cube rather than a
+// thin slab, so less of a box's halo belongs to boxes on other XCDs.
+struct BoxWork {
+  int b, h, tz, ty, tx;
+};
+#ifndef PK_SUPERBLOCK
+#define PK_SUPERBLOCK 4
+#endif
+__device__ __forceinline__ BoxWork box_work(int w, int nh, int ntz, int nty, int ntx) {
+  const int h = w % nh;
+  w /= nh;
+  const int ntiles = ntz * nty * ntx;
+  const int b = w / ntiles;
+  int r = w - b * ntiles;
+  constexpr int S = PK_SUPERBLOCK;
+  if (S <= 1) return {b, h, r / (nty * ntx), (r / ntx) % nty, r % ntx};
+  const int bz = r / (S * nty * ntx);  // slab of cubes; those before it are whole
+  r -= bz * S * nty * ntx;
+  const int nz = min(S, ntz - bz * S);
+  const int by = r / (nz * S * ntx);   // row of cubes within the slab
+  r -= by * nz * S * ntx;
+  const int ny = min(S, nty - by * S);
+  const int bx = r / (nz * ny * S);    // cube within the row
+  r -= bx * nz * ny * S;
+  const int nx = min(S, ntx - bx * S);
+  return {b, h, bz * S + r / (ny * nx), by * S + (r / nx) % ny, bx * S + r % nx};
+}
+
 }  // namespace pk

@@ -44,12 +44,9 @@ __global__ __launch_bounds__(TZ *TY *TX) void k_local(Geo g, const void *geom, c
   __shared__ T sV[NH * PITCH];
   __shared__ int sSlot[NH];
 
-  const int ntiles = ntz * nty * ntx;
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = w % g.H;
-  const int tile = (w / g.H) % ntiles;
-  const int b = w / (g.H * ntiles);
-  const int z0 = (tile / (nty * ntx)) * TZ, y0 = ((tile / ntx) % nty) * TY, x0 = (tile % ntx) * TX;
+  const BoxWork wk = box_work(xcd_remap(blockIdx.x, gridDim.x), g.H, ntz, nty, ntx);
+  const int h = wk.h, b = wk.b;
+  const int z0 = wk.tz * TZ, y0 = wk.ty * TY, x0 = wk.tx * TX;
   const int32_t *slot = slot_map(geom, g);
   const float2 *tab = rope_table(geom, g);
   const int64_t bN = (int64_t)b * g.N;
@@ -184,12 +181,9 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX, D == 96 ? 4 : 1) void k_loca
   const bf16 *sV = sK;
   __shared__ int sSlot[NH];
 
-  const int ntiles = ntz * nty * ntx;
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = w % g.H;
-  const int tile = (w / g.H) % ntiles;
-  const int b = w / (g.H * ntiles);
-  const int z0 = (tile / (nty * ntx)) * TZ, y0 = ((tile / ntx) % nty) * TY, x0 = (tile % ntx) * TX;
+  const BoxWork wk = box_work(xcd_remap(blockIdx.x, gridDim.x), g.H, ntz, nty, ntx);
+  const int h = wk.h, b = wk.b;
+  const int z0 = wk.tz * TZ, y0 = wk.ty * TY, x0 = wk.tx * TX;
   const int32_t *slot = slot_map(geom, g);
   const float2 *tab = rope_table(geom, g);
   const int64_t bN = (int64_t)b * g.N;
@@ -413,7 +407,8 @@ hipError_t launch_local(const Geo &g, int dtype, const void *geom, const void *q
       case 6: return run_local<bf16, 6, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
       case 12: return run_local<bf16, 12, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
       case 24: return run_local<bf16, 24, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
-      case 48: return run_local_pair<48, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
+      case 48:
+        return run_local_pair<48, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
       case 96: return run_local_pair<96, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
     }
   } else {

@@ -139,11 +139,10 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX, D == 48 ? 3 : 2) void k_bwd_
   __shared__ int sSlot[NH];
   __shared__ float2 sCS[(HZ + HY + HX) * P];
 
-  const int ntiles = ntz * nty * ntx;
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = w % g.H, tile = (w / g.H) % ntiles, b = w / (g.H * ntiles);
+  const BoxWork wk = box_work(xcd_remap(blockIdx.x, gridDim.x), g.H, ntz, nty, ntx);
+  const int h = wk.h, b = wk.b;
   const int hk = h / g.G;
-  const int z0 = (tile / (nty * ntx)) * TZ, y0 = ((tile / ntx) % nty) * TY, x0 = (tile % ntx) * TX;
+  const int z0 = wk.tz * TZ, y0 = wk.ty * TY, x0 = wk.tx * TX;
   const int64_t bN = (int64_t)b * g.N;
   auto cs_at = [&](int a, int rc, int p) {
     const int base = a == 0 ? 0 : (a == 1 ? HZ : HZ + HY);
@@ -332,10 +331,9 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX, 2) void k_bwd_local_kv_pair(
   __shared__ float2 sCS[(HZ + HY + HX) * P];
   __shared__ float sOmg[NH], sL[NH], sDl[NH];
 
-  const int ntiles = ntz * nty * ntx;
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
-  const int hk = w % g.Hkv, tile = (w / g.Hkv) % ntiles, b = w / (g.Hkv * ntiles);
-  const int z0 = (tile / (nty * ntx)) * TZ, y0 = ((tile / ntx) % nty) * TY, x0 = (tile % ntx) * TX;
+  const BoxWork wk = box_work(xcd_remap(blockIdx.x, gridDim.x), g.Hkv, ntz, nty, ntx);
+  const int hk = wk.h, b = wk.b;
+  const int z0 = wk.tz * TZ, y0 = wk.ty * TY, x0 = wk.tx * TX;
   const int64_t bN = (int64_t)b * g.N;
   const float2 *tab = rope_table(geom, g);
   auto cs_at = [&](int a, int rc, int p) {
