@@ -155,10 +155,13 @@ __global__ __launch_bounds__(TZ *TY *TX) void k_local(Geo g, const void *geom, c
 // query meet through DPP lane swaps; the value sum pairs neighbours (k, k+1)
 // so that one v_dot2 accumulates two neighbours for one channel, the pairs
 // being formed with v_perm_b32.
-// D = 96 workgroups are 8 waves with 74 KB of LDS: asking for four waves per
-// SIMD (128 VGPRs, a few values spilled) lets two of them share a CU
+// At D = 96 a query takes four lanes, so the box is 2 x 4 x 8 sites: four
+// waves and 49 KB of LDS, three workgroups per CU at three waves per SIMD with
+// no spill. (A 4 x 4 x 8 box needs 8 waves and 74 KB; two of those fit a CU
+// only under a 128-VGPR cap, whose spills cost more than the larger halo.)
 template <int D, int TZ, int TY, int TX>
-__global__ __launch_bounds__((D / 24) * TZ *TY *TX, D == 96 ? 4 : 1) void k_local_pair(
+__global__ __launch_bounds__((D / 24) * TZ *TY *TX,
+                             D == 96 ? (TZ * TY * TX == 128 ? 4 : 3) : 1) void k_local_pair(
     Geo g, const void *geom, const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const bf16 *__restrict__ v, const bf16 *gate, const bf16 *oglob, bf16 *out, int ntz, int nty,
     int ntx) {
@@ -409,7 +412,7 @@ hipError_t launch_local(const Geo &g, int dtype, const void *geom, const void *q
       case 24: return run_local<bf16, 24, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
       case 48:
         return run_local_pair<48, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
-      case 96: return run_local_pair<96, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
+      case 96: return run_local_pair<96, 2, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
     }
   } else {
     switch (g.D) {
