@@ -18,8 +18,11 @@
 //   k_bwd_prep_mfma   per (batch, query head, grid site): bf16 q~ s log2(e)
 //                     and dO_glob = g dO (rounded as the forward rounds q~),
 //                     in 32-row blocks and 8-row transposed blocks, with the
-//                     saved lse and Delta = <dO_glob, O_glob>, in grid-site
-//                     (raster) order -- the order every reduction runs in
+//                     saved lse and Delta = <dO_glob, O_glob>, both negated,
+//                     in grid-site (raster) order -- the order every
+//                     reduction runs in. The negated values start the
+//                     accumulators of the score and dP products, so the
+//                     products return t - lse and dP - Delta directly.
 //   k_bwd_relayout    v_sum in the key-summary layout and k_sum in the
 //                     value-summary layout, the operand shapes the
 //                     contractions above need
@@ -49,7 +52,7 @@ __device__ __forceinline__ int swap23(int r) {
 //   qn [B*H, Np/32, D/8, 32, 8]  q~ s log2(e): row p%32 of 32-row block p/32
 //   qt [B*H, Np/8, D, 8]         the same, channel-major: 8 sites per chunk
 //   dn, dt                       dO_glob, likewise
-//   lse_p, dl_p [B*H, Np]        saved lse (+inf where no token: P = 0), Delta
+//   lse_p, dl_p [B*H, Np]        -lse (-inf where no token: P = 0), -Delta
 //   tok [B, Np]                  token at the site (-1: none)
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_prep_mfma(
@@ -105,8 +108,8 @@ __global__ __launch_bounds__(256) void k_bwd_prep_mfma(
       dt[tb] = dv[e];
     }
   }
-  lse_p[t] = i >= 0 ? lse[row] : INFINITY;
-  dl_p[t] = dl;
+  lse_p[t] = i >= 0 ? -lse[row] : -INFINITY;
+  dl_p[t] = -dl;
 }
 
 // v_sum [B*Hkv, Mp/8, D, 8] -> vk [B*Hkv, Mp/32, D/8, 32, 8] and
@@ -155,7 +158,9 @@ __global__ __launch_bounds__(64 * NW, G == 1 ? 2 : 1) void k_bwd_gq_mfma(
   // this lane's query site of each group (Np is a multiple of NW * 32 * G)
   int p[G];
   bf16x8 qf[G][KD], df[G][KD];
-  float lq[G], dq[G];
+  // -lse and -Delta of the lane's query, in every register: the start value
+  // of its score and dP columns
+  f32x16 lq[G], dq[G];
   f32x16 acc[G][DT];
 #pragma unroll
   for (int gi = 0; gi < G; gi++) {
@@ -167,14 +172,17 @@ __global__ __launch_bounds__(64 * NW, G == 1 ? 2 : 1) void k_bwd_gq_mfma(
       qf[gi][c] = *reinterpret_cast<const bf16x8 *>(qn + o);
       df[gi][c] = *reinterpret_cast<const bf16x8 *>(dn + o);
     }
-    lq[gi] = lse_p[(int64_t)bh * Np + p[gi]];
-    dq[gi] = dl_p[(int64_t)bh * Np + p[gi]];
+    const float nl = lse_p[(int64_t)bh * Np + p[gi]], nd = dl_p[(int64_t)bh * Np + p[gi]];
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      lq[gi][j] = nl;
+      dq[gi][j] = nd;
+    }
 #pragma unroll
     for (int t = 0; t < DT; t++)
 #pragma unroll
       for (int j = 0; j < 16; j++) acc[gi][t][j] = 0.f;
   }
-  const f32x16 zero16 = {};
 
   // per-lane parts of the tile offsets: row chunk e = (ch, pos) holds summary
   // 32*(pos/32) + swap23(pos%32) of the tile; kt chunk e = (j8, d)
@@ -226,8 +234,8 @@ __global__ __launch_bounds__(64 * NW, G == 1 ? 2 : 1) void k_bwd_gq_mfma(
       const bf16x8 vf = V[(2 * c + hi) * TS + 32 * sub + l32];
 #pragma unroll
       for (int gi = 0; gi < G; gi++) {
-        s[gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[gi][c], c == 0 ? zero16 : s[gi], 0, 0, 0);
-        dp[gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[gi][c], c == 0 ? zero16 : dp[gi], 0, 0, 0);
+        s[gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[gi][c], c == 0 ? lq[gi] : s[gi], 0, 0, 0);
+        dp[gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[gi][c], c == 0 ? dq[gi] : dp[gi], 0, 0, 0);
       }
     }
 #pragma unroll
@@ -236,7 +244,7 @@ __global__ __launch_bounds__(64 * NW, G == 1 ? 2 : 1) void k_bwd_gq_mfma(
       bf16x8 tf[2];
 #pragma unroll
       for (int j = 0; j < 16; j++) {
-        float t = __builtin_amdgcn_exp2f(s[gi][j] - lq[gi]) * (dp[gi][j] - dq[gi]);
+        float t = __builtin_amdgcn_exp2f(s[gi][j]) * dp[gi][j];
         if constexpr (decltype(mask)::value)
           t = (mbase + 16 * (j >> 3) + 8 * hi + (j & 7) < g.M) ? t : 0.f;
         tf[j >> 3][j & 7] = (bf16)t;
@@ -274,16 +282,15 @@ __global__ __launch_bounds__(64 * NW, G == 1 ? 2 : 1) void k_bwd_gq_mfma(
         for (int c = 0; c < KD; c++) {
           const bf16x8 kf = K[(2 * c + hi) * TS + 32 * sub + l32];
           const bf16x8 vf = V[(2 * c + hi) * TS + 32 * sub + l32];
-          s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0][c], c == 0 ? zero16 : s[sub], 0, 0, 0);
-          dp[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[0][c], c == 0 ? zero16 : dp[sub], 0, 0, 0);
+          s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0][c], c == 0 ? lq[0] : s[sub], 0, 0, 0);
+          dp[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[0][c], c == 0 ? dq[0] : dp[sub], 0, 0, 0);
         }
 #pragma unroll
       for (int sub = 0; sub < NSUB; sub++) {
         bf16x8 tf[2];
 #pragma unroll
         for (int j = 0; j < 16; j++)
-          tf[j >> 3][j & 7] =
-              (bf16)(__builtin_amdgcn_exp2f(s[sub][j] - lq[0]) * (dp[sub][j] - dq[0]));
+          tf[j >> 3][j & 7] = (bf16)(__builtin_amdgcn_exp2f(s[sub][j]) * dp[sub][j]);
 #pragma unroll
         for (int t = 0; t < DT; t++) {
           const int d = min(32 * t + l32, D - 1);
@@ -370,7 +377,6 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gk_mfma(
   for (int t = 0; t < DT; t++)
 #pragma unroll
     for (int j = 0; j < 16; j++) aK[t][j] = aV[t][j] = 0.f;
-  const f32x16 zero16 = {};
 
   const int nqt = Np / TQ;
   const int per = (nqt + nsplit - 1) / nsplit;
@@ -418,7 +424,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gk_mfma(
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rdt, (lds_ptr)&dDT[NTH * r + 64 * wv], 16, o, 0, 0, 0);
       }
     }
-    // per-site statistics: wave 0 the log-sum-exp, wave 1 Delta (4 bytes a lane)
+    // per-site statistics: wave 0 -lse, wave 1 -Delta (4 bytes a lane)
     if (wv < 2) {
       const __amdgpu_buffer_rsrc_t rs = buffer_rsrc((wv == 0 ? lse_p : dl_p) + bh * Np, Np * 4);
       const uint32_t o = (uint32_t)(qtile * TQ + min(lane, TQ - 1)) * 4;
@@ -440,37 +446,44 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gk_mfma(
     // the score products of every sub-tile of the tile first, so that each
     // sub-tile's vector work runs while the matrix core still works on the
     // next one's products (and on the previous one's accumulation)
-    // C[query rows][summary columns]: row r holds query site swap23(r)
+    // C[query rows][summary columns]: row r holds query site swap23(r), so
+    // register 8*c2 + e of half hi <-> site 32*sub + 16*c2 + 8*hi + e. The
+    // products start from -lse and -Delta of those sites.
     f32x16 s[NSUB], dp[NSUB];
 #pragma unroll
     for (int sub = 0; sub < NSUB; sub++) {
 #pragma unroll
+      for (int c2 = 0; c2 < 2; c2++)
+#pragma unroll
+        for (int hq = 0; hq < 2; hq++) {
+          const int q0 = 32 * sub + 16 * c2 + 8 * hi + 4 * hq;
+          const f32x4 l4 = *reinterpret_cast<const f32x4 *>(L + q0);
+          const f32x4 d4 = *reinterpret_cast<const f32x4 *>(Dl + q0);
+#pragma unroll
+          for (int u = 0; u < 4; u++) {
+            s[sub][8 * c2 + 4 * hq + u] = l4[u];
+            dp[sub][8 * c2 + 4 * hq + u] = d4[u];
+          }
+        }
+#pragma unroll
       for (int c = 0; c < KD; c++) {
         const bf16x8 qa = Q[(2 * c + hi) * TQ + 32 * sub + l32];
         const bf16x8 da = Dd[(2 * c + hi) * TQ + 32 * sub + l32];
-        s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb[c], c == 0 ? zero16 : s[sub], 0, 0, 0);
-        dp[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vb[c], c == 0 ? zero16 : dp[sub], 0, 0, 0);
+        s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb[c], s[sub], 0, 0, 0);
+        dp[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vb[c], dp[sub], 0, 0, 0);
       }
     }
 #pragma unroll
     for (int sub = 0; sub < NSUB; sub++) {
-      // register 8*c2 + e of half hi <-> site 32*sub + 16*c2 + 8*hi + e
       bf16x8 pa[2], ta[2];
 #pragma unroll
-      for (int c2 = 0; c2 < 2; c2++) {
-        const int q0 = 32 * sub + 16 * c2 + 8 * hi;
-        const f32x4 l0 = *reinterpret_cast<const f32x4 *>(L + q0);
-        const f32x4 l1 = *reinterpret_cast<const f32x4 *>(L + q0 + 4);
-        const f32x4 d0 = *reinterpret_cast<const f32x4 *>(Dl + q0);
-        const f32x4 d1 = *reinterpret_cast<const f32x4 *>(Dl + q0 + 4);
+      for (int c2 = 0; c2 < 2; c2++)
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-          const float le = e < 4 ? l0[e] : l1[e - 4], de = e < 4 ? d0[e] : d1[e - 4];
-          const float pr = __builtin_amdgcn_exp2f(s[sub][8 * c2 + e] - le);
+          const float pr = __builtin_amdgcn_exp2f(s[sub][8 * c2 + e]);
           pa[c2][e] = (bf16)pr;
-          ta[c2][e] = (bf16)(pr * (dp[sub][8 * c2 + e] - de));
+          ta[c2][e] = (bf16)(pr * dp[sub][8 * c2 + e]);
         }
-      }
 #pragma unroll
       for (int t = 0; t < DT; t++) {
         const int d = min(32 * t + l32, D - 1);
@@ -569,7 +582,7 @@ bool bwd_global_mfma_supported(const Geo &g, int dtype) {
 
 hipError_t launch_bwd_global_mfma(const Geo &g, const BwdArgs &a, const BwdMfmaArgs &m,
                                   hipStream_t s) {
-  if (g.D == 48) return run_bwd_global_mfma<48, 64, 64, 4, 1, 4>(g, a, m, s);
+  if (g.D == 48) return run_bwd_global_mfma<48, 128, 64, 4, 1, 4>(g, a, m, s);
   return run_bwd_global_mfma<96, 64, 32, 4, 1, 4>(g, a, m, s);
 }
 
