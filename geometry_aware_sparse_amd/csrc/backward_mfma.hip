@@ -54,16 +54,23 @@ __device__ __forceinline__ int swap23(int r) {
 //   dn, dt                       dO_glob, likewise
 //   lse_p, dl_p [B*H, Np]        -lse (-inf where no token: P = 0), -Delta
 //   tok [B, Np]                  token at the site (-1: none)
+// A workgroup of NTH threads takes NTH consecutive sites of one (b, h) (Np is
+// a multiple of 256), one site per thread. The 32-row blocks are written
+// straight from registers; the transposed blocks go through LDS, so that each
+// lane then stores one whole 16-byte chunk (8 sites of one channel) and a
+// wave's stores are contiguous.
 template <int D>
-__global__ __launch_bounds__(256) void k_bwd_prep_mfma(
+__global__ __launch_bounds__(D == 48 ? 256 : 128) void k_bwd_prep_mfma(
     Geo g, const void *geom, const bf16 *__restrict__ q, const bf16 *__restrict__ gate,
     const bf16 *__restrict__ dout, const bf16 *__restrict__ oglob, const float *__restrict__ lse,
     bf16 *qn, bf16 *qt, bf16 *dn, bf16 *dt, float *lse_p, float *dl_p, int32_t *tok, int Np) {
   constexpr int DA = D / 3, NCH = D / 8;
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;  // ((b*H + h) * Np + p)
-  if (t >= (int64_t)g.B * g.H * Np) return;
+  constexpr int NTH = D == 48 ? 256 : 128;
+  constexpr int PITCH = D + 8;  // LDS row pitch (elements): 16-byte rows, fewer bank conflicts
+  __shared__ __attribute__((aligned(16))) bf16 sQ[NTH * PITCH], sD[NTH * PITCH];
+  const int64_t t = (int64_t)blockIdx.x * NTH + threadIdx.x;  // ((b*H + h) * Np + p)
   const int p = (int)(t % Np);
-  const int64_t bh = t / Np;
+  const int64_t bh = t / Np;  // the same for the whole workgroup
   const int h = (int)(bh % g.H), b = (int)(bh / g.H);
   const int32_t *slot = slot_map(geom, g);
   const float2 *tab = rope_table(geom, g);
@@ -101,15 +108,28 @@ __global__ __launch_bounds__(256) void k_bwd_prep_mfma(
     const int64_t nb = (((bh * (Np / 32) + p / 32) * NCH + c) * 32 + p % 32) * 8;
     *reinterpret_cast<bf16x8 *>(qn + nb) = qv;
     *reinterpret_cast<bf16x8 *>(dn + nb) = dv;
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-      const int64_t tb = ((bh * (Np / 8) + p / 8) * D + 8 * c + e) * 8 + p % 8;
-      qt[tb] = qv[e];
-      dt[tb] = dv[e];
-    }
+    *reinterpret_cast<bf16x8 *>(&sQ[threadIdx.x * PITCH + 8 * c]) = qv;
+    *reinterpret_cast<bf16x8 *>(&sD[threadIdx.x * PITCH + 8 * c]) = dv;
   }
   lse_p[t] = i >= 0 ? -lse[row] : -INFINITY;
   dl_p[t] = -dl;
+  __syncthreads();
+  // chunk (g8, d) of the workgroup: channel d of its sites 8*g8 .. 8*g8 + 7
+  const int p0 = (int)(((int64_t)blockIdx.x * NTH) % Np);
+#pragma unroll
+  for (int r = 0; r < NCH; r++) {
+    const int e = (int)threadIdx.x + NTH * r;
+    const int g8 = e / D, d = e % D;
+    bf16x8 qv, dv;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      qv[k] = sQ[(8 * g8 + k) * PITCH + d];
+      dv[k] = sD[(8 * g8 + k) * PITCH + d];
+    }
+    const int64_t tb = ((bh * (Np / 8) + p0 / 8 + g8) * D + d) * 8;
+    *reinterpret_cast<bf16x8 *>(qt + tb) = qv;
+    *reinterpret_cast<bf16x8 *>(dt + tb) = dv;
+  }
 }
 
 // v_sum [B*Hkv, Mp/8, D, 8] -> vk [B*Hkv, Mp/32, D/8, 32, 8] and
@@ -533,8 +553,9 @@ hipError_t run_bwd_global_mfma(const Geo &g, const BwdArgs &a, const BwdMfmaArgs
                                hipStream_t s) {
   const int Np = (g.N + kSiteAlign - 1) / kSiteAlign * kSiteAlign, Mp = (g.M + 31) / 32 * 32;
   {
+    constexpr int NTH = D == 48 ? 256 : 128;  // divides Np
     const int64_t n = (int64_t)g.B * g.H * Np;
-    hipLaunchKernelGGL((k_bwd_prep_mfma<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, g,
+    hipLaunchKernelGGL((k_bwd_prep_mfma<D>), dim3((unsigned)(n / NTH)), dim3(NTH), 0, s, g,
                        a.geom, static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.gate),
                        static_cast<const bf16 *>(a.dout), static_cast<const bf16 *>(a.oglob),
                        a.lse_g, m.qn, m.qt, m.dn, m.dt, m.lse_p, m.dl_p, m.tok, Np);
