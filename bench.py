@@ -59,17 +59,23 @@ def _sha(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(config):
     """HBM bytes per launch of the dominant kernel from the committed
     rocprofv3 counter summary, or None when the kernel source has changed
-    since the counters were taken."""
+    since the counters were taken or the counters were taken on another
+    configuration (workload, block shape, KV heads, summary RoPE)."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if t.get("source_sha") != _sha(DOMINANT_SRC):
+    if t.get("source_sha") != _sha(DOMINANT_SRC) or t.get("config") != config:
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def traffic_config(line_config):
+    """The part of a bench line's config that the counters depend on."""
+    return {k: line_config[k] for k in ("workload", "block", "kv_heads", "summary_rope")}
 
 
 def cpu_baseline(w, coords, q, k, v, g, target_s=15.0):
@@ -393,7 +399,7 @@ def main():
              else "k_global_valu")
     roofline = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 1),
                 "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4), "traffic": measured_traffic(),
+                "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
                 "traffic_unit": "bytes/launch"}
     stage_roof = {}
     for name in STAGES:
@@ -417,6 +423,7 @@ def main():
                         f"from {stage_passes} extra steps after the timed ones"),
         "wall_s_timed_region": round(wall, 4),
     }
+    roofline["traffic"] = measured_traffic(traffic_config(line["config"]))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, coords, q, k, v, g)
     else:

@@ -1,4 +1,5 @@
 """ctypes declarations of include/pack3d.h."""
+import contextlib
 import ctypes as C
 import os
 
@@ -19,7 +20,7 @@ PACK3D_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 STATUS = {0: "PACK3D_OK", -1: "PACK3D_ERR_INVALID_ARG", -2: "PACK3D_ERR_SHAPE",
           -3: "PACK3D_ERR_WORKSPACE", -4: "PACK3D_ERR_UNSUPPORTED", -5: "PACK3D_ERR_HIP",
-          -6: "PACK3D_ERR_COORDS"}
+          -6: "PACK3D_ERR_COORDS", -7: "PACK3D_ERR_INTERNAL"}
 
 
 class Pack3DError(RuntimeError):
@@ -68,22 +69,46 @@ _SIGS = {
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
 _lib = None
+_debug_lib = None
+_use_debug = False
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(LIB_PATH), "libpack3d_debug.so")
+
+
+def _load(path):
+    if not os.path.exists(path):
+        raise ImportError(f"PACK3D HIP library not built: {path} is missing "
+                          "(run geometry_aware_sparse_amd/build.py)")
+    L = C.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    if L.pack3d_abi_version() != ABI_VERSION:
+        raise ImportError(f"{path} reports ABI {L.pack3d_abi_version()}, the binding "
+                          f"expects {ABI_VERSION}: rebuild the library")
+    return L
 
 
 def library():
-    """Load lib/libpack3d.so once; raises when it is missing (no fallback)."""
+    """Load lib/libpack3d.so once; raises when it is missing (no fallback).
+    Inside `with debug_library():` the debug build is returned instead."""
     global _lib
+    if _use_debug:
+        return _debug_lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"PACK3D HIP library not built: {LIB_PATH} is missing "
-                              "(run geometry_aware_sparse_amd/build.py)")
-        L = C.CDLL(LIB_PATH)
-        for name, (res, args) in _SIGS.items():
-            fn = getattr(L, name)
-            fn.restype = res
-            fn.argtypes = args
-        if L.pack3d_abi_version() != ABI_VERSION:
-            raise ImportError(f"{LIB_PATH} reports ABI {L.pack3d_abi_version()}, the binding "
-                              f"expects {ABI_VERSION}: rebuild the library")
-        _lib = L
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def debug_library():
+    """Route every call of the binding to lib/libpack3d_debug.so (the build
+    with checked slot-map reads, `build.py --debug`) inside the block."""
+    global _debug_lib, _use_debug
+    if _debug_lib is None:
+        _debug_lib = _load(DEBUG_LIB_PATH)
+    prev, _use_debug = _use_debug, True
+    try:
+        yield _debug_lib
+    finally:
+        _use_debug = prev

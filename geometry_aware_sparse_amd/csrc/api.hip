@@ -94,7 +94,20 @@ int validate_coords(const pack3d_desc *d, const void *geom, hipStream_t s) {
   if (hipMemcpyAsync(&status, geom, sizeof(status), hipMemcpyDeviceToHost, s) != hipSuccess)
     return PACK3D_ERR_HIP;
   if (hipStreamSynchronize(s) != hipSuccess) return PACK3D_ERR_HIP;
+  if (status & kStatusDebugBounds) return PACK3D_ERR_INTERNAL;
   return status ? PACK3D_ERR_COORDS : PACK3D_OK;
+}
+
+// Debug builds (PK_DEBUG_BOUNDS) check the status word again once a call's
+// kernels have run, under PACK3D_VALIDATE, so that a slot-map read out of
+// range in any of them is reported; other builds skip it.
+int debug_check(const pack3d_desc *d, const void *geom, hipStream_t s) {
+#ifdef PK_DEBUG_BOUNDS
+  return validate_coords(d, geom, s);
+#else
+  (void)d, (void)geom, (void)s;
+  return PACK3D_OK;
+#endif
 }
 
 }  // namespace
@@ -112,6 +125,7 @@ const char *pack3d_strerror(int status) {
     case PACK3D_ERR_UNSUPPORTED: return "dtype / head-dim / exclusion combination not built";
     case PACK3D_ERR_HIP: return "HIP runtime or launch failure";
     case PACK3D_ERR_COORDS: return "coordinate off the grid or duplicated";
+    case PACK3D_ERR_INTERNAL: return "a debug build's bounds check found a slot-map read out of range";
     default: return "unknown pack3d status";
   }
 }
@@ -174,8 +188,10 @@ int pack3d_block_summarize(const pack3d_desc *desc, const void *geom, const void
   int rc = make_geo(desc, &g);
   if (rc) return rc;
   if (!geom || !k || !v || !k_sum || !v_sum) return PACK3D_ERR_INVALID_ARG;
-  return hip_status(launch_summarize(g, desc->dtype, geom, k, v, k_sum, v_sum,
-                                     static_cast<hipStream_t>(stream)));
+  if ((rc = hip_status(launch_summarize(g, desc->dtype, geom, k, v, k_sum, v_sum,
+                                        static_cast<hipStream_t>(stream)))))
+    return rc;
+  return debug_check(desc, geom, static_cast<hipStream_t>(stream));
 }
 
 int pack3d_local_attn(const pack3d_desc *desc, const void *geom, const void *q, const void *k,
@@ -188,7 +204,8 @@ int pack3d_local_attn(const pack3d_desc *desc, const void *geom, const void *q, 
   hipError_t e = launch_local(g, desc->dtype, geom, q, k, v, nullptr, nullptr, o_local,
                               static_cast<hipStream_t>(stream), &ok);
   if (!ok) return PACK3D_ERR_UNSUPPORTED;
-  return hip_status(e);
+  if ((rc = hip_status(e))) return rc;
+  return debug_check(desc, geom, static_cast<hipStream_t>(stream));
 }
 
 int pack3d_global_attn(const pack3d_desc *desc, const void *geom, const int32_t *coords,
@@ -202,7 +219,8 @@ int pack3d_global_attn(const pack3d_desc *desc, const void *geom, const int32_t 
   hipError_t e = launch_global(g, desc->dtype, geom, coords, q, k_sum, v_sum, o_global, nullptr,
                                static_cast<hipStream_t>(stream), &ok);
   if (!ok) return PACK3D_ERR_UNSUPPORTED;
-  return hip_status(e);
+  if ((rc = hip_status(e))) return rc;
+  return debug_check(desc, geom, static_cast<hipStream_t>(stream));
 }
 
 int pack3d_mix(const pack3d_desc *desc, const void *gate, const void *o_local,
@@ -283,7 +301,8 @@ int forward_impl(const pack3d_desc *desc, const int32_t *coords, const void *q, 
                                             len, s))))
       return rc;
   }
-  return mark(7);
+  if ((rc = mark(7))) return rc;
+  return debug_check(desc, geom, s);
 }
 
 // Backward workspace: geometry | k_sum | v_sum | fp32 intermediates, then
@@ -518,7 +537,8 @@ int pack3d_backward(const pack3d_desc *desc, const int32_t *coords, const void *
   bool ok = true;
   if ((rc = hip_status(launch_backward(g, desc->dtype, a, s, &ok)))) return rc;
   if (!ok) return PACK3D_ERR_UNSUPPORTED;
-  return mark(5);
+  if ((rc = mark(5))) return rc;
+  return debug_check(desc, base + L.geom, s);
 }
 
 }  // extern "C"

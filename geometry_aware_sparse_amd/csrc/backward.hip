@@ -235,7 +235,7 @@ __global__ __launch_bounds__(64) void k_bwd_global_kv(Geo g, const void *geom,
       __syncthreads();
       for (int e = threadIdx.x; e < ni; e += 64) {
         const int site = i0 + e;
-        const int i = slot[site];
+        const int i = slot_get(g, slot, site);
         const int64_t row = ((int64_t)b * g.N + max(i, 0)) * g.H + h;
         sTok[e] = i;
         sL[e] = i >= 0 ? lse[row] : -INFINITY;  // an empty site takes no part
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(TZ *TY *TX) void k_bwd_local_q(
     const int hz = hs / (HY * HX), hy = (hs / HX) % HY, hx = hs % HX;
     const int z = z0 - 1 + hz, y = y0 - 1 + hy, x = x0 - 1 + hx;
     int j = -1;
-    if (z >= 0 && y >= 0 && x >= 0 && z < g.Z && y < g.Y && x < g.X) j = slot[site_of(g, z, y, x)];
+    if (z >= 0 && y >= 0 && x >= 0 && z < g.Z && y < g.Y && x < g.X) j = slot_get(g, slot, site_of(g, z, y, x));
     if (d0 == 0) sSlot[hs] = j;
     float k0 = 0.f, k1 = 0.f, v0 = 0.f, v1 = 0.f;
     if (j >= 0) {
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(TZ *TY *TX) void k_bwd_local_kv(
   const int ks_ = ((tz + 1) * HY + (ty + 1)) * HX + (tx + 1);
   const int c3[3] = {z0 + tz, y0 + ty, x0 + tx};
   const bool on = c3[0] < g.Z && c3[1] < g.Y && c3[2] < g.X;
-  const int j = on ? slot[site_of(g, c3[0], c3[1], c3[2])] : -1;
+  const int j = on ? slot_get(g, slot, site_of(g, c3[0], c3[1], c3[2])) : -1;
   const int64_t jrow = (bN + max(j, 0)) * g.Hkv + hk;
   // own key, rotated and rounded to T exactly as the query side staged it
   float kv[D], vv[D];
@@ -482,7 +482,7 @@ __global__ __launch_bounds__(TZ *TY *TX) void k_bwd_local_kv(
       const int hz = hs / (HY * HX), hy = (hs / HX) % HY, hx = hs % HX;
       const int z = z0 - 1 + hz, y = y0 - 1 + hy, x = x0 - 1 + hx;
       int i = -1;
-      if (z >= 0 && y >= 0 && x >= 0 && z < g.Z && y < g.Y && x < g.X) i = slot[site_of(g, z, y, x)];
+      if (z >= 0 && y >= 0 && x >= 0 && z < g.Z && y < g.Y && x < g.X) i = slot_get(g, slot, site_of(g, z, y, x));
       const int64_t row = (bN + max(i, 0)) * g.H + h;
       sQ[hs * PITCH + d] = i >= 0 ? q[row * D + d] : from_f32<T>(0.f);
       sO[hs * PITCH + d] = i >= 0 ? dout[row * D + d] : from_f32<T>(0.f);

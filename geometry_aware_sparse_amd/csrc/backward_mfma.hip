@@ -74,7 +74,7 @@ __global__ __launch_bounds__(D == 48 ? 256 : 128) void k_bwd_prep_mfma(
   const int h = (int)(bh % g.H), b = (int)(bh / g.H);
   const int32_t *slot = slot_map(geom, g);
   const float2 *tab = rope_table(geom, g);
-  const int i = p < g.N ? slot[p] : -1;
+  const int i = p < g.N ? slot_get(g, slot, p) : -1;
   if (h == 0) tok[(int64_t)b * Np + p] = i;
   const int c3[3] = {p / (g.Y * g.X), (p / g.X) % g.Y, p % g.X};
   const int64_t row = ((int64_t)b * g.N + max(i, 0)) * g.H + h;

@@ -97,13 +97,31 @@ __device__ __forceinline__ void rotate(float &x0, float &x1, float2 cs) {
 __device__ __forceinline__ int site_of(const Geo &g, int z, int y, int x) {
   return (z * g.Y + y) * g.X + x;
 }
+// Status word bit set by a debug build's bounds check.
+constexpr int kStatusDebugBounds = 4;
+// The slot-map entry of a grid site. A debug build (PK_DEBUG_BOUNDS, made
+// by build.py --debug) checks every such read: a site outside the grid sets
+// kStatusDebugBounds in the geometry buffer's status word (which sits
+// g.slot_off bytes before the map) and reads -1, so an indexing mistake
+// surfaces as a status error on the host rather than as a stray read.
+__device__ __forceinline__ int32_t slot_get(const Geo &g, const int32_t *slot, int64_t site) {
+#ifdef PK_DEBUG_BOUNDS
+  if (site < 0 || site >= (int64_t)g.Z * g.Y * g.X) {
+    int *status = reinterpret_cast<int *>(const_cast<char *>(
+        reinterpret_cast<const char *>(slot) - g.slot_off));
+    atomicOr(status, kStatusDebugBounds);
+    return -1;
+  }
+#endif
+  return slot[site];
+}
 // Whether the token at memory position i, with coordinate (z, y, x), takes
 // part: its coordinate is on the grid and its site's slot names it (a
 // repeated coordinate leaves every token but the lowest index out).
 __device__ __forceinline__ bool takes_part(const Geo &g, const int32_t *slot, int i, int z, int y,
                                            int x) {
   if (z < 0 || y < 0 || x < 0 || z >= g.Z || y >= g.Y || x >= g.X) return false;
-  return slot[site_of(g, z, y, x)] == i;
+  return slot_get(g, slot, site_of(g, z, y, x)) == i;
 }
 __device__ __forceinline__ int block_of(const Geo &g, int z, int y, int x) {
   return ((z / g.bz) * g.My + (y / g.by)) * g.Mx + (x / g.bx);

@@ -54,7 +54,7 @@ __global__ void k_geom_export(Geo g, const int32_t *coords, const int32_t *slot,
     for (int k = 0; k < 27; k++) {
       int zz = z + k / 9 - 1, yy = y + (k / 3) % 3 - 1, xx = x + k % 3 - 1;
       bool ok = in && zz >= 0 && yy >= 0 && xx >= 0 && zz < g.Z && yy < g.Y && xx < g.X;
-      nbr[(int64_t)i * 27 + k] = ok ? slot[site_of(g, zz, yy, xx)] : -1;
+      nbr[(int64_t)i * 27 + k] = ok ? slot_get(g, slot, site_of(g, zz, yy, xx)) : -1;
     }
   }
 }

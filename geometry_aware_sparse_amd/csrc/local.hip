@@ -57,7 +57,7 @@ __global__ __launch_bounds__(TZ *TY *TX) void k_local(Geo g, const void *geom, c
     const int hz = hs / (HY * HX), hy = (hs / HX) % HY, hx = hs % HX;
     const int z = z0 - 1 + hz, y = y0 - 1 + hy, x = x0 - 1 + hx;
     int j = -1;
-    if (z >= 0 && y >= 0 && x >= 0 && z < g.Z && y < g.Y && x < g.X) j = slot[site_of(g, z, y, x)];
+    if (z >= 0 && y >= 0 && x >= 0 && z < g.Z && y < g.Y && x < g.X) j = slot_get(g, slot, site_of(g, z, y, x));
     if (ch == 0) sSlot[hs] = j;
     float kv[CW], vv[CW];
     if (j >= 0) {
@@ -201,7 +201,7 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX,
       const int hz = hs / (HY * HX), hy = (hs / HX) % HY, hx = hs % HX;
       const int z = z0 - 1 + hz, y = y0 - 1 + hy, x = x0 - 1 + hx;
       const bool on = z >= 0 && y >= 0 && x >= 0 && z < g.Z && y < g.Y && x < g.X;
-      const int j = slot[on ? site_of(g, z, y, x) : 0];
+      const int j = slot_get(g, slot, on ? site_of(g, z, y, x) : 0);
       sv[r] = on ? j : -1;
     }
 #pragma unroll

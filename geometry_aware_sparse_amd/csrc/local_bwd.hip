@@ -110,7 +110,7 @@ __device__ __forceinline__ void stage_box(const Geo &g, const int32_t *slot, con
     const int hz = hs / (HY * HX), hy = (hs / HX) % HY, hx = hs % HX;
     const int z = z0 - 1 + hz, y = y0 - 1 + hy, x = x0 - 1 + hx;
     const bool on = z >= 0 && y >= 0 && x >= 0 && z < g.Z && y < g.Y && x < g.X;
-    const int j = slot[on ? site_of(g, z, y, x) : 0];
+    const int j = slot_get(g, slot, on ? site_of(g, z, y, x) : 0);
     sv[r] = on ? j : -1;
   }
 #pragma unroll

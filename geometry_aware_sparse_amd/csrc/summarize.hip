@@ -95,7 +95,7 @@ __global__ __launch_bounds__(512) void k_summarize(Geo g, const void *geom, cons
           const int z = (mm / (g.My * g.Mx)) * g.bz + rr / (g.by * g.bx);
           const int y = ((mm / g.Mx) % g.My) * g.by + (rr / g.bx) % g.by;
           const int x = (mm % g.Mx) * g.bx + rr % g.bx;
-          if (z < g.Z && y < g.Y && x < g.X) j = slot[site_of(g, z, y, x)];
+          if (z < g.Z && y < g.Y && x < g.X) j = slot_get(g, slot, site_of(g, z, y, x));
         }
         s_slot[e] = j;
       }
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(512, 5) void k_summarize_b8(Geo g, const void *geom
       for (int ss = 0; ss < 8; ss++) {
         const int z = oz[ss] + lz, y = oy[ss] + ly, x = ox[ss] + lx;
         const bool on = m0 + ss < g.M && z < g.Z && y < g.Y && x < g.X;
-        j[ss] = slot[on ? site_of(g, z, y, x) : 0];
+        j[ss] = slot_get(g, slot, on ? site_of(g, z, y, x) : 0);
         j[ss] = on ? j[ss] : -1;
       }
 #pragma unroll

@@ -54,6 +54,12 @@
  *    fail. Coordinate errors are detected on the device: kernels never read
  *    out of bounds, and the error is reported to the host only when
  *    desc->flags has PACK3D_VALIDATE (the call then synchronises the stream).
+ *  - Debug build (lib/libpack3d_debug.so, built by build.py --debug): every
+ *    slot-map read in every kernel is checked against the grid; one out of
+ *    range sets bit 2 of the status word and reads as an empty site. Under
+ *    PACK3D_VALIDATE, the entry points that run kernels reading the map
+ *    then synchronise once more at their end and return PACK3D_ERR_INTERNAL
+ *    if the bit is set. Results are otherwise those of the normal build.
  *  - Without PACK3D_VALIDATE a bad coordinate is resolved deterministically.
  *    A token whose coordinate is off the grid takes no part. A site claimed
  *    by several tokens goes to the lowest memory index among them, and the
@@ -94,7 +100,8 @@ typedef enum pack3d_status {
   PACK3D_ERR_WORKSPACE = -3,   /* workspace or saved buffer smaller than required  */
   PACK3D_ERR_UNSUPPORTED = -4, /* dtype / D / exclusion combination not built */
   PACK3D_ERR_HIP = -5,         /* a HIP launch or runtime call failed */
-  PACK3D_ERR_COORDS = -6       /* coordinate off the grid or duplicated (VALIDATE only) */
+  PACK3D_ERR_COORDS = -6,      /* coordinate off the grid or duplicated (VALIDATE only) */
+  PACK3D_ERR_INTERNAL = -7     /* debug builds only: a slot-map read out of range (VALIDATE) */
 } pack3d_status;
 
 typedef enum pack3d_dtype { PACK3D_F32 = 0, PACK3D_BF16 = 1 } pack3d_dtype;
@@ -153,7 +160,8 @@ int64_t pack3d_num_summaries(const pack3d_desc *desc);
  * Ch. 4, Prop. 2). It lives in one caller buffer `geom` of
  * pack3d_geometry_bytes() bytes, 256-byte aligned, laid out as:
  *   [0, 256)               int32 status word (bit 0: coordinate off the grid,
- *                          bit 1: coordinate duplicated); bytes [64, 128)
+ *                          bit 1: coordinate duplicated, bit 2: a debug
+ *                          build's bounds check fired); bytes [64, 128)
  *                          are zero (read in place of an absent block
  *                          member); the rest is padding
  *   [slot_offset, ...)     int32 slot map [Z*Y*X]: slot[(z*Y + y)*X + x] =

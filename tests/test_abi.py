@@ -31,12 +31,28 @@ def test_library_exports_every_declared_symbol(gas):
     assert sorted(gas.EXPORTED_SYMBOLS) == names
 
 
+def test_debug_build_loads_and_exports_the_same_symbols(gas):
+    """lib/libpack3d_debug.so (checked slot-map reads) is built beside the
+    library and declares the same ABI; inside debug_library() the binding
+    calls it."""
+    from geometry_aware_sparse_amd import _lib
+    assert os.path.exists(_lib.DEBUG_LIB_PATH)
+    dbg = C.CDLL(_lib.DEBUG_LIB_PATH)
+    for n in _declared():
+        assert hasattr(dbg, n), f"{n} missing from the debug build"
+    with _lib.debug_library() as L:
+        assert gas.library() is L
+        assert L.pack3d_abi_version() == 2
+        assert L.pack3d_strerror(-7) and b"debug" in L.pack3d_strerror(-7)
+    assert gas.library() is not L
+
+
 def test_version_and_strerror(gas):
     lib = gas.library()
     assert lib.pack3d_abi_version() == 2
     # the ctypes descriptor matches the C struct: kv_heads is the last field
     assert C.sizeof(gas.Desc) == 4 * 4 + 4 * 6 + 4 * 2 + 4 * 4
-    for code in (0, -1, -2, -3, -4, -5, -6, -99):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -99):
         assert lib.pack3d_strerror(code)
 
 
