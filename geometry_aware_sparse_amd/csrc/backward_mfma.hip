@@ -418,16 +418,15 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gk_mfma(
     rt_j8[r] = e / D;
     rt_d[r] = e % D;
   }
-  auto issue = [&](int it, bf16x8 *dQ, bf16x8 *dD, bf16x8 *dQT, bf16x8 *dDT, float *dL,
-                   float *dDl) {
+  // buffer resources of head h's slices: both query layouts are Np * D
+  // elements per head
+  auto rsrc = [&](const bf16 *base, int h) {
+    return buffer_rsrc(base + ((int64_t)b * g.H + h) * Np * D, Np * D * 2);
+  };
+  // the row-layout part of iteration it's query tile (q~, dO, -lse, -Delta)
+  auto issue_a = [&](int it, bf16x8 *dQ, bf16x8 *dD, float *dL, float *dDl) {
     const int h = hk * g.G + it / nq, qtile = qt0 + it % nq;
-    const int64_t bh = (int64_t)b * g.H + h;
-    // this head's slices: both query layouts are Np * D elements per head
-    const int32_t bytes = Np * D * 2;
-    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(qn + bh * Np * D, bytes);
-    const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(dn + bh * Np * D, bytes);
-    const __amdgpu_buffer_rsrc_t rqt = buffer_rsrc(qt + bh * Np * D, bytes);
-    const __amdgpu_buffer_rsrc_t rdt = buffer_rsrc(dt + bh * Np * D, bytes);
+    const __amdgpu_buffer_rsrc_t rq = rsrc(qn, h), rd = rsrc(dn, h);
 #pragma unroll
     for (int r = 0; r < RN; r++) {
       if (NTH * r + 64 * wv < NNC) {
@@ -436,6 +435,18 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gk_mfma(
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_ptr)&dD[NTH * r + 64 * wv], 16, o, 0, 0, 0);
       }
     }
+    // per-site statistics: wave 0 -lse, wave 1 -Delta (4 bytes a lane)
+    if (wv < 2) {
+      const int64_t bh = (int64_t)b * g.H + h;
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc((wv == 0 ? lse_p : dl_p) + bh * Np, Np * 4);
+      const uint32_t o = (uint32_t)(qtile * TQ + min(lane, TQ - 1)) * 4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(wv == 0 ? dL : dDl), 4, o, 0, 0, 0);
+    }
+  };
+  // the channel-major part (q~ and dO, 8 sites per chunk)
+  auto issue_b = [&](int it, bf16x8 *dQT, bf16x8 *dDT) {
+    const int h = hk * g.G + it / nq, qtile = qt0 + it % nq;
+    const __amdgpu_buffer_rsrc_t rqt = rsrc(qt, h), rdt = rsrc(dt, h);
 #pragma unroll
     for (int r = 0; r < RTT; r++) {
       if (NTH * r + 64 * wv < NTC) {
@@ -444,81 +455,216 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gk_mfma(
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rdt, (lds_ptr)&dDT[NTH * r + 64 * wv], 16, o, 0, 0, 0);
       }
     }
-    // per-site statistics: wave 0 -lse, wave 1 -Delta (4 bytes a lane)
-    if (wv < 2) {
-      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc((wv == 0 ? lse_p : dl_p) + bh * Np, Np * 4);
-      const uint32_t o = (uint32_t)(qtile * TQ + min(lane, TQ - 1)) * 4;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(wv == 0 ? dL : dDl), 4, o, 0, 0, 0);
-    }
   };
-  if (ntile > 0) issue(0, sQ0, sD0, sQT0, sDT0, sL0, sDl0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int it = 0; it < ntile; it++) {
-    const bool odd = it & 1;
-    if (it + 1 < ntile) {
-      if (odd) issue(it + 1, sQ0, sD0, sQT0, sDT0, sL0, sDl0);
-      else issue(it + 1, sQ1, sD1, sQT1, sDT1, sL1, sDl1);
-    }
-    const bf16x8 *Q = odd ? sQ1 : sQ0, *Dd = odd ? sD1 : sD0;
-    const bf16x8 *QT = odd ? sQT1 : sQT0, *DTt = odd ? sDT1 : sDT0;
-    const float *L = odd ? sL1 : sL0, *Dl = odd ? sDl1 : sDl0;
-    // the score products of every sub-tile of the tile first, so that each
-    // sub-tile's vector work runs while the matrix core still works on the
-    // next one's products (and on the previous one's accumulation)
-    // C[query rows][summary columns]: row r holds query site swap23(r), so
-    // register 8*c2 + e of half hi <-> site 32*sub + 16*c2 + 8*hi + e. The
-    // products start from -lse and -Delta of those sites.
-    f32x16 s[NSUB], dp[NSUB];
+  auto issue = [&](int it, bf16x8 *dQ, bf16x8 *dD, bf16x8 *dQT, bf16x8 *dDT, float *dL,
+                   float *dDl) {
+    issue_a(it, dQ, dD, dL, dDl);
+    issue_b(it, dQT, dDT);
+  };
+  if constexpr (NSUB == 2) {
+    // Three-stage pipeline over the 32-query sub-tiles of all iterations.
+    // Step j issues the dK/dV products of sub-tile j-2, runs the softmax of
+    // sub-tile j-1 while they execute, then issues the score and dP products
+    // of sub-tile j, and reads from LDS the fragments of the next step's
+    // products: the row layout of sub-tile j+1 and the channel-major layout
+    // of sub-tile j-1. Those two are two sub-tiles apart, so the
+    // channel-major tiles trail the row tiles by one: tile u holds the row
+    // part of iteration u and the channel-major part of iteration u-1, in
+    // buffer u & 1. Odd steps switch to tile u = (j+1)/2 after their score
+    // products (which read tile u-1): a barrier publishes tile u, and the
+    // loads of tile u+1 then go into the buffers of tile u-1. Only one score
+    // tile is live at a time: the softmax empties it before the start values
+    // of the next sub-tile go in.
+    const int S = 2 * ntile;
+    auto issue_tile = [&](int u, auto par) {
+      constexpr int P = decltype(par)::value;
+      if (u < ntile) issue_a(u, P ? sQ1 : sQ0, P ? sD1 : sD0, P ? sL1 : sL0, P ? sDl1 : sDl0);
+      if (u >= 1 && u - 1 < ntile) issue_b(u - 1, P ? sQT1 : sQT0, P ? sDT1 : sDT0);
+    };
+    f32x16 s, dp;                // scores and dP of one sub-tile
+    bf16x8 pa[2], ta[2];         // P and dT of the sub-tile the softmax last produced
+    bf16x8 qa[KD], da[KD];       // score / dP operands of the next sub-tile
+    bf16x8 qb[DT][2], db[DT][2]; // dK / dV operands of the next sub-tile
+    // the q~ and dO fragments of the sub-tile at position POS of a tile
+    auto read_sd = [&](auto par, auto pos) {
+      constexpr int P = decltype(par)::value, POS = decltype(pos)::value;
+      const bf16x8 *Q = P ? sQ1 : sQ0, *Dd = P ? sD1 : sD0;
 #pragma unroll
-    for (int sub = 0; sub < NSUB; sub++) {
+      for (int c = 0; c < KD; c++) {
+        qa[c] = Q[(2 * c + hi) * TQ + 32 * POS + l32];
+        da[c] = Dd[(2 * c + hi) * TQ + 32 * POS + l32];
+      }
+    };
+    // -lse and -Delta of its sites, the start values of the products:
+    // register 8*c2 + e of half hi <-> site 32*POS + 16*c2 + 8*hi + e
+    auto read_init = [&](auto par, auto pos) {
+      constexpr int P = decltype(par)::value, POS = decltype(pos)::value;
+      const float *L = P ? sL1 : sL0, *Dl = P ? sDl1 : sDl0;
 #pragma unroll
       for (int c2 = 0; c2 < 2; c2++)
 #pragma unroll
         for (int hq = 0; hq < 2; hq++) {
-          const int q0 = 32 * sub + 16 * c2 + 8 * hi + 4 * hq;
+          const int q0 = 32 * POS + 16 * c2 + 8 * hi + 4 * hq;
           const f32x4 l4 = *reinterpret_cast<const f32x4 *>(L + q0);
           const f32x4 d4 = *reinterpret_cast<const f32x4 *>(Dl + q0);
 #pragma unroll
           for (int u = 0; u < 4; u++) {
-            s[sub][8 * c2 + 4 * hq + u] = l4[u];
-            dp[sub][8 * c2 + 4 * hq + u] = d4[u];
+            s[8 * c2 + 4 * hq + u] = l4[u];
+            dp[8 * c2 + 4 * hq + u] = d4[u];
           }
         }
-#pragma unroll
-      for (int c = 0; c < KD; c++) {
-        const bf16x8 qa = Q[(2 * c + hi) * TQ + 32 * sub + l32];
-        const bf16x8 da = Dd[(2 * c + hi) * TQ + 32 * sub + l32];
-        s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb[c], s[sub], 0, 0, 0);
-        dp[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vb[c], dp[sub], 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int sub = 0; sub < NSUB; sub++) {
-      bf16x8 pa[2], ta[2];
-#pragma unroll
-      for (int c2 = 0; c2 < 2; c2++)
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-          const float pr = __builtin_amdgcn_exp2f(s[sub][8 * c2 + e]);
-          pa[c2][e] = (bf16)pr;
-          ta[c2][e] = (bf16)(pr * dp[sub][8 * c2 + e]);
-        }
+    };
+    auto read_kv = [&](auto par, auto pos) {
+      constexpr int P = decltype(par)::value, POS = decltype(pos)::value;
+      const bf16x8 *QT = P ? sQT1 : sQT0, *DTt = P ? sDT1 : sDT0;
 #pragma unroll
       for (int t = 0; t < DT; t++) {
         const int d = min(32 * t + l32, D - 1);
 #pragma unroll
         for (int c2 = 0; c2 < 2; c2++) {
-          const int j8 = 4 * sub + 2 * c2 + hi;
-          const bf16x8 qb = QT[j8 * D + d];
-          const bf16x8 db = DTt[j8 * D + d];
-          aK[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[c2], qb, aK[t], 0, 0, 0);
-          aV[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[c2], db, aV[t], 0, 0, 0);
+          const int j8 = 4 * POS + 2 * c2 + hi;
+          qb[t][c2] = QT[j8 * D + d];
+          db[t][c2] = DTt[j8 * D + d];
         }
       }
-    }
+    };
+    issue_tile(0, std::integral_constant<int, 0>{});
+    issue_tile(1, std::integral_constant<int, 1>{});
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (S > 0) read_sd(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    // one step; JJ = position in a group of four steps (two tiles)
+    auto step = [&](int grp, auto jc, auto fc) {
+      constexpr int JJ = decltype(jc)::value;
+      constexpr bool FULL = decltype(fc)::value;  // every part of the step exists
+      constexpr int TC = (JJ / 2) & 1, PC = JJ % 2;              // tile, position of sub-tile j
+      constexpr int TN = ((JJ + 1) / 2) & 1, PN = (JJ + 1) % 2;  // of sub-tile j+1
+      constexpr bool SWITCH = PN == 0;
+      const int j = 4 * grp + JJ;
+      __builtin_amdgcn_sched_barrier(0);
+      if (FULL || (j >= 2 && j - 2 < S)) {
+#pragma unroll
+        for (int t = 0; t < DT; t++)
+#pragma unroll
+          for (int c2 = 0; c2 < 2; c2++) {
+            aK[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[c2], qb[t][c2], aK[t], 0, 0, 0);
+            aV[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[c2], db[t][c2], aV[t], 0, 0, 0);
+          }
+      }
+      if (FULL || (j >= 1 && j - 1 < S)) {
+#pragma unroll
+        for (int c2 = 0; c2 < 2; c2++)
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const float pr = __builtin_amdgcn_exp2f(s[8 * c2 + e]);
+            pa[c2][e] = (bf16)pr;
+            ta[c2][e] = (bf16)(pr * dp[8 * c2 + e]);
+          }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (FULL || j < S) {
+        read_init(std::integral_constant<int, TC>{}, std::integral_constant<int, PC>{});
+#pragma unroll
+        for (int c = 0; c < KD; c++) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[c], kb[c], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[c], vb[c], dp, 0, 0, 0);
+        }
+      }
+      if constexpr (SWITCH) {
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads landed, its LDS reads done
+        __syncthreads();
+        issue_tile(2 * grp + (JJ + 1) / 2 + 1,
+                   std::integral_constant<int, ((JJ + 1) / 2 + 1) & 1>{});
+      }
+      if (FULL || j + 1 < S)
+        read_sd(std::integral_constant<int, TN>{}, std::integral_constant<int, PN>{});
+      if (FULL || (j >= 1 && j - 1 < S))
+        read_kv(std::integral_constant<int, TN>{}, std::integral_constant<int, PN>{});
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // groups whose four steps are whole (2 <= j and j + 1 < S) run without
+    // checks; the first and the last ones check each part
+    auto group = [&](int grp, auto fc) {
+      step(grp, std::integral_constant<int, 0>{}, fc);
+      step(grp, std::integral_constant<int, 1>{}, fc);
+      step(grp, std::integral_constant<int, 2>{}, fc);
+      step(grp, std::integral_constant<int, 3>{}, fc);
+    };
+    const int ngrp = (S + 2 + 3) / 4;  // steps 0 .. S+1
+    int grp = 0;
+    if (ngrp > 0) group(grp++, std::false_type{});
+    for (; 4 * grp + 4 < S; grp++) group(grp, std::true_type{});
+    for (; grp < ngrp; grp++) group(grp, std::false_type{});
+  } else {
+    if (ntile > 0) issue(0, sQ0, sD0, sQT0, sDT0, sL0, sDl0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int it = 0; it < ntile; it++) {
+      const bool odd = it & 1;
+      if (it + 1 < ntile) {
+        if (odd) issue(it + 1, sQ0, sD0, sQT0, sDT0, sL0, sDl0);
+        else issue(it + 1, sQ1, sD1, sQT1, sDT1, sL1, sDl1);
+      }
+      const bf16x8 *Q = odd ? sQ1 : sQ0, *Dd = odd ? sD1 : sD0;
+      const bf16x8 *QT = odd ? sQT1 : sQT0, *DTt = odd ? sDT1 : sDT0;
+      const float *L = odd ? sL1 : sL0, *Dl = odd ? sDl1 : sDl0;
+      // the score products of every sub-tile of the tile first, so that each
+      // sub-tile's vector work runs while the matrix core still works on the
+      // next one's products (and on the previous one's accumulation)
+      // C[query rows][summary columns]: row r holds query site swap23(r), so
+      // register 8*c2 + e of half hi <-> site 32*sub + 16*c2 + 8*hi + e. The
+      // products start from -lse and -Delta of those sites.
+      f32x16 s[NSUB], dp[NSUB];
+  #pragma unroll
+      for (int sub = 0; sub < NSUB; sub++) {
+  #pragma unroll
+        for (int c2 = 0; c2 < 2; c2++)
+  #pragma unroll
+          for (int hq = 0; hq < 2; hq++) {
+            const int q0 = 32 * sub + 16 * c2 + 8 * hi + 4 * hq;
+            const f32x4 l4 = *reinterpret_cast<const f32x4 *>(L + q0);
+            const f32x4 d4 = *reinterpret_cast<const f32x4 *>(Dl + q0);
+  #pragma unroll
+            for (int u = 0; u < 4; u++) {
+              s[sub][8 * c2 + 4 * hq + u] = l4[u];
+              dp[sub][8 * c2 + 4 * hq + u] = d4[u];
+            }
+          }
+  #pragma unroll
+        for (int c = 0; c < KD; c++) {
+          const bf16x8 qa = Q[(2 * c + hi) * TQ + 32 * sub + l32];
+          const bf16x8 da = Dd[(2 * c + hi) * TQ + 32 * sub + l32];
+          s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb[c], s[sub], 0, 0, 0);
+          dp[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vb[c], dp[sub], 0, 0, 0);
+        }
+      }
+  #pragma unroll
+      for (int sub = 0; sub < NSUB; sub++) {
+        bf16x8 pa[2], ta[2];
+  #pragma unroll
+        for (int c2 = 0; c2 < 2; c2++)
+  #pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const float pr = __builtin_amdgcn_exp2f(s[sub][8 * c2 + e]);
+            pa[c2][e] = (bf16)pr;
+            ta[c2][e] = (bf16)(pr * dp[sub][8 * c2 + e]);
+          }
+  #pragma unroll
+        for (int t = 0; t < DT; t++) {
+          const int d = min(32 * t + l32, D - 1);
+  #pragma unroll
+          for (int c2 = 0; c2 < 2; c2++) {
+            const int j8 = 4 * sub + 2 * c2 + hi;
+            const bf16x8 qb = QT[j8 * D + d];
+            const bf16x8 db = DTt[j8 * D + d];
+            aK[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[c2], qb, aK[t], 0, 0, 0);
+            aV[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[c2], db, aV[t], 0, 0, 0);
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   }
   if (!wave_live) return;
   // lane: channel column 32t + l32, rows = summaries 8jj + 4hi + u of the group
