@@ -526,20 +526,26 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX, 2) void k_bwd_local_kv_pair(
 
 // ---------------------------------------------------------------------------
 namespace {
-template <int D, int TZ, int TY, int TX>
+// The query side and the key side may use different boxes (KZ, KY, KX for
+// the key side).
+template <int D, int TZ, int TY, int TX, int KZ, int KY, int KX>
 hipError_t run_local_bwd_pair(const Geo &g, const BwdArgs &a, hipStream_t s) {
-  const int ntz = (g.Z + TZ - 1) / TZ, nty = (g.Y + TY - 1) / TY, ntx = (g.X + TX - 1) / TX;
-  const int nt = (D / 24) * TZ * TY * TX;
-  hipLaunchKernelGGL((k_bwd_local_q_pair<D, TZ, TY, TX>),
-                     dim3((unsigned)(g.B * ntz * nty * ntx * g.H)), dim3(nt), 0, s, g, a.geom,
-                     static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.k),
-                     static_cast<const bf16 *>(a.v), static_cast<const bf16 *>(a.gate),
-                     static_cast<const bf16 *>(a.dout), static_cast<const bf16 *>(a.oglob), a.dqg,
-                     static_cast<bf16 *>(a.dq), static_cast<bf16 *>(a.dgate), a.lse_l, a.delta_l,
-                     ntz, nty, ntx);
-  if (hipError_t e = hipGetLastError()) return e;
-  auto kv = (g.flags & PACK3D_SUMMARY_CENTRE) ? k_bwd_local_kv_pair<D, TZ, TY, TX, true>
-                                               : k_bwd_local_kv_pair<D, TZ, TY, TX, false>;
+  {
+    const int ntz = (g.Z + TZ - 1) / TZ, nty = (g.Y + TY - 1) / TY, ntx = (g.X + TX - 1) / TX;
+    const int nt = (D / 24) * TZ * TY * TX;
+    hipLaunchKernelGGL((k_bwd_local_q_pair<D, TZ, TY, TX>),
+                       dim3((unsigned)(g.B * ntz * nty * ntx * g.H)), dim3(nt), 0, s, g, a.geom,
+                       static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.k),
+                       static_cast<const bf16 *>(a.v), static_cast<const bf16 *>(a.gate),
+                       static_cast<const bf16 *>(a.dout), static_cast<const bf16 *>(a.oglob), a.dqg,
+                       static_cast<bf16 *>(a.dq), static_cast<bf16 *>(a.dgate), a.lse_l, a.delta_l,
+                       ntz, nty, ntx);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  const int ntz = (g.Z + KZ - 1) / KZ, nty = (g.Y + KY - 1) / KY, ntx = (g.X + KX - 1) / KX;
+  const int nt = (D / 24) * KZ * KY * KX;
+  auto kv = (g.flags & PACK3D_SUMMARY_CENTRE) ? k_bwd_local_kv_pair<D, KZ, KY, KX, true>
+                                               : k_bwd_local_kv_pair<D, KZ, KY, KX, false>;
   hipLaunchKernelGGL(kv, dim3((unsigned)(g.B * ntz * nty * ntx * g.Hkv)), dim3(nt), 0, s, g, a.geom,
                      static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.k),
                      static_cast<const bf16 *>(a.v), static_cast<const bf16 *>(a.gate),
@@ -554,8 +560,11 @@ bool bwd_local_pair_supported(const Geo &g, int dtype) {
 }
 
 hipError_t launch_bwd_local_pair(const Geo &g, const BwdArgs &a, hipStream_t s) {
-  if (g.D == 48) return run_local_bwd_pair<48, 4, 4, 8>(g, a, s);
-  return run_local_bwd_pair<96, 2, 4, 8>(g, a, s);
+  if (g.D == 48) return run_local_bwd_pair<48, 4, 4, 8, 4, 4, 8>(g, a, s);
+  // D = 96: the key side stages two halo tensors (q~ and dO); with 2 x 4 x 8
+  // boxes (4 waves, 102 KB of LDS) one workgroup fits a CU, one wave per
+  // SIMD; 4 x 4 x 8 boxes (8 waves, 152 KB) give two waves per SIMD
+  return run_local_bwd_pair<96, 2, 4, 8, 4, 4, 8>(g, a, s);
 }
 
 }  // namespace pk
