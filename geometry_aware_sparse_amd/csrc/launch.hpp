@@ -84,17 +84,13 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
 struct BoxWork {
   int b, h, tz, ty, tx;
 };
-#ifndef PK_SUPERBLOCK
-#define PK_SUPERBLOCK 4
-#endif
 __device__ __forceinline__ BoxWork box_work(int w, int nh, int ntz, int nty, int ntx) {
   const int h = w % nh;
   w /= nh;
   const int ntiles = ntz * nty * ntx;
   const int b = w / ntiles;
   int r = w - b * ntiles;
-  constexpr int S = PK_SUPERBLOCK;
-  if (S <= 1) return {b, h, r / (nty * ntx), (r / ntx) % nty, r % ntx};
+  constexpr int S = 4;  // cube edge, in boxes
   const int bz = r / (S * nty * ntx);  // slab of cubes; those before it are whole
   r -= bz * S * nty * ntx;
   const int nz = min(S, ntz - bz * S);
