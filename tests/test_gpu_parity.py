@@ -37,6 +37,14 @@ CASES = [
     W(112, "gqa6x3_f32_d24", (5, 7, 9), 2, 6, 24, (2, 2, 3), "f32", "iid", "block", "random", Hkv=3),
     W(113, "gqa8x2_bf16_d48", (12, 16, 20), 1, 8, 48, (2, 2, 2), "bf16", "iid", "block", "random",
       Hkv=2),
+    # bf16 token rows wider than 512 elements (12 heads x 48): the pooling
+    # pass takes its generic form
+    W(116, "wide_rows_bf16_h12_d48", (5, 6, 7), 1, 12, 48, (2, 2, 2), "bf16", "iid", "random",
+      "raster"),
+    # one block spans the whole grid (M = 1, padded to 32 summaries): the
+    # pooling pass stages its 2,048 members in several passes
+    W(117, "one_big_block_bf16_d48", (8, 16, 16), 1, 2, 48, (8, 16, 16), "bf16", "iid", "random",
+      "raster"),
 ]
 IDS = [c.name for c in CASES]
 BY_NAME = {c.name: c for c in CASES}
