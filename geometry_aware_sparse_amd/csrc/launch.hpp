@@ -19,6 +19,10 @@ hipError_t launch_summarize(const Geo &g, int dtype, const void *geom, const voi
                             const void *v, void *ks, void *vs, hipStream_t s);
 // gate / oglob may be null (plain local output); when set the kernel writes
 // (1-g)*O_local + g*O_global. oglob may equal out.
+// bf16, D = 48: the local branch with its value sums on the matrix cores
+hipError_t launch_local_tr48(const Geo &g, const void *geom, const void *q, const void *k,
+                             const void *v, const void *gate, const void *og, void *out,
+                             hipStream_t s);
 hipError_t launch_local(const Geo &g, int dtype, const void *geom, const void *q, const void *k,
                         const void *v, const void *gate, const void *oglob, void *out,
                         hipStream_t s, bool *supported);

@@ -410,8 +410,7 @@ hipError_t launch_local(const Geo &g, int dtype, const void *geom, const void *q
       case 6: return run_local<bf16, 6, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
       case 12: return run_local<bf16, 12, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
       case 24: return run_local<bf16, 24, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
-      case 48:
-        return run_local_pair<48, 4, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
+      case 48: return launch_local_tr48(g, geom, q, k, v, gate, oglob, out, s);
       case 96: return run_local_pair<96, 2, 4, 8>(g, geom, q, k, v, gate, oglob, out, s);
     }
   } else {
