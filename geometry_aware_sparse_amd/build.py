@@ -23,6 +23,13 @@ DEBUG_OBJDIR = os.path.join(ROOT, "_build", "pack3d_debug")
 DEBUG_LIB = os.path.join(PKG, "lib", "libpack3d_debug.so")
 DEBUG_FLAGS = ["-DPK_DEBUG_BOUNDS"]
 ARCH = "gfx950"
+# Per-file code generation flags.
+FILE_FLAGS = {
+    # Matrix accumulators in ordinary VGPRs (no AGPR split): the local
+    # kernel's pipelined key reads need 155 registers, which fit three waves
+    # per SIMD as one file and two as 156 VGPRs + 32 AGPRs.
+    "local_tr.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -42,7 +49,8 @@ def _hipcc():
 def _compile(job):
     src, objdir, extra = job
     obj = os.path.join(objdir, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *HIPCC_FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src,
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -46,6 +46,7 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s *lds_v4s;
 }  // namespace
 
+template <bool MIX>
 __global__ __launch_bounds__(256, 1) void k_local_tr48(
     Geo g, const void *geom, const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const bf16 *__restrict__ v, const bf16 *gate, const bf16 *oglob, bf16 *out, int ntz, int nty,
@@ -62,6 +63,7 @@ __global__ __launch_bounds__(256, 1) void k_local_tr48(
   // real rows, so every operand read stays in the buffer and finite.
   __shared__ __attribute__((aligned(16))) bf16 sbuf[RS * NT * 8];
   __shared__ int sSlot[NH];
+  __shared__ float sBias[NH];  // 0 for a site with a token, -inf for one without
   // the furthest operand read: padding site 63 of the last plane, channel 63
   static_assert(((HZ - 1) * NPL + 64) * D + (64 - D) <= RS * NT * 8,
                 "padding sites and channels stay in the buffer");
@@ -72,6 +74,11 @@ __global__ __launch_bounds__(256, 1) void k_local_tr48(
   const int32_t *slot = slot_map(geom, g);
   const float2 *tab = rope_table(geom, g);
   const int64_t bN = (int64_t)b * g.N;
+  // this (batch, KV head)'s rows: token j's row starts j * rstride bytes in
+  const int64_t kvbase = (bN * g.Hkv + h / g.G) * D;
+  const char *kb = reinterpret_cast<const char *>(k + kvbase);
+  const char *vb = reinterpret_cast<const char *>(v + kvbase);
+  const uint32_t rstride = (uint32_t)g.Hkv * D * sizeof(bf16);
   {
     constexpr int RSL = (NH + NT - 1) / NT;
     int sv[RSL];
@@ -86,7 +93,10 @@ __global__ __launch_bounds__(256, 1) void k_local_tr48(
     }
 #pragma unroll
     for (int r = 0; r < RSL; r++)
-      if ((int)threadIdx.x + r * NT < NH) sSlot[threadIdx.x + r * NT] = sv[r];
+      if ((int)threadIdx.x + r * NT < NH) {
+        sSlot[threadIdx.x + r * NT] = sv[r];
+        sBias[threadIdx.x + r * NT] = sv[r] >= 0 ? 0.f : -INFINITY;
+      }
   }
   __syncthreads();
 
@@ -102,35 +112,25 @@ __global__ __launch_bounds__(256, 1) void k_local_tr48(
   const int i = sSlot[((tz + 1) * HY + (ty + 1)) * HX + (tx + 1)];
   const int wbase = __builtin_amdgcn_readfirstlane(threadIdx.x & ~63);
 
-  // Every global load goes out before any is waited for: key chunks straight
-  // into LDS, value chunks into registers, this lane's query slices, the
-  // one-step (cos, sin) of its planes and, for the fused mix, its O_glob
-  // slices and gate. A site off the grid reads token 0 (only finiteness
-  // matters: its weight is exactly 0).
+  // The loads the logits wait for go out together: key chunks straight into
+  // LDS, value chunks into registers, this lane's query slices and the
+  // one-step (cos, sin) of its planes. A site off the grid reads token 0
+  // (only finiteness matters: its weight is exactly 0).
   bf16x8 vraw[RS];
 #pragma unroll
   for (int r = 0; r < RS; r++) {
     const int e = min((int)threadIdx.x + r * NT, NCK - 1);
     const int hs = e / CPS, ch = e % CPS;
-    const int64_t off = ((bN + max(sSlot[hs], 0)) * g.Hkv + h / g.G) * D + ch * 8;  // KV head of h
-    __builtin_amdgcn_global_load_lds(k + off, (lds_ptr)&sbuf[(wbase + r * NT) * 8], 16, 0, 0);
-    vraw[r] = *reinterpret_cast<const bf16x8 *>(v + off);
+    const uint64_t off = (uint64_t)(uint32_t)max(sSlot[hs], 0) * rstride + (uint32_t)ch * 16u;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(kb + off),
+                                     (lds_ptr)&sbuf[(wbase + r * NT) * 8], 16, 0, 0);
+    vraw[r] = *reinterpret_cast<const bf16x8 *>(vb + off);
   }
   const int64_t row = ((bN + max(i, 0)) * g.H + h) * D;
   const int64_t rowL = ((bN + max(iL, 0)) * g.H + h) * D;
   bf16x8 qraw[3];
 #pragma unroll
   for (int a = 0; a < 3; a++) qraw[a] = *reinterpret_cast<const bf16x8 *>(q + rowL + a * DA + 8 * hh);
-  // this lane's output channels once the halves have traded pieces (below):
-  // 16*m + 8*hi .. +7 for m = 0, 1, 2
-  bf16x8 ograw[3];
-  float gl = 0.f;
-  if (gate) {
-#pragma unroll
-    for (int m = 0; m < 3; m++)
-      ograw[m] = *reinterpret_cast<const bf16x8 *>(oglob + row + 16 * m + 8 * hi);
-    gl = (float)gate[(bN + max(i, 0)) * g.H + h];
-  }
   float2 cs1[3][4];
 #pragma unroll
   for (int a = 0; a < 3; a++) {
@@ -140,6 +140,18 @@ __global__ __launch_bounds__(256, 1) void k_local_tr48(
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // The fused mix's O_glob slices and gate go out only now: issued with the
+  // gathers above they delay them, and they are not needed before the end.
+  // They hold this lane's output channels once the halves have traded
+  // pieces (below): 16*m + 8*hi .. +7 for m = 0, 1, 2.
+  bf16x8 ograw[3];
+  float gl = 0.f;
+  if constexpr (MIX) {
+#pragma unroll
+    for (int m = 0; m < 3; m++)
+      ograw[m] = *reinterpret_cast<const bf16x8 *>(oglob + row + 16 * m + 8 * hi);
+    gl = (float)gate[(bN + max(i, 0)) * g.H + h];
+  }
   const float qscale = g.scale * kLog2e;
 
   // query slices, scaled, rotated by the relative angles -1, 0, +1 of each axis
@@ -158,25 +170,46 @@ __global__ __launch_bounds__(256, 1) void k_local_tr48(
       }
     }
 
-  // logits (log2 units) in canonical offset order k = (dz+1)*9 + (dy+1)*3 + dx+1
+  // logits (log2 units) in canonical offset order k = (dz+1)*9 + (dy+1)*3 + dx+1.
+  // The key slices of neighbour k + PF are read while neighbour k is summed
+  // (each step its own scheduling region), so LDS latency hides under the
+  // dot products instead of stalling every neighbour.
+  constexpr int PF = 2;
   float lg[27];
   float mx = -INFINITY;
+  bf16x8 kbuf[PF + 1][3];
+  float bbuf[PF + 1];
+  auto kload = [&](int kk, bf16x8 *dst, float &bias) {
+    const int hs = qsL + (kk / 9 - 1) * NPL + ((kk / 3) % 3 - 1) * HX + kk % 3 - 1;
+#pragma unroll
+    for (int a = 0; a < 3; a++) dst[a] = *reinterpret_cast<const bf16x8 *>(sbuf + hs * D + a * DA + 8 * hh);
+    bias = sBias[hs];
+  };
+#pragma unroll
+  for (int kk = 0; kk < PF; kk++) kload(kk, kbuf[kk], bbuf[kk]);
 #pragma unroll
   for (int kk = 0; kk < 27; kk++) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (kk + PF < 27) kload(kk + PF, kbuf[(kk + PF) % (PF + 1)], bbuf[(kk + PF) % (PF + 1)]);
     const int dd[3] = {kk / 9 - 1, (kk / 3) % 3 - 1, kk % 3 - 1};
-    const int hs = qsL + dd[0] * NPL + dd[1] * HX + dd[2];
-    const bf16x2 *kr = reinterpret_cast<const bf16x2 *>(sbuf + hs * D + 8 * hh);
+    const bf16x8 *kr = kbuf[kk % (PF + 1)];
     float acc = 0.f;
 #pragma unroll
     for (int a = 0; a < 3; a++)
 #pragma unroll
-      for (int u = 0; u < 4; u++)
-        acc = __builtin_amdgcn_fdot2_f32_bf16(qv[a][dd[a] + 1][u], kr[a * (DA / 2) + u], acc, false);
-    acc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, acc), 0xB1,
-                                                               0xf, 0xf, false));  // quad_perm 1,0,3,2
-    lg[kk] = sSlot[hs] >= 0 ? acc : -INFINITY;
+      for (int u = 0; u < 4; u++) {
+        bf16x2 kp;
+        kp[0] = kr[a][2 * u];
+        kp[1] = kr[a][2 * u + 1];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(qv[a][dd[a] + 1][u], kp, acc, false);
+      }
+    acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc),
+                                                                  0xB1, 0xf, 0xf,
+                                                                  true));  // quad_perm 1,0,3,2
+    lg[kk] = acc + bbuf[kk % (PF + 1)];
     mx = fmaxf(mx, lg[kk]);
   }
+  __builtin_amdgcn_sched_barrier(0);
   // the keys are no longer read: the buffer takes the values, row-major
   __syncthreads();
 #pragma unroll
@@ -186,6 +219,8 @@ __global__ __launch_bounds__(256, 1) void k_local_tr48(
   // words (p-, p0) and (p+, 0); the denominator sums the same bf16 weights
   uint32_t tev[9][2];
   float den = 0.f;
+  bf16x2 ones;
+  ones[0] = ones[1] = (bf16)1.0f;
 #pragma unroll
   for (int r9 = 0; r9 < 9; r9++) {
     bf16x2 t0, t1;
@@ -193,7 +228,8 @@ __global__ __launch_bounds__(256, 1) void k_local_tr48(
     t0[1] = (bf16)__builtin_amdgcn_exp2f(lg[3 * r9 + 1] - mx);
     t1[0] = (bf16)__builtin_amdgcn_exp2f(lg[3 * r9 + 2] - mx);
     t1[1] = (bf16)0.0f;
-    den += (float)t0[0] + (float)t0[1] + (float)t1[0];
+    den = __builtin_amdgcn_fdot2_f32_bf16(t0, ones, den, false);  // exact products
+    den = __builtin_amdgcn_fdot2_f32_bf16(t1, ones, den, false);
     tev[r9][0] = __builtin_bit_cast(uint32_t, t0);
     tev[r9][1] = __builtin_bit_cast(uint32_t, t1);
   }
@@ -265,6 +301,9 @@ __global__ __launch_bounds__(256, 1) void k_local_tr48(
   // query n (tile jj / 4, registers 4*(jj % 4) ..). The two halves trade
   // pieces so that each lane holds 8 consecutive channels 16*m + 8*hi .. +7:
   // whole 16-byte pieces of the row for the O_glob reads and the stores.
+  // v_permlane32_swap exchanges lanes 32..63 of its first operand with
+  // lanes 0..31 of its second: with (piece 2m, piece 2m + 1) as operands the
+  // first result is channels 16m + 8hi .. +3 and the second the 4 after them.
   const float inv = 1.0f / den;
   float oc[3][8];
 #pragma unroll
@@ -273,19 +312,28 @@ __global__ __launch_bounds__(256, 1) void k_local_tr48(
     for (int u = 0; u < 4; u++) {
       const float e0 = acc2[(2 * m) / 4][4 * ((2 * m) % 4) + u];          // piece 2m
       const float e1 = acc2[(2 * m + 1) / 4][4 * ((2 * m + 1) % 4) + u];  // piece 2m + 1
-      const float got = __shfl_xor(hi ? e0 : e1, 32);
-      oc[m][u] = hi ? got : e0;
-      oc[m][4 + u] = hi ? e1 : got;
+      const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, e0),
+                                                       __builtin_bit_cast(uint32_t, e1), false,
+                                                       false);
+      oc[m][u] = __builtin_bit_cast(float, (uint32_t)sw[0]);
+      oc[m][4 + u] = __builtin_bit_cast(float, (uint32_t)sw[1]);
     }
   if (i < 0) return;
-  const float gg = gate ? 1.0f / (1.0f + expf(-gl)) : 0.f;
+  // O = (1 - g) * acc / den + g * O_glob, with (1 - g) / den taken once
+  float gg = 0.f, sl = inv;
+  if constexpr (MIX) {
+    gg = 1.0f / (1.0f + expf(-gl));
+    sl = (1.0f - gg) * inv;
+  }
 #pragma unroll
   for (int m = 0; m < 3; m++) {
     bf16x8 r;
 #pragma unroll
     for (int u = 0; u < 8; u++) {
-      const float o = oc[m][u] * inv;
-      r[u] = (bf16)(gate ? (1.0f - gg) * o + gg * (float)ograw[m][u] : o);
+      if constexpr (MIX)
+        r[u] = (bf16)fmaf(oc[m][u], sl, gg * (float)ograw[m][u]);
+      else
+        r[u] = (bf16)(oc[m][u] * sl);
     }
     *reinterpret_cast<bf16x8 *>(out + row + 16 * m + 8 * hi) = r;
   }
@@ -296,10 +344,12 @@ hipError_t launch_local_tr48(const Geo &g, const void *geom, const void *q, cons
                              hipStream_t s) {
   const int ntz = (g.Z + 3) / 4, nty = (g.Y + 3) / 4, ntx = (g.X + 7) / 8;
   const int64_t nwg = (int64_t)g.B * ntz * nty * ntx * g.H;
-  hipLaunchKernelGGL(k_local_tr48, dim3((unsigned)nwg), dim3(256), 0, s, g, geom,
-                     static_cast<const bf16 *>(q), static_cast<const bf16 *>(k),
-                     static_cast<const bf16 *>(v), static_cast<const bf16 *>(gate),
-                     static_cast<const bf16 *>(og), static_cast<bf16 *>(out), ntz, nty, ntx);
+  const bool mix = gate != nullptr;
+  hipLaunchKernelGGL(mix ? k_local_tr48<true> : k_local_tr48<false>, dim3((unsigned)nwg),
+                     dim3(256), 0, s, g, geom, static_cast<const bf16 *>(q),
+                     static_cast<const bf16 *>(k), static_cast<const bf16 *>(v),
+                     static_cast<const bf16 *>(gate), static_cast<const bf16 *>(og),
+                     static_cast<bf16 *>(out), ntz, nty, ntx);
   return hipGetLastError();
 }
 
