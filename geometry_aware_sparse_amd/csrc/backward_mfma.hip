@@ -579,24 +579,33 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gk_mfma(
           }
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (FULL || j < S) {
+      // The next step's dK / dV operands (sub-tile j-1) are read as early as
+      // their tile allows: in a step without a switch that tile is published
+      // already, so they go out before this step's score products.
+      if constexpr (!SWITCH)
+        if (FULL || (j >= 1 && j - 1 < S))
+          read_kv(std::integral_constant<int, TN>{}, std::integral_constant<int, PN>{});
+      if (FULL || j < S)
         read_init(std::integral_constant<int, TC>{}, std::integral_constant<int, PC>{});
+      if constexpr (SWITCH) {
+        // read_init above was the last read of tile u-1; the score products
+        // below use operands already in registers
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads landed, its LDS reads done
+        __syncthreads();
+        issue_tile(2 * grp + (JJ + 1) / 2 + 1,
+                   std::integral_constant<int, ((JJ + 1) / 2 + 1) & 1>{});
+        if (FULL || (j >= 1 && j - 1 < S))
+          read_kv(std::integral_constant<int, TN>{}, std::integral_constant<int, PN>{});
+      }
+      if (FULL || j < S) {
 #pragma unroll
         for (int c = 0; c < KD; c++) {
           s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[c], kb[c], s, 0, 0, 0);
           dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[c], vb[c], dp, 0, 0, 0);
         }
       }
-      if constexpr (SWITCH) {
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads landed, its LDS reads done
-        __syncthreads();
-        issue_tile(2 * grp + (JJ + 1) / 2 + 1,
-                   std::integral_constant<int, ((JJ + 1) / 2 + 1) & 1>{});
-      }
       if (FULL || j + 1 < S)
         read_sd(std::integral_constant<int, TN>{}, std::integral_constant<int, PN>{});
-      if (FULL || (j >= 1 && j - 1 < S))
-        read_kv(std::integral_constant<int, TN>{}, std::integral_constant<int, PN>{});
       __builtin_amdgcn_sched_barrier(0);
     };
     // groups whose four steps are whole (2 <= j and j + 1 < S) run without
