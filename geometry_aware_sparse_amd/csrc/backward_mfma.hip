@@ -297,6 +297,144 @@ __global__ __launch_bounds__(64 * NW, G == 1 ? 2 : 1) void k_bwd_gq_mfma(
       }
     }
   };
+  if constexpr (G == 1 && NSUB == 4) {
+    // Three-stage software pipeline over 32-summary sub-tiles, as in the
+    // forward: step j issues the dq products of sub-tile j, runs the vector
+    // work of sub-tile j+1 (dT = exp2(t - lse) (dP - Delta), rounded to bf16)
+    // and issues the score and dP products of sub-tile j+2, so the matrix
+    // products of a step depend on none of its vector instructions. The
+    // operands of the next step's products are read from LDS right after
+    // this step's products take the current ones.
+    //
+    // Tile u (buffer u & 1) holds the k_sum and v_sum rows of sub-tiles
+    // 4u .. 4u+3 and the channel-major k_sum of sub-tiles 4u-2 .. 4u+1, two
+    // behind: step j reads the rows of sub-tile j+3 and the channel-major
+    // part of sub-tile j+1, both at position (j+3) % 4 of tile (j+3) / 4.
+    // So both switch tiles at the steps with (j+3) % 4 == 0, after one
+    // barrier, which also ends every read of the tile before; the loads of
+    // the tile after go into that tile's buffers right after it, four steps
+    // ahead of their use. Summaries at or past M get dT = 0 (a select, so
+    // whatever a clamped or stale LDS row held is discarded), and the steps
+    // past the last sub-tile issue no dq products.
+    // An iteration is two tiles (2 * NSUB steps), so that every buffer
+    // choice is known at compile time: the compiler can then tell the LDS
+    // reads from the loads into the other buffer and does not wait for those.
+    const int S = M32;                                  // sub-tiles with summaries
+    const int NIT = (S + 2 * NSUB - 1) / (2 * NSUB);    // iterations
+    const int NTL = (S + 2 + NSUB - 1) / NSUB;          // tiles to load
+    const int MF = g.M / 32;                            // sub-tiles wholly below M
+    const int IT_CLEAN = MF >= 1 ? min(NIT, (MF - 1) / (2 * NSUB)) : 0;
+    auto issue_p = [&](int tt, bf16x8 *dK, bf16x8 *dV, bf16x8 *dT) {
+#pragma unroll
+      for (int r = 0; r < RK; r++) {
+        if (NTH * r + 64 * wv < NKC) {  // wave-uniform
+          const int m32 = min(tt * NSUB + rk_sub[r], M32 - 1);
+          const uint32_t o = (uint32_t)(m32 * (NCH * 256) + rk_in[r]) * 2;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, (lds_ptr)&dK[NTH * r + 64 * wv], 16, o, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rvk, (lds_ptr)&dV[NTH * r + 64 * wv], 16, o, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < RT; r++) {
+        if (NTH * r + 64 * wv < NTC) {
+          const int g8 = min(max(tt * NJ8 - 8 + rt_j8[r], 0), 4 * M32 - 1);  // two sub-tiles back
+          const uint32_t o = (uint32_t)(g8 * D + rt_d[r]) * 16;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rkt, (lds_ptr)&dT[NTH * r + 64 * wv], 16, o, 0, 0, 0);
+        }
+      }
+    };
+    f32x16 s2[2], dp2[2];  // scores and dP, by parity of the sub-tile
+    bf16x8 tf2[2][2];      // dT, by parity of the sub-tile
+    bf16x8 kf[KD], vf[KD]; // score / dP operands of the next products
+    bf16x8 tq[DT][2];      // dq operands of the next products
+    auto read_kv = [&](const bf16x8 *K, const bf16x8 *V, int pos) {
+#pragma unroll
+      for (int c = 0; c < KD; c++) {
+        kf[c] = K[(2 * c + hi) * TS + 32 * pos + l32];
+        vf[c] = V[(2 * c + hi) * TS + 32 * pos + l32];
+      }
+    };
+    auto read_t = [&](const bf16x8 *T, int ls) {
+#pragma unroll
+      for (int t = 0; t < DT; t++) {
+        const int d = min(32 * t + l32, D - 1);
+#pragma unroll
+        for (int c2 = 0; c2 < 2; c2++) tq[t][c2] = T[(4 * ls + 2 * c2 + hi) * D + d];
+      }
+    };
+    auto sd = [&](f32x16 &sx, f32x16 &dx) {
+#pragma unroll
+      for (int c = 0; c < KD; c++) {
+        sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c], qf[0][c], c == 0 ? lq[0] : sx, 0, 0, 0);
+        dx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[c], df[0][c], c == 0 ? dq[0] : dx, 0, 0, 0);
+      }
+    };
+    // register e <-> summary mbase + 16*(e/8) + 8*hi + e%8
+    auto tvec = [&](const f32x16 &sx, const f32x16 &dx, bf16x8 *tx, int mbase, auto mask) {
+#pragma unroll
+      for (int e = 0; e < 16; e++) {
+        float t = __builtin_amdgcn_exp2f(sx[e]) * dx[e];
+        if constexpr (decltype(mask)::value)
+          t = (mbase + 16 * (e >> 3) + 8 * hi + (e & 7) < g.M) ? t : 0.f;
+        tx[e >> 3][e & 7] = (bf16)t;
+      }
+    };
+    auto qprod = [&](const bf16x8 *tx) {
+#pragma unroll
+      for (int t = 0; t < DT; t++)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; c2++)
+          acc[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[t][c2], tx[c2], acc[0][t], 0, 0, 0);
+    };
+    issue_p(0, sK0, sV0, sT0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (NTL > 1) issue_p(1, sK1, sV1, sT1);
+    read_kv(sK0, sV0, 0);
+    sd(s2[0], dp2[0]);
+    read_kv(sK0, sV0, 1);
+    sd(s2[1], dp2[1]);
+    tvec(s2[0], dp2[0], tf2[0], 0, std::true_type{});
+    read_kv(sK0, sV0, 2);
+    read_t(sT0, 2);  // sub-tile 0 sits at position 2 of tile 0's channel-major part
+    auto step = [&](int it, auto jc, auto mc) {
+      constexpr int JJ = decltype(jc)::value;  // step within the iteration
+      constexpr int POS = (JJ + 3) % NSUB, P = JJ & 1;
+      constexpr int KB = ((JJ + 3) / NSUB) & 1;  // buffer of tile (j+3) / NSUB
+      const int KT = 2 * it + (JJ + 3) / NSUB;
+      const int j = 2 * NSUB * it + JJ;
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (POS == 0) {
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads landed, its LDS reads done
+        __syncthreads();
+        if (KT + 1 < NTL) issue_p(KT + 1, KB ? sK0 : sK1, KB ? sV0 : sV1, KB ? sT0 : sT1);
+      }
+      const bf16x8 *K = KB ? sK1 : sK0, *V = KB ? sV1 : sV0, *T = KB ? sT1 : sT0;
+      // sub-tile j; past the last sub-tile its operands may come from a
+      // buffer never loaded (0 * NaN would reach the sums), so skip it
+      if constexpr (!decltype(mc)::value) qprod(tf2[P]);
+      else if (j < S) qprod(tf2[P]);
+      sd(s2[P], dp2[P]);      // sub-tile j+2
+      read_kv(K, V, POS);     // sub-tile j+3
+      tvec(s2[P ^ 1], dp2[P ^ 1], tf2[P ^ 1], 32 * (j + 1), mc);  // sub-tile j+1
+      read_t(T, POS);         // sub-tile j+1
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto iteration = [&](int it, auto mc) {
+      step(it, std::integral_constant<int, 0>{}, mc);
+      step(it, std::integral_constant<int, 1>{}, mc);
+      step(it, std::integral_constant<int, 2>{}, mc);
+      step(it, std::integral_constant<int, 3>{}, mc);
+      step(it, std::integral_constant<int, 4>{}, mc);
+      step(it, std::integral_constant<int, 5>{}, mc);
+      step(it, std::integral_constant<int, 6>{}, mc);
+      step(it, std::integral_constant<int, 7>{}, mc);
+    };
+    int it = 0;
+    for (; it < IT_CLEAN; it++) iteration(it, std::false_type{});
+    for (; it < NIT; it++) iteration(it, std::true_type{});
+    __builtin_amdgcn_s_waitcnt(0);
+  } else {
   const int ntile = (M32 + NSUB - 1) / NSUB;
   issue(0, sK0, sV0, sT0);
   __builtin_amdgcn_s_waitcnt(0);
@@ -354,6 +492,7 @@ __global__ __launch_bounds__(64 * NW, G == 1 ? 2 : 1) void k_bwd_gq_mfma(
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
     __syncthreads();
+  }
   }
   // lane: query site p (column l32), rows d = 32t + 8jj + 4hi + u
 #pragma unroll
