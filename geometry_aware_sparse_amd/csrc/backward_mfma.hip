@@ -55,10 +55,12 @@ __device__ __forceinline__ int swap23(int r) {
 //   lse_p, dl_p [B*H, Np]        -lse (-inf where no token: P = 0), -Delta
 //   tok [B, Np]                  token at the site (-1: none)
 // A workgroup of NTH threads takes NTH consecutive sites of one (b, h) (Np is
-// a multiple of 256), one site per thread. The 32-row blocks are written
-// straight from registers; the transposed blocks go through LDS, so that each
-// lane then stores one whole 16-byte chunk (8 sites of one channel) and a
-// wave's stores are contiguous.
+// a multiple of 256), one site per thread. Every gather (the site's q, dO and
+// O_glob rows, its (cos, sin) rows, gate and lse) goes out before any is
+// used. The 32-row blocks are written straight from registers; the
+// transposed blocks go through one LDS buffer, q~ first and dO_glob after
+// it, so that each lane then stores one whole 16-byte chunk (8 sites of one
+// channel) and a wave's stores are contiguous.
 template <int D>
 __global__ __launch_bounds__(D == 48 ? 256 : 128) void k_bwd_prep_mfma(
     Geo g, const void *geom, const bf16 *__restrict__ q, const bf16 *__restrict__ gate,
@@ -67,7 +69,9 @@ __global__ __launch_bounds__(D == 48 ? 256 : 128) void k_bwd_prep_mfma(
   constexpr int DA = D / 3, NCH = D / 8;
   constexpr int NTH = D == 48 ? 256 : 128;
   constexpr int PITCH = D + 8;  // LDS row pitch (elements): 16-byte rows, fewer bank conflicts
-  __shared__ __attribute__((aligned(16))) bf16 sQ[NTH * PITCH], sD[NTH * PITCH];
+  // one staging buffer, used for q~ and then for dO_glob, so that more
+  // workgroups fit a CU
+  __shared__ __attribute__((aligned(16))) bf16 sQ[NTH * PITCH];
   // Workgroups at D = 48: (batch, site chunk, head) with the heads
   // innermost, so that the workgroups reading the heads of the same tokens
   // run together on one XCD and share the token rows' cache lines in its L2
@@ -97,27 +101,37 @@ __global__ __launch_bounds__(D == 48 ? 256 : 128) void k_bwd_prep_mfma(
   const int c3[3] = {p / (g.Y * g.X), (p / g.X) % g.Y, p % g.X};
   const int64_t row = ((int64_t)b * g.N + max(i, 0)) * g.H + h;
   const float qscale = g.scale * kLog2e;
-  const float gg = i >= 0 ? 1.0f / (1.0f + expf(-(float)gate[row])) : 0.f;
+  // Every load goes out before any is used, without branches: a site with
+  // no token reads token 0's row (its results are replaced by zeros below).
+  bf16x8 raw[NCH], draw[NCH], oraw[NCH];
+  float2 cs[D / 2];
+#pragma unroll
+  for (int c = 0; c < NCH; c++) {
+    raw[c] = *reinterpret_cast<const bf16x8 *>(q + row * D + 8 * c);
+    draw[c] = *reinterpret_cast<const bf16x8 *>(dout + row * D + 8 * c);
+    oraw[c] = *reinterpret_cast<const bf16x8 *>(oglob + row * D + 8 * c);
+  }
+#pragma unroll
+  for (int pp = 0; pp < D / 2; pp++) cs[pp] = rope_cs(tab, g, pp / (DA / 2), c3[pp / (DA / 2)], pp % (DA / 2));
+  const float graw = (float)gate[row], lraw = lse[row];
+  const float gg = i >= 0 ? 1.0f / (1.0f + expf(-graw)) : 0.f;
   float dl = 0.f;
+  bf16x8 dvs[NCH];  // dO_glob, staged after q~
 #pragma unroll
   for (int c = 0; c < NCH; c++) {
     bf16x8 qv, dv;
     if (i >= 0) {
-      const bf16x8 raw = *reinterpret_cast<const bf16x8 *>(q + row * D + 8 * c);
-      const bf16x8 draw = *reinterpret_cast<const bf16x8 *>(dout + row * D + 8 * c);
-      const bf16x8 oraw = *reinterpret_cast<const bf16x8 *>(oglob + row * D + 8 * c);
-      const int a = (8 * c) / DA, p0 = ((8 * c) % DA) / 2;
 #pragma unroll
       for (int u = 0; u < 4; u++) {
-        float x0 = (float)raw[2 * u], x1 = (float)raw[2 * u + 1];
-        rotate(x0, x1, rope_cs(tab, g, a, c3[a], p0 + u));
+        float x0 = (float)raw[c][2 * u], x1 = (float)raw[c][2 * u + 1];
+        rotate(x0, x1, cs[4 * c + u]);
         qv[2 * u] = (bf16)(x0 * qscale);
         qv[2 * u + 1] = (bf16)(x1 * qscale);
       }
 #pragma unroll
       for (int e = 0; e < 8; e++) {
-        dv[e] = (bf16)(gg * (float)draw[e]);
-        dl += (float)dv[e] * (float)oraw[e];
+        dv[e] = (bf16)(gg * (float)draw[c][e]);
+        dl += (float)dv[e] * (float)oraw[c][e];
       }
     } else {
 #pragma unroll
@@ -127,26 +141,30 @@ __global__ __launch_bounds__(D == 48 ? 256 : 128) void k_bwd_prep_mfma(
     *reinterpret_cast<bf16x8 *>(qn + nb) = qv;
     *reinterpret_cast<bf16x8 *>(dn + nb) = dv;
     *reinterpret_cast<bf16x8 *>(&sQ[threadIdx.x * PITCH + 8 * c]) = qv;
-    *reinterpret_cast<bf16x8 *>(&sD[threadIdx.x * PITCH + 8 * c]) = dv;
+    dvs[c] = dv;
   }
-  lse_p[t] = i >= 0 ? -lse[row] : -INFINITY;
+  lse_p[t] = i >= 0 ? -lraw : -INFINITY;
   dl_p[t] = -dl;
-  __syncthreads();
   // chunk (g8, d) of the workgroup: channel d of its sites 8*g8 .. 8*g8 + 7
+  auto transpose_out = [&](bf16 *dst) {
 #pragma unroll
-  for (int r = 0; r < NCH; r++) {
-    const int e = (int)threadIdx.x + NTH * r;
-    const int g8 = e / D, d = e % D;
-    bf16x8 qv, dv;
+    for (int r = 0; r < NCH; r++) {
+      const int e = (int)threadIdx.x + NTH * r;
+      const int g8 = e / D, d = e % D;
+      bf16x8 x;
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
-      qv[k] = sQ[(8 * g8 + k) * PITCH + d];
-      dv[k] = sD[(8 * g8 + k) * PITCH + d];
+      for (int k = 0; k < 8; k++) x[k] = sQ[(8 * g8 + k) * PITCH + d];
+      const int64_t tb = ((bh * (Np / 8) + pbase / 8 + g8) * D + d) * 8;
+      *reinterpret_cast<bf16x8 *>(dst + tb) = x;
     }
-    const int64_t tb = ((bh * (Np / 8) + pbase / 8 + g8) * D + d) * 8;
-    *reinterpret_cast<bf16x8 *>(qt + tb) = qv;
-    *reinterpret_cast<bf16x8 *>(dt + tb) = dv;
-  }
+  };
+  __syncthreads();
+  transpose_out(qt);
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < NCH; c++) *reinterpret_cast<bf16x8 *>(&sQ[threadIdx.x * PITCH + 8 * c]) = dvs[c];
+  __syncthreads();
+  transpose_out(dt);
 }
 
 // v_sum [B*Hkv, Mp/8, D, 8] -> vk [B*Hkv, Mp/32, D/8, 32, 8] and
