@@ -50,6 +50,14 @@ CASES = [
        "raster"), "token", 0),
     (W(130, "bf16_d48_single_site", (1, 1, 1), 1, 2, 48, (1, 1, 1), "bf16", "iid", "raster",
        "raster", Hkv=1), "token", 0),
+    # the query side's pipeline at head dim 48 runs iterations of eight
+    # 32-summary sub-tiles: 288 summaries fill nine sub-tiles exactly (one
+    # unmasked iteration, then a tail of one sub-tile); 300 end in a partial
+    # sub-tile, with grouped KV heads
+    (W(131, "bf16_d48_m288_nine_subtiles", (8, 12, 24), 1, 2, 48, (2, 2, 2), "bf16", "iid",
+       "random", "raster"), "token", 0),
+    (W(132, "bf16_d48_m300_ragged_tail", (10, 12, 20), 1, 4, 48, (2, 2, 2), "bf16", "iid", "block",
+       "raster", Hkv=2), "token", 0),
 ]
 IDS = [f"{w.name}-{sr}" for w, sr, _ in CASES]
 BY_NAME = {w.name: (w, sr, excl) for w, sr, excl in CASES}
