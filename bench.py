@@ -301,7 +301,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the PACK3D "
-              "forward here is a single-GPU operator and this build has no multi-GPU path",
+              "forward is a single-GPU operator and the library has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
 
