@@ -82,9 +82,12 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
 // (batch, head, box) of the local kernels' work item w, over nh heads: heads
 // innermost (the heads of one token are adjacent in memory, so the workgroups
 // of one box share cache lines), then the boxes in cubes of S x S x S boxes
-// (the last cube of each axis may be cut short), each cube in z, y, x order.
-// With the XCD-contiguous dealing above, one XCD holds a cube rather than a
-// thin slab, so less of a box's halo belongs to boxes on other XCDs.
+// (the last cube of each axis may be cut short). Within a cube z varies
+// fastest, then y, then x: a box shares more halo with its z and y
+// neighbours than with its x neighbours (the boxes are longest along x), so
+// those follow it closely, while its lines are still in L2. With the
+// XCD-contiguous dealing above, one XCD holds a cube rather than a thin
+// slab, so less of a box's halo belongs to boxes on other XCDs.
 struct BoxWork {
   int b, h, tz, ty, tx;
 };
@@ -104,7 +107,7 @@ __device__ __forceinline__ BoxWork box_work(int w, int nh, int ntz, int nty, int
   const int bx = r / (nz * ny * S);    // cube within the row
   r -= bx * nz * ny * S;
   const int nx = min(S, ntx - bx * S);
-  return {b, h, bz * S + r / (ny * nx), by * S + (r / nx) % ny, bx * S + r % nx};
+  return {b, h, bz * S + r % nz, by * S + (r / nz) % ny, bx * S + r / (nz * ny)};
 }
 
 }  // namespace pk
