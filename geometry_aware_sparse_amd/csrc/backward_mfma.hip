@@ -112,7 +112,10 @@ __global__ __launch_bounds__(D == 48 ? 256 : 128) void k_bwd_prep_mfma(
     oraw[c] = *reinterpret_cast<const bf16x8 *>(oglob + row * D + 8 * c);
   }
 #pragma unroll
-  for (int pp = 0; pp < D / 2; pp++) cs[pp] = rope_cs(tab, g, pp / (DA / 2), c3[pp / (DA / 2)], pp % (DA / 2));
+  for (int pp = 0; pp < D / 2; pp++) {
+    const int a = pp / (DA / 2);  // the axis of channel pair pp
+    cs[pp] = rope_cs(tab, g, a, c3[a], pp % (DA / 2));
+  }
   const float graw = (float)gate[row], lraw = lse[row];
   const float gg = i >= 0 ? 1.0f / (1.0f + expf(-graw)) : 0.f;
   float dl = 0.f;
