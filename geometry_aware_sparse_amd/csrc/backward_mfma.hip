@@ -45,6 +45,32 @@ constexpr int kSiteAlign = 256;  // query sites padded to whole query tiles of e
 __device__ __forceinline__ int swap23(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
+
+// bf16 pair w (elements 2w, 2w+1) of v replaced by p, as one 32-bit word
+__device__ __forceinline__ bf16x8 set_pair(bf16x8 v, int w, bf16x2 p) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 u = __builtin_bit_cast(u32x4, v);
+  u[w] = __builtin_bit_cast(uint32_t, p);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// v_permlane16_swap on each 32-bit word of the pair (a[0], a[1]), in place:
+// a[0] keeps its lanes 0..15 / 32..47 and takes lanes 0..15 / 32..47 of a[1]
+// into its lanes 16..31 / 48..63; a[1] gets the rest (lanes 16..31 / 48..63
+// of a[0] in its lanes 0..15 / 32..47, and its own lanes 16..31 / 48..63).
+__device__ __forceinline__ void swap_rows16(bf16x8 *a) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 x = __builtin_bit_cast(u32x4, a[0]), y = __builtin_bit_cast(u32x4, a[1]);
+  u32x4 r0, r1;
+#pragma unroll
+  for (int w = 0; w < 4; w++) {
+    const auto sw = __builtin_amdgcn_permlane16_swap(x[w], y[w], false, false);
+    r0[w] = sw[0];
+    r1[w] = sw[1];
+  }
+  a[0] = __builtin_bit_cast(bf16x8, r0);
+  a[1] = __builtin_bit_cast(bf16x8, r1);
+}
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -547,7 +573,13 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gk_mfma(
     const bf16 *__restrict__ dt, const float *__restrict__ lse_p, const float *__restrict__ dl_p,
     const bf16 *__restrict__ ks, const bf16 *__restrict__ vk, float *dks_part, float *dvs_part,
     int Np, int mtiles, int nsplit) {
-  constexpr int KD = D / 16, NCH = D / 8, DT = (D + 31) / 32, NSUB = TQ / 32, NJ8 = TQ / 8;
+  constexpr int KD = D / 16, NCH = D / 8, NSUB = TQ / 32, NJ8 = TQ / 8;
+  // dK / dV columns: DF whole 32-channel tiles, and with T16 a last tile of
+  // 16 channels, done as two 16x16x32 products (one per 16 summaries) so
+  // that no matrix-core cycle goes to padding channels
+  constexpr int DF = D / 32;
+  constexpr bool T16 = D % 32 == 16;
+  static_assert(D % 32 == 0 || T16, "channels in whole 16-channel tiles");
   constexpr int NNC = NCH * TQ, NTC = NJ8 * D, NTH = 64 * NW;  // chunks per tile
   static_assert(NNC % 64 == 0 && NTC % 64 == 0 && TQ <= 64, "tile loads in whole waves");
   constexpr int RN = (NNC + NTH - 1) / NTH, RTT = (NTC + NTH - 1) / NTH;
@@ -569,11 +601,16 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gk_mfma(
     kb[c] = *reinterpret_cast<const bf16x8 *>(ks + o);
     vb[c] = *reinterpret_cast<const bf16x8 *>(vk + o);
   }
-  f32x16 aK[DT], aV[DT];
+  f32x16 aK[DF], aV[DF];
+  f32x4 aKt[2], aVt[2];  // the 16-channel tile: summaries 16*half ..
 #pragma unroll
-  for (int t = 0; t < DT; t++)
+  for (int t = 0; t < DF; t++)
 #pragma unroll
     for (int j = 0; j < 16; j++) aK[t][j] = aV[t][j] = 0.f;
+#pragma unroll
+  for (int hf = 0; hf < 2; hf++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) aKt[hf][j] = aVt[hf][j] = 0.f;
 
   const int nqt = Np / TQ;
   const int per = (nqt + nsplit - 1) / nsplit;
@@ -661,7 +698,8 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gk_mfma(
     f32x16 s, dp;                // scores and dP of one sub-tile
     bf16x8 pa[2], ta[2];         // P and dT of the sub-tile the softmax last produced
     bf16x8 qa[KD], da[KD];       // score / dP operands of the next sub-tile
-    bf16x8 qb[DT][2], db[DT][2]; // dK / dV operands of the next sub-tile
+    bf16x8 qb[DF][2], db[DF][2]; // dK / dV operands of the next sub-tile
+    bf16x8 qbt, dbt;             // ... of its 16-channel tile (T16)
     // the q~ and dO fragments of the sub-tile at position POS of a tile
     auto read_sd = [&](auto par, auto pos) {
       constexpr int P = decltype(par)::value, POS = decltype(pos)::value;
@@ -695,14 +733,23 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gk_mfma(
       constexpr int P = decltype(par)::value, POS = decltype(pos)::value;
       const bf16x8 *QT = P ? sQT1 : sQT0, *DTt = P ? sDT1 : sDT0;
 #pragma unroll
-      for (int t = 0; t < DT; t++) {
-        const int d = min(32 * t + l32, D - 1);
+      for (int t = 0; t < DF; t++) {
+        const int d = 32 * t + l32;
 #pragma unroll
         for (int c2 = 0; c2 < 2; c2++) {
           const int j8 = 4 * POS + 2 * c2 + hi;
           qb[t][c2] = QT[j8 * D + d];
           db[t][c2] = DTt[j8 * D + d];
         }
+      }
+      if constexpr (T16) {
+        // lane: channel 32*DF + lane%16, k block lane/16 <-> sites
+        // 8*sigma(lane/16) .. +7 of the sub-tile (sigma swaps the two bits;
+        // the order the lane swap below leaves P and dT in)
+        const int kb = lane >> 4;
+        const int j8 = 4 * POS + ((kb >> 1) | ((kb & 1) << 1));
+        qbt = QT[j8 * D + 32 * DF + (lane & 15)];
+        dbt = DTt[j8 * D + 32 * DF + (lane & 15)];
       }
     };
     issue_tile(0, std::integral_constant<int, 0>{});
@@ -721,21 +768,45 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gk_mfma(
       __builtin_amdgcn_sched_barrier(0);
       if (FULL || (j >= 2 && j - 2 < S)) {
 #pragma unroll
-        for (int t = 0; t < DT; t++)
+        for (int t = 0; t < DF; t++)
 #pragma unroll
           for (int c2 = 0; c2 < 2; c2++) {
             aK[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[c2], qb[t][c2], aK[t], 0, 0, 0);
             aV[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[c2], db[t][c2], aV[t], 0, 0, 0);
           }
+        if constexpr (T16) {
+          // Lane (n, hi) holds summary n, sites 16*c2 + 8*hi .. +7 in
+          // operand c2. v_permlane16_swap trades lanes 16..31 / 48..63 of
+          // its first operand with lanes 0..15 / 32..47 of its second, so
+          // with (c2 = 0, c2 = 1) as operands the first result holds
+          // summaries 0..15 and the second summaries 16..31, in every lane
+          // row r = lane/16 the sites 8*sigma(r) .. +7: the A operand of a
+          // 16x16x32 product. The swap goes in place, after the products
+          // above have taken the first layout.
+          swap_rows16(pa);
+          swap_rows16(ta);
+#pragma unroll
+          for (int hf = 0; hf < 2; hf++) {
+            aKt[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ta[hf], qbt, aKt[hf], 0, 0, 0);
+            aVt[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[hf], dbt, aVt[hf], 0, 0, 0);
+          }
+        }
       }
       if (FULL || (j >= 1 && j - 1 < S)) {
+        // built a pair at a time, so each pair is one packed conversion
 #pragma unroll
         for (int c2 = 0; c2 < 2; c2++)
 #pragma unroll
-          for (int e = 0; e < 8; e++) {
-            const float pr = __builtin_amdgcn_exp2f(s[8 * c2 + e]);
-            pa[c2][e] = (bf16)pr;
-            ta[c2][e] = (bf16)(pr * dp[8 * c2 + e]);
+          for (int e = 0; e < 8; e += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(s[8 * c2 + e]);
+            const float p1 = __builtin_amdgcn_exp2f(s[8 * c2 + e + 1]);
+            bf16x2 pp, tp;
+            pp[0] = (bf16)p0;
+            pp[1] = (bf16)p1;
+            tp[0] = (bf16)(p0 * dp[8 * c2 + e]);
+            tp[1] = (bf16)(p1 * dp[8 * c2 + e + 1]);
+            pa[c2] = set_pair(pa[c2], e / 2, pp);
+            ta[c2] = set_pair(ta[c2], e / 2, tp);
           }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -782,6 +853,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gk_mfma(
     for (; 4 * grp + 4 < S; grp++) group(grp, std::true_type{});
     for (; grp < ngrp; grp++) group(grp, std::false_type{});
   } else {
+    static_assert(!T16, "the one-tile-at-a-time form has whole 32-channel tiles only");
     if (ntile > 0) issue(0, sQ0, sD0, sQT0, sDT0, sL0, sDl0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -836,8 +908,8 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gk_mfma(
             ta[c2][e] = (bf16)(pr * dp[sub][8 * c2 + e]);
           }
   #pragma unroll
-        for (int t = 0; t < DT; t++) {
-          const int d = min(32 * t + l32, D - 1);
+        for (int t = 0; t < DF; t++) {
+          const int d = 32 * t + l32;
   #pragma unroll
           for (int c2 = 0; c2 < 2; c2++) {
             const int j8 = 4 * sub + 2 * c2 + hi;
@@ -856,9 +928,8 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gk_mfma(
   // lane: channel column 32t + l32, rows = summaries 8jj + 4hi + u of the group
   const int64_t base = (((int64_t)split * g.B * g.Hkv + bk) * g.M) * D;
 #pragma unroll
-  for (int t = 0; t < DT; t++) {
+  for (int t = 0; t < DF; t++) {
     const int d = 32 * t + l32;
-    if (d >= D) continue;
 #pragma unroll
     for (int j = 0; j < 16; j++) {
       const int m = m32 * 32 + (j >> 2) * 8 + hi * 4 + (j & 3);
@@ -867,6 +938,21 @@ __global__ __launch_bounds__(64 * NW, 2) void k_bwd_gk_mfma(
         dvs_part[base + (int64_t)m * D + d] = aV[t][j];
       }
     }
+  }
+  if constexpr (T16) {
+    // 16x16 blocks: lane: channel 32*DF + lane%16, summaries 16*half +
+    // 4*(lane/16) + u
+    const int d = 32 * DF + (lane & 15);
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++)
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int m = m32 * 32 + 16 * hf + 4 * (lane >> 4) + u;
+        if (m < g.M) {
+          dks_part[base + (int64_t)m * D + d] = kLn2 * aKt[hf][u];
+          dvs_part[base + (int64_t)m * D + d] = aVt[hf][u];
+        }
+      }
   }
 }
 
