@@ -225,7 +225,13 @@ __global__ __launch_bounds__(64 * NW, G == 1 ? 2 : 1) void k_bwd_gq_mfma(
     const float *__restrict__ lse_p, const float *__restrict__ dl_p,
     const int32_t *__restrict__ tok, const bf16 *__restrict__ ks, const bf16 *__restrict__ vk,
     const bf16 *__restrict__ kt, float *dqg, int Np, int ntiles) {
-  constexpr int KD = D / 16, NCH = D / 8, DT = (D + 31) / 32, NSUB = TS / 32;
+  constexpr int KD = D / 16, NCH = D / 8, NSUB = TS / 32;
+  // dq rows: DF whole 32-channel tiles, and with T16 a last tile of 16
+  // channels, done as two 16x16x32 products (one per 16 queries) so that no
+  // matrix-core cycle goes to padding channels
+  constexpr int DF = D / 32;
+  constexpr bool T16 = D % 32 == 16;
+  static_assert(D % 32 == 0 || T16, "channels in whole 16-channel tiles");
   constexpr int NJ8 = TS / 8;
   // chunks per tile: k_sum and vk rows (NCH x TS), kt (NJ8 x D); whole waves
   constexpr int NKC = NCH * TS, NTC = NJ8 * D, NTH = 64 * NW;
@@ -245,7 +251,8 @@ __global__ __launch_bounds__(64 * NW, G == 1 ? 2 : 1) void k_bwd_gq_mfma(
   // -lse and -Delta of the lane's query, in every register: the start value
   // of its score and dP columns
   f32x16 lq[G], dq[G];
-  f32x16 acc[G][DT];
+  f32x16 acc[G][DF];
+  f32x4 accT[2] = {};  // the 16-channel tile (T16): queries 16*half ..
 #pragma unroll
   for (int gi = 0; gi < G; gi++) {
     p[gi] = tile * (NW * 32 * G) + (wv * G + gi) * 32 + l32;
@@ -263,7 +270,7 @@ __global__ __launch_bounds__(64 * NW, G == 1 ? 2 : 1) void k_bwd_gq_mfma(
       dq[gi][j] = nd;
     }
 #pragma unroll
-    for (int t = 0; t < DT; t++)
+    for (int t = 0; t < DF; t++)
 #pragma unroll
       for (int j = 0; j < 16; j++) acc[gi][t][j] = 0.f;
   }
@@ -334,8 +341,8 @@ __global__ __launch_bounds__(64 * NW, G == 1 ? 2 : 1) void k_bwd_gq_mfma(
         tf[j >> 3][j & 7] = (bf16)t;
       }
 #pragma unroll
-      for (int t = 0; t < DT; t++) {
-        const int d = min(32 * t + l32, D - 1);
+      for (int t = 0; t < DF; t++) {
+        const int d = 32 * t + l32;
 #pragma unroll
         for (int c2 = 0; c2 < 2; c2++) {
           const bf16x8 kf2 = T[(4 * sub + 2 * c2 + hi) * D + d];
@@ -393,7 +400,8 @@ __global__ __launch_bounds__(64 * NW, G == 1 ? 2 : 1) void k_bwd_gq_mfma(
     f32x16 s2[2], dp2[2];  // scores and dP, by parity of the sub-tile
     bf16x8 tf2[2][2];      // dT, by parity of the sub-tile
     bf16x8 kf[KD], vf[KD]; // score / dP operands of the next products
-    bf16x8 tq[DT][2];      // dq operands of the next products
+    bf16x8 tq[DF][2];      // dq operands of the next products
+    bf16x8 tqt;            // ... of the 16-channel tile (T16)
     auto read_kv = [&](const bf16x8 *K, const bf16x8 *V, int pos) {
 #pragma unroll
       for (int c = 0; c < KD; c++) {
@@ -403,10 +411,17 @@ __global__ __launch_bounds__(64 * NW, G == 1 ? 2 : 1) void k_bwd_gq_mfma(
     };
     auto read_t = [&](const bf16x8 *T, int ls) {
 #pragma unroll
-      for (int t = 0; t < DT; t++) {
-        const int d = min(32 * t + l32, D - 1);
+      for (int t = 0; t < DF; t++) {
+        const int d = 32 * t + l32;
 #pragma unroll
         for (int c2 = 0; c2 < 2; c2++) tq[t][c2] = T[(4 * ls + 2 * c2 + hi) * D + d];
+      }
+      if constexpr (T16) {
+        // lane: channel 32*DF + lane%16, k block lane/16 <-> summaries
+        // 8*sigma(lane/16) .. +7 of the sub-tile (sigma swaps the two bits;
+        // the order the lane swap in qprod leaves dT in)
+        const int kb = lane >> 4;
+        tqt = T[(4 * ls + ((kb >> 1) | ((kb & 1) << 1))) * D + 32 * DF + (lane & 15)];
       }
     };
     auto sd = [&](f32x16 &sx, f32x16 &dx) {
@@ -417,21 +432,41 @@ __global__ __launch_bounds__(64 * NW, G == 1 ? 2 : 1) void k_bwd_gq_mfma(
       }
     };
     // register e <-> summary mbase + 16*(e/8) + 8*hi + e%8
+    // (built a pair at a time, so each pair is one packed conversion)
     auto tvec = [&](const f32x16 &sx, const f32x16 &dx, bf16x8 *tx, int mbase, auto mask) {
 #pragma unroll
-      for (int e = 0; e < 16; e++) {
-        float t = __builtin_amdgcn_exp2f(sx[e]) * dx[e];
-        if constexpr (decltype(mask)::value)
-          t = (mbase + 16 * (e >> 3) + 8 * hi + (e & 7) < g.M) ? t : 0.f;
-        tx[e >> 3][e & 7] = (bf16)t;
+      for (int e = 0; e < 16; e += 2) {
+        float t0 = __builtin_amdgcn_exp2f(sx[e]) * dx[e];
+        float t1 = __builtin_amdgcn_exp2f(sx[e + 1]) * dx[e + 1];
+        if constexpr (decltype(mask)::value) {
+          const int m0 = mbase + 16 * (e >> 3) + 8 * hi + (e & 7);
+          t0 = m0 < g.M ? t0 : 0.f;
+          t1 = m0 + 1 < g.M ? t1 : 0.f;
+        }
+        bf16x2 pr;
+        pr[0] = (bf16)t0;
+        pr[1] = (bf16)t1;
+        tx[e >> 3] = set_pair(tx[e >> 3], (e & 7) / 2, pr);
       }
     };
-    auto qprod = [&](const bf16x8 *tx) {
+    auto qprod = [&](bf16x8 *tx) {
 #pragma unroll
-      for (int t = 0; t < DT; t++)
+      for (int t = 0; t < DF; t++)
 #pragma unroll
         for (int c2 = 0; c2 < 2; c2++)
           acc[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[t][c2], tx[c2], acc[0][t], 0, 0, 0);
+      if constexpr (T16) {
+        // Lane (n, hi) holds query n, summaries 16*c2 + 8*hi .. +7 in
+        // operand c2; v_permlane16_swap of (c2 = 0, c2 = 1) leaves queries
+        // 0..15 in the first and 16..31 in the second, in lane row r the
+        // summaries 8*sigma(r) .. +7: the B operand of a 16x16x32 product.
+        // In place: the products above have taken the first layout, and
+        // dT of this sub-tile has no later reader.
+        swap_rows16(tx);
+#pragma unroll
+        for (int hf = 0; hf < 2; hf++)
+          accT[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tqt, tx[hf], accT[hf], 0, 0, 0);
+      }
     };
     issue_p(0, sK0, sV0, sT0);
     __builtin_amdgcn_s_waitcnt(0);
@@ -482,6 +517,7 @@ __global__ __launch_bounds__(64 * NW, G == 1 ? 2 : 1) void k_bwd_gq_mfma(
     for (; it < NIT; it++) iteration(it, std::true_type{});
     __builtin_amdgcn_s_waitcnt(0);
   } else {
+  static_assert(!T16, "the one-tile-at-a-time form has whole 32-channel tiles only");
   const int ntile = (M32 + NSUB - 1) / NSUB;
   issue(0, sK0, sV0, sT0);
   __builtin_amdgcn_s_waitcnt(0);
@@ -514,8 +550,8 @@ __global__ __launch_bounds__(64 * NW, G == 1 ? 2 : 1) void k_bwd_gq_mfma(
         for (int j = 0; j < 16; j++)
           tf[j >> 3][j & 7] = (bf16)(__builtin_amdgcn_exp2f(s[sub][j]) * dp[sub][j]);
 #pragma unroll
-        for (int t = 0; t < DT; t++) {
-          const int d = min(32 * t + l32, D - 1);
+        for (int t = 0; t < DF; t++) {
+          const int d = 32 * t + l32;
 #pragma unroll
           for (int c2 = 0; c2 < 2; c2++) {
             const bf16x8 kf = T[(4 * sub + 2 * c2 + hi) * D + d];
@@ -548,17 +584,31 @@ __global__ __launch_bounds__(64 * NW, G == 1 ? 2 : 1) void k_bwd_gq_mfma(
     if (i < 0) continue;
     float *orow = dqg + (((int64_t)b * g.N + i) * g.H + h) * D;
 #pragma unroll
-    for (int t = 0; t < DT; t++)
+    for (int t = 0; t < DF; t++)
 #pragma unroll
       for (int jj = 0; jj < 4; jj++) {
         const int d = 32 * t + 8 * jj + 4 * hi;
-        if (d < D) {
-          f32x4 o4;
+        f32x4 o4;
 #pragma unroll
-          for (int u = 0; u < 4; u++) o4[u] = g.scale * acc[gi][t][4 * jj + u];
-          *reinterpret_cast<f32x4 *>(orow + d) = o4;
-        }
+        for (int u = 0; u < 4; u++) o4[u] = g.scale * acc[gi][t][4 * jj + u];
+        *reinterpret_cast<f32x4 *>(orow + d) = o4;
       }
+  }
+  if constexpr (T16) {
+    // 16x16 blocks: lane: query site 16*half + lane%16 of the wave's 32,
+    // channels 32*DF + 4*(lane/16) .. +3
+    static_assert(G == 1, "one query group per wave");
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++) {
+      const int pt = tile * (NW * 32) + wv * 32 + 16 * hf + (lane & 15);
+      const int i = pt < g.N ? tok[(int64_t)b * Np + pt] : -1;
+      if (i < 0) continue;
+      f32x4 o4;
+#pragma unroll
+      for (int u = 0; u < 4; u++) o4[u] = g.scale * accT[hf][u];
+      *reinterpret_cast<f32x4 *>(dqg + (((int64_t)b * g.N + i) * g.H + h) * D + 32 * DF +
+                                 4 * (lane >> 4)) = o4;
+    }
   }
 }
 
