@@ -55,9 +55,11 @@
  * float64; summaries -> the block-weighted displacement identity of §B.5;
  * global -> torch's scaled_dot_product_attention over the summaries; mix ->
  * saturated and neutral gates; whole operator -> bitwise packing equivariance.
- * The sequence-position RoPE control is pinned only by its failure to be
- * equivariant (parity with the authors' code is unpinned: no code, tables or
- * worked numbers with all parameters are printed on the pages).
+ * The sequence-position RoPE control is pinned to the matrix exponential of
+ * a 1-D rotation generator at the packed index, and by its failure to be
+ * equivariant. Parity with the authors' own RoPE convention and numbers is
+ * unpinned: no code, tables or worked numbers with all parameters are
+ * printed on the pages.
  */
 #include <math.h>
 #include <stdint.h>
