@@ -19,6 +19,9 @@
 //                        summed in the same order), then
 //                        dk~ += s dS q~, dv += P (1 - g) dO, and the pooling
 //                        and RoPE transposes
+//   k_bwd_local_kv_tr48  the key side at head dim 48 with those two sums on
+//                        the matrix cores (LDS transpose loads of the staged
+//                        q~ and dO rows, the weights placed as runs of three)
 #include "launch.hpp"
 
 namespace pk {
@@ -525,6 +528,344 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX, 2) void k_bwd_local_kv_pair(
 }
 
 // ---------------------------------------------------------------------------
+// The key side at head dim 48 with its two weighted sums over neighbour
+// queries on the matrix cores, as the forward's local kernel sums values.
+// The logits, u_ij and the weights are formed exactly as in
+// k_bwd_local_kv_pair (lanes 2n, 2n + 1 serve key n, one channel half each);
+// then, per wave (the keys of one z-plane of the 4 x 4 x 8 box),
+//   dk~^T (two 32-row tiles of channels x 32 keys) += Q~^T * dS^T,
+//   dv^T                                           += dO^T * (P (1 - g))^T
+// with v_mfma_f32_32x32x16_bf16 over the 3 planes x 4 blocks of 16 sites a
+// plane of keys can see. The A operands come from the staged row-major q~
+// and dO rows through the LDS transpose load; the B operands hold each key's
+// bf16 weights for 8 sites, placed as one run of three (dx = -1, 0, +1) by
+// byte permutes. The weights are rounded to bf16 as the vector form rounds
+// them; each sum's order is fixed by the key's position in its box.
+template <bool CENTRE>
+__global__ __launch_bounds__(256, 2) void k_bwd_local_kv_tr48(
+    Geo g, const void *geom, const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+    const bf16 *__restrict__ v, const bf16 *__restrict__ gate, const bf16 *__restrict__ dout,
+    const float *__restrict__ lse_l, const float *__restrict__ delta_l,
+    const float *__restrict__ dks, const float *__restrict__ dvs, bf16 *dk, bf16 *dv, int ntz,
+    int nty, int ntx) {
+  constexpr int D = 48, TZ = 4, TY = 4, TX = 8;
+  constexpr int HZ = TZ + 2, HY = TY + 2, HX = TX + 2, NPL = HY * HX, NH = HZ * NPL;
+  constexpr int LPQ = 2, NT = 256, DA = D / 3, DH = 24, P = D / 6;
+  constexpr int CPS = D / 8, NCK = NH * CPS, RS = (NCK + NT - 1) / NT, RSL = (NH + NT - 1) / NT;
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s *lds_v4s;
+  __shared__ __attribute__((aligned(16))) bf16 sQ[RS * NT * 8];
+  __shared__ __attribute__((aligned(16))) bf16 sO[RS * NT * 8];
+  __shared__ int sSlot[NH];
+  __shared__ float2 sCS[(HZ + HY + HX) * P];
+  __shared__ float sOmg[NH], sL[NH], sDl[NH];
+  // the furthest operand read: padding site 63 of the last plane, channel 63
+  static_assert(((HZ - 1) * NPL + 64) * D + (64 - D) <= RS * NT * 8,
+                "padding sites and channels stay in the buffers");
+
+  const BoxWork wk = box_work(xcd_remap(blockIdx.x, gridDim.x), g.Hkv, ntz, nty, ntx);
+  const int hk = wk.h, b = wk.b;
+  const int z0 = wk.tz * TZ, y0 = wk.ty * TY, x0 = wk.tx * TX;
+  const int64_t bN = (int64_t)b * g.N;
+  const float2 *tab = rope_table(geom, g);
+  auto cs_at = [&](int a, int rc, int p) {
+    const int base = a == 0 ? 0 : (a == 1 ? HZ : HZ + HY);
+    return sCS[(base + rc) * P + p];
+  };
+  stage_box<NT, HZ, HY, HX, P>(g, slot_map(geom, g), tab, z0, y0, x0, sSlot, sCS);
+  __syncthreads();
+
+  // logits layout: lanes 2n, 2n + 1 serve key n (channel halves hh)
+  const int lane = threadIdx.x & 63;
+  const int kn = threadIdx.x / LPQ, hh = threadIdx.x % LPQ;
+  const int tz = kn / (TY * TX), ty = (kn / TX) % TY, tx = kn % TX;
+  const int ks_ = ((tz + 1) * HY + (ty + 1)) * HX + (tx + 1);
+  const int j = sSlot[ks_];
+  const int rc3[3] = {tz + 1, ty + 1, tx + 1};
+  const int wbase = __builtin_amdgcn_readfirstlane(threadIdx.x & ~63);
+  const float qscale = g.scale * kLog2e;
+  // this key's rotated bf16 slice (as the query side staged it) and values
+  bf16x2 kp[DH / 2], vp[DH / 2];
+  {
+    const int64_t joff = ((bN + max(j, 0)) * g.Hkv + hk) * D + hh * DH;
+#pragma unroll
+    for (int c8 = 0; c8 < DH / 8; c8++) {
+      const bf16x8 kr = *reinterpret_cast<const bf16x8 *>(k + joff + 8 * c8);
+      const bf16x8 vr = *reinterpret_cast<const bf16x8 *>(v + joff + 8 * c8);
+      const int d0 = hh * DH + 8 * c8, a = d0 / DA, p0 = (d0 % DA) / 2;
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        float k0 = (float)kr[2 * u], k1 = (float)kr[2 * u + 1];
+        rotate(k0, k1, cs_at(a, rc3[a], p0 + u));
+        kp[4 * c8 + u][0] = (bf16)k0;
+        kp[4 * c8 + u][1] = (bf16)k1;
+        vp[4 * c8 + u][0] = vr[2 * u];
+        vp[4 * c8 + u][1] = vr[2 * u + 1];
+      }
+    }
+  }
+  // product layout: lanes n, n + 32 serve key n (site halves hi)
+  const int hi = lane >> 5, ql = lane & 31;
+  const int pty = ql >> 3, ptx = ql & 7;
+  f32x16 accK[2], accV[2];
+#pragma unroll
+  for (int t = 0; t < 2; t++)
+#pragma unroll
+    for (int e = 0; e < 16; e++) accK[t][e] = accV[t][e] = 0.f;
+
+  for (int h = hk * g.G; h < (hk + 1) * g.G; h++) {
+    __syncthreads();  // the previous head's stage is no longer read
+    // the thread index, opaque within this head: the staging addresses and
+    // slots are formed here rather than hoisted out of the head loop (spilled)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    // all loads first: raw q chunks, dO straight to LDS, per-site statistics
+    bf16x8 qraw[RS];
+#pragma unroll
+    for (int r = 0; r < RS; r++) {
+      const int e = min(tid + r * NT, NCK - 1);
+      const int hs = e / CPS, ch = e % CPS;
+      const int64_t off = ((bN + max(sSlot[hs], 0)) * g.H + h) * D + ch * 8;
+      qraw[r] = *reinterpret_cast<const bf16x8 *>(q + off);
+      __builtin_amdgcn_global_load_lds(dout + off, (lds_ptr)&sO[(wbase + r * NT) * 8], 16, 0, 0);
+    }
+    float st_g[RSL], st_l[RSL], st_d[RSL];
+#pragma unroll
+    for (int r = 0; r < RSL; r++) {
+      const int hs = min(tid + r * NT, NH - 1);
+      const int64_t srow = (bN + max(sSlot[hs], 0)) * g.H + h;
+      st_g[r] = (float)gate[srow];
+      st_l[r] = lse_l[srow];
+      st_d[r] = delta_l[srow];
+    }
+#pragma unroll
+    for (int r = 0; r < RS; r++) {
+      const int e = tid + r * NT;
+      const int ec = min(e, NCK - 1);
+      const int hs = ec / CPS, ch = ec % CPS;
+      const int qc3[3] = {hs / (HY * HX), (hs / HX) % HY, hs % HX};
+      const int a = (ch * 8) / DA, p0 = ((ch * 8) % DA) / 2;
+      bf16x8 qo;
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        float x0 = (float)qraw[r][2 * u], x1 = (float)qraw[r][2 * u + 1];
+        rotate(x0, x1, cs_at(a, qc3[a], p0 + u));
+        qo[2 * u] = (bf16)(x0 * qscale);
+        qo[2 * u + 1] = (bf16)(x1 * qscale);
+      }
+      *reinterpret_cast<bf16x8 *>(&sQ[e * 8]) = qo;
+    }
+#pragma unroll
+    for (int r = 0; r < RSL; r++) {
+      const int hs = tid + r * NT;
+      if (hs < NH) {
+        sOmg[hs] = 1.0f - 1.0f / (1.0f + expf(-st_g[r]));
+        sL[hs] = st_l[r];
+        sDl[hs] = st_d[r];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // the key's corner index, opaque within this head (see k_bwd_local_kv_pair)
+    int ksh = ((tz * HY) + ty) * HX + tx;
+    asm volatile("" : "+v"(ksh));
+    // logits (the query side's, bit for bit) and u_ij = <dO_i, v_j>; the
+    // weights as bf16 triples (dx = -1, 0, +1) of each (dz, dy), packed as
+    // the words (w-, w0) and (w+, 0); a key site without a token gets zeros
+    uint32_t tK[9][2], tV[9][2];
+#pragma unroll
+    for (int r9 = 0; r9 < 9; r9++) {
+      float pwr[3], dsr[3];
+#pragma unroll
+      for (int dx = 0; dx < 3; dx++) {
+        const int kk = 3 * r9 + dx;
+        const int hs = ksh + halo_from_corner(kk, HY, HX);
+        const bf16x2 *qr = reinterpret_cast<const bf16x2 *>(sQ + hs * D + hh * DH);
+        const bf16x2 *orr = reinterpret_cast<const bf16x2 *>(sO + hs * D + hh * DH);
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < DH / 2; jj++) {
+          a0 = __builtin_amdgcn_fdot2_f32_bf16(qr[jj], kp[jj], a0, false);
+          a1 = __builtin_amdgcn_fdot2_f32_bf16(orr[jj], vp[jj], a1, false);
+        }
+        a0 = lane_sum<LPQ>(a0);
+        a1 = lane_sum<LPQ>(a1);
+        const bool valid = sSlot[hs] >= 0 && j >= 0;
+        const float pr = valid ? __builtin_amdgcn_exp2f(a0 - sL[hs]) : 0.f;
+        pwr[dx] = valid ? pr * sOmg[hs] : 0.f;
+        dsr[dx] = valid ? pr * (sOmg[hs] * a1 - sDl[hs]) : 0.f;
+        asm volatile("" ::: "memory");  // as on the query side
+      }
+      bf16x2 k0, k1, v0, v1;
+      k0[0] = (bf16)dsr[0];
+      k0[1] = (bf16)dsr[1];
+      k1[0] = (bf16)dsr[2];
+      k1[1] = (bf16)0.0f;
+      v0[0] = (bf16)pwr[0];
+      v0[1] = (bf16)pwr[1];
+      v1[0] = (bf16)pwr[2];
+      v1[1] = (bf16)0.0f;
+      tK[r9][0] = __builtin_bit_cast(uint32_t, k0);
+      tK[r9][1] = __builtin_bit_cast(uint32_t, k1);
+      tV[r9][0] = __builtin_bit_cast(uint32_t, v0);
+      tV[r9][1] = __builtin_bit_cast(uint32_t, v1);
+    }
+    // into the product layout: key n's words come from lane 2n
+#pragma unroll
+    for (int r9 = 0; r9 < 9; r9++)
+#pragma unroll
+      for (int w = 0; w < 2; w++) {
+        tK[r9][w] = (uint32_t)__shfl((int)tK[r9][w], 2 * ql);
+        tV[r9][w] = (uint32_t)__shfl((int)tV[r9][w], 2 * ql);
+      }
+    // Where this lane's weights sit in block kb4 of a plane: its window is
+    // sites kappa0 = 16*kb4 + 8*hi .. +7 (kappa = y*10 + x of a halo plane);
+    // the run of neighbour row dy starts at s_dy = (pty + 1 + dy)*10 + ptx,
+    // and at most one run meets the window, at slot offset o in [-2, 7]
+    // (for even o = 2m the pair itself in words m, m + 1; for odd o the
+    // words (0, w-) and (w0, w+); zeros elsewhere).
+    // the lane index, opaque within this head: the selectors and addresses
+    // below are formed here rather than hoisted out of the head loop, where
+    // they would spill
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lhi = ln >> 5, lq = ln & 31;
+    const int grp = (ln >> 4) & 1, rq = ln & 3, re = (ln >> 2) & 3;
+    const int abase = (tz * NPL + re) * D + 16 * grp + 4 * rq;  // elements
+#pragma unroll
+    for (int kb4 = 0; kb4 < 4; kb4++) {
+      const int k0 = 16 * kb4 + 8 * lhi;
+      const int sm = (lq >> 3) * 10 + (lq & 7);
+      const int rel = k0 - sm + 7;
+      const int di = rel >= 0 ? rel / 10 : -1;
+      const bool ok = di >= 0 && di <= 2;
+      const int o = sm + 10 * di - k0;
+      const int m = ok ? (o >> 1) : -8;
+      const bool odd = (o & 1) != 0;
+      const uint32_t s0 = odd ? 0x01000C0Cu : 0x03020100u, s1 = odd ? 0x05040302u : 0x07060504u;
+      uint32_t sel[4];
+#pragma unroll
+      for (int jd = 0; jd < 4; jd++) sel[jd] = jd == m ? s0 : (jd == m + 1 ? s1 : 0x0C0C0C0Cu);
+#pragma unroll
+      for (int dzi = 0; dzi < 3; dzi++) {
+        // the even-packed triples of run di of plane dzi (selects between
+        // constant indices: a run-time index would put the arrays in scratch)
+        uint32_t xk[2], xv[2];
+#pragma unroll
+        for (int w = 0; w < 2; w++) {
+          xk[w] = di == 0 ? tK[3 * dzi][w] : (di == 1 ? tK[3 * dzi + 1][w] : tK[3 * dzi + 2][w]);
+          xv[w] = di == 0 ? tV[3 * dzi][w] : (di == 1 ? tV[3 * dzi + 1][w] : tV[3 * dzi + 2][w]);
+        }
+        uint32_t bk[4], bv[4];
+#pragma unroll
+        for (int jd = 0; jd < 4; jd++) {
+          bk[jd] = __builtin_amdgcn_perm(xk[1], xk[0], sel[jd]);
+          bv[jd] = __builtin_amdgcn_perm(xv[1], xv[0], sel[jd]);
+        }
+        bf16x8 bopK, bopV;
+        __builtin_memcpy(&bopK, bk, 16);
+        __builtin_memcpy(&bopV, bv, 16);
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+          const int ad = abase + (dzi * NPL + k0) * D + 32 * t;
+          const v4s ql4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(sQ + ad));
+          const v4s qh4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(sQ + ad + 4 * D));
+          const v4s ol4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(sO + ad));
+          const v4s oh4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(sO + ad + 4 * D));
+          bf16x8 aq, ao;
+          __builtin_memcpy(&aq, &ql4, 8);
+          __builtin_memcpy(reinterpret_cast<char *>(&aq) + 8, &qh4, 8);
+          __builtin_memcpy(&ao, &ol4, 8);
+          __builtin_memcpy(reinterpret_cast<char *>(&ao) + 8, &oh4, 8);
+          accK[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bopK, accK[t], 0, 0, 0);
+          accV[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, bopV, accV[t], 0, 0, 0);
+        }
+        // a compiler-only fence per plane: the next operands' LDS reads are
+        // not all hoisted ahead, which would spill
+        asm volatile("" ::: "memory");
+      }
+    }
+  }
+  // Lane (n, hi) holds channels 8*jj + 4*hi .. +3 of key n (tile jj / 4,
+  // registers 4*(jj % 4) ..); the halves trade pieces (v_permlane32_swap)
+  // so that each lane holds channels 16*mm + 8*hi .. +7, mm = 0, 1, 2.
+  float okd[3][8], ovd[3][8];
+#pragma unroll
+  for (int mm = 0; mm < 3; mm++)
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int t0 = (2 * mm) / 4, r0 = 4 * ((2 * mm) % 4) + u;
+      const int t1 = (2 * mm + 1) / 4, r1 = 4 * ((2 * mm + 1) % 4) + u;
+      // elements copied out first: a bit cast applied straight to a vector
+      // element subscript compiles to a cast of element 0
+      const float k0 = accK[t0][r0], k1 = accK[t1][r1], v0 = accV[t0][r0], v1 = accV[t1][r1];
+      const auto sk = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, k0),
+                                                       __builtin_bit_cast(uint32_t, k1), false, false);
+      const auto sv = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v0),
+                                                       __builtin_bit_cast(uint32_t, v1), false, false);
+      okd[mm][u] = __builtin_bit_cast(float, (uint32_t)sk[0]);
+      okd[mm][4 + u] = __builtin_bit_cast(float, (uint32_t)sk[1]);
+      ovd[mm][u] = __builtin_bit_cast(float, (uint32_t)sv[0]);
+      ovd[mm][4 + u] = __builtin_bit_cast(float, (uint32_t)sv[1]);
+    }
+  // key n = ql of plane tz, in the product layout
+  const int pj = sSlot[((tz + 1) * HY + (pty + 1)) * HX + (ptx + 1)];
+  if (pj < 0) return;
+  const int prc3[3] = {tz + 1, pty + 1, ptx + 1};
+  // pooling transpose, then dk = R(c_j)^T dk~ (centre variant: its block part
+  // goes through R(centre)^T instead)
+  const int c3[3] = {z0 + tz, y0 + pty, x0 + ptx};
+  const int mb = block_of(g, c3[0], c3[1], c3[2]);
+  const int mz = mb / (g.My * g.Mx), my = (mb / g.Mx) % g.My, mx = mb % g.Mx;
+  const int nm = min(g.bz, g.Z - mz * g.bz) * min(g.by, g.Y - my * g.by) * min(g.bx, g.X - mx * g.bx);
+  const float inv_n = 1.0f / (float)nm;
+  const int64_t prow = ((bN + pj) * g.Hkv + hk) * D;
+  const float *gk = dks + (((int64_t)b * g.Hkv + hk) * g.M + mb) * D;
+  const float *gv = dvs + (((int64_t)b * g.Hkv + hk) * g.M + mb) * D;
+#pragma unroll
+  for (int mm = 0; mm < 3; mm++) {
+    const int d0 = 16 * mm + 8 * hi, a = mm, p0 = 4 * hi;  // axis chunk mm, its planes 4hi ..
+    const f32x4 gk0 = *reinterpret_cast<const f32x4 *>(gk + d0);
+    const f32x4 gk1 = *reinterpret_cast<const f32x4 *>(gk + d0 + 4);
+    const f32x4 gv0 = *reinterpret_cast<const f32x4 *>(gv + d0);
+    const f32x4 gv1 = *reinterpret_cast<const f32x4 *>(gv + d0 + 4);
+    const float gkf[8] = {gk0[0], gk0[1], gk0[2], gk0[3], gk1[0], gk1[1], gk1[2], gk1[3]};
+    const float gvf[8] = {gv0[0], gv0[1], gv0[2], gv0[3], gv1[0], gv1[1], gv1[2], gv1[3]};
+    bf16x8 okv, ovv;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int c = 2 * u;
+      float x0 = kLn2 * okd[mm][c], x1 = kLn2 * okd[mm][c + 1];  // s / (s log2 e)
+      if (!CENTRE) {
+        x0 += gkf[c] * inv_n;
+        x1 += gkf[c + 1] * inv_n;
+      }
+      rotate_t(x0, x1, cs_at(a, prc3[a], p0 + u));
+      if (CENTRE) {
+        const int o = a == 0 ? mz * g.bz : (a == 1 ? my * g.by : mx * g.bx);
+        const int ext = min(a == 0 ? g.bz : (a == 1 ? g.by : g.bx),
+                            (a == 0 ? g.Z : (a == 1 ? g.Y : g.X)) - o);
+        float2 t = rope_cs(tab, g, a, o + (ext - 1) / 2, p0 + u);
+        if ((ext & 1) == 0) {
+          const float2 hf = rope_half(tab, g, p0 + u);
+          t = make_float2(t.x * hf.x - t.y * hf.y, t.y * hf.x + t.x * hf.y);
+        }
+        float y0 = gkf[c] * inv_n, y1 = gkf[c + 1] * inv_n;
+        rotate_t(y0, y1, t);
+        x0 += y0;
+        x1 += y1;
+      }
+      okv[c] = (bf16)x0;
+      okv[c + 1] = (bf16)x1;
+      ovv[c] = (bf16)(ovd[mm][c] + gvf[c] * inv_n);
+      ovv[c + 1] = (bf16)(ovd[mm][c + 1] + gvf[c + 1] * inv_n);
+    }
+    *reinterpret_cast<bf16x8 *>(dk + prow + d0) = okv;
+    *reinterpret_cast<bf16x8 *>(dv + prow + d0) = ovv;
+  }
+}
+
+// ---------------------------------------------------------------------------
 namespace {
 // The query side and the key side may use different boxes (KZ, KY, KX for
 // the key side).
@@ -544,8 +885,15 @@ hipError_t run_local_bwd_pair(const Geo &g, const BwdArgs &a, hipStream_t s) {
   }
   const int ntz = (g.Z + KZ - 1) / KZ, nty = (g.Y + KY - 1) / KY, ntx = (g.X + KX - 1) / KX;
   const int nt = (D / 24) * KZ * KY * KX;
-  auto kv = (g.flags & PACK3D_SUMMARY_CENTRE) ? k_bwd_local_kv_pair<D, KZ, KY, KX, true>
-                                               : k_bwd_local_kv_pair<D, KZ, KY, KX, false>;
+  const bool centre = (g.flags & PACK3D_SUMMARY_CENTRE) != 0;
+  // head dim 48: the weighted sums on the matrix cores
+  auto kv = [&] {
+    if constexpr (D == 48 && KZ == 4 && KY == 4 && KX == 8)
+      return centre ? k_bwd_local_kv_tr48<true> : k_bwd_local_kv_tr48<false>;
+    else
+      return centre ? k_bwd_local_kv_pair<D, KZ, KY, KX, true>
+                    : k_bwd_local_kv_pair<D, KZ, KY, KX, false>;
+  }();
   hipLaunchKernelGGL(kv, dim3((unsigned)(g.B * ntz * nty * ntx * g.Hkv)), dim3(nt), 0, s, g, a.geom,
                      static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.k),
                      static_cast<const bf16 *>(a.v), static_cast<const bf16 *>(a.gate),
