@@ -19,6 +19,8 @@
 //                        summed in the same order), then
 //                        dk~ += s dS q~, dv += P (1 - g) dO, and the pooling
 //                        and RoPE transposes
+//   k_bwd_local_q_tr48   the query side at head dim 48 with dq~ on the matrix
+//                        cores
 //   k_bwd_local_kv_tr48  the key side at head dim 48 with those two sums on
 //                        the matrix cores (LDS transpose loads of the staged
 //                        q~ and dO rows, the weights placed as runs of three)
@@ -308,6 +310,291 @@ __global__ __launch_bounds__((D / 24) * TZ *TY *TX, D == 48 ? 3 : 2) void k_bwd_
   }
 #pragma unroll
   for (int c8 = 0; c8 < DH / 8; c8++) *reinterpret_cast<bf16x8 *>(dq + off + 8 * c8) = outv[c8];
+  dgo = lane_sum<LPQ>(dgo);
+  if (hh == 0) {
+    dgate[row] = (bf16)(gg * omg * (dgo - dol));
+    lse_l[row] = mx + __log2f(den);
+    delta_l[row] = delta;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The query side at head dim 48 with dq~ = sum_j dS_j k~_j on the matrix
+// cores, as k_bwd_local_kv_tr48 sums over neighbour queries; the logits,
+// u_j, the softmax, dG and the statistics are those of k_bwd_local_q_pair.
+__global__ __launch_bounds__(256, 3) void k_bwd_local_q_tr48(
+    Geo g, const void *geom, const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+    const bf16 *__restrict__ v, const bf16 *__restrict__ gate, const bf16 *__restrict__ dout,
+    const bf16 *__restrict__ oglob, const float *__restrict__ dqg, bf16 *dq, bf16 *dgate,
+    float *lse_l, float *delta_l, int ntz, int nty, int ntx) {
+  constexpr int D = 48, TZ = 4, TY = 4, TX = 8;
+  constexpr int HZ = TZ + 2, HY = TY + 2, HX = TX + 2, NPL = HY * HX, NH = HZ * NPL, NQ = TZ * TY * TX;
+  constexpr int LPQ = 2, NT = LPQ * NQ, DA = D / 3, DH = 24, P = D / 6;
+  constexpr int CPS = D / 8, NCK = NH * CPS, RS = (NCK + NT - 1) / NT;
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s *lds_v4s;
+  // one LDS buffer holds the values for u_j = <dO, v_j>, then the rotated
+  // keys for the logits and dq, so that more workgroups fit a CU
+  __shared__ __attribute__((aligned(16))) bf16 sK[RS * NT * 8];
+  const bf16 *sV = sK;
+  __shared__ int sSlot[NH];
+  __shared__ float2 sCS[(HZ + HY + HX) * P];
+  // the furthest operand read: padding site 63 of the last plane, channel 63
+  static_assert(((HZ - 1) * NPL + 64) * D + (64 - D) <= RS * NT * 8,
+                "padding sites and channels stay in the buffer");
+
+  const BoxWork wk = box_work(xcd_remap(blockIdx.x, gridDim.x), g.H, ntz, nty, ntx);
+  const int h = wk.h, b = wk.b;
+  const int hk = h / g.G;
+  const int z0 = wk.tz * TZ, y0 = wk.ty * TY, x0 = wk.tx * TX;
+  const int64_t bN = (int64_t)b * g.N;
+  auto cs_at = [&](int a, int rc, int p) {
+    const int base = a == 0 ? 0 : (a == 1 ? HZ : HZ + HY);
+    return sCS[(base + rc) * P + p];
+  };
+  stage_box<NT, HZ, HY, HX, P>(g, slot_map(geom, g), rope_table(geom, g), z0, y0, x0, sSlot, sCS);
+  __syncthreads();
+
+  const int qn = threadIdx.x / LPQ, hh = threadIdx.x % LPQ;
+  const int tz = qn / (TY * TX), ty = (qn / TX) % TY, tx = qn % TX;
+  const int qs = ((tz + 1) * HY + (ty + 1)) * HX + (tx + 1);
+  const int qc = (tz * HY + ty) * HX + tx;  // the query's (-1, -1, -1) corner
+  const int i = sSlot[qs];
+  const int wbase = __builtin_amdgcn_readfirstlane(threadIdx.x & ~63);
+  // global loads first: raw K chunks, V straight to LDS, this lane's q and dO
+  // slices and the gate (O_glob and dq~_glob, needed only at the end, are
+  // loaded after the neighbour loop so they hold no registers through it)
+  bf16x8 kraw[RS];
+#pragma unroll
+  for (int r = 0; r < RS; r++) {
+    const int e = min((int)threadIdx.x + r * NT, NCK - 1);
+    const int hs = e / CPS, ch = e % CPS;
+    const int64_t off = ((bN + max(sSlot[hs], 0)) * g.Hkv + hk) * D + ch * 8;
+    kraw[r] = *reinterpret_cast<const bf16x8 *>(k + off);
+    __builtin_amdgcn_global_load_lds(v + off, (lds_ptr)&sK[(wbase + r * NT) * 8], 16, 0, 0);
+  }
+  const int64_t row = (bN + max(i, 0)) * g.H + h;
+  const int64_t off = row * D + hh * DH;
+  bf16x8 qraw[DH / 8], draw[DH / 8];
+#pragma unroll
+  for (int c8 = 0; c8 < DH / 8; c8++) {
+    qraw[c8] = *reinterpret_cast<const bf16x8 *>(q + off + 8 * c8);
+    draw[c8] = *reinterpret_cast<const bf16x8 *>(dout + off + 8 * c8);
+  }
+  const float gl = (float)gate[row];
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // every lane runs to the end (the barriers below need the whole
+  // workgroup); a query site off the grid stores nothing
+  const float qscale = g.scale * kLog2e;
+  const int rc3[3] = {tz + 1, ty + 1, tx + 1};
+
+  bf16x2 qp[DH / 2], dp[DH / 2];
+#pragma unroll
+  for (int c8 = 0; c8 < DH / 8; c8++) {
+    const int d0 = hh * DH + 8 * c8, a = d0 / DA, p0 = (d0 % DA) / 2;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      float x0 = (float)qraw[c8][2 * u], x1 = (float)qraw[c8][2 * u + 1];
+      rotate(x0, x1, cs_at(a, rc3[a], p0 + u));
+      qp[4 * c8 + u][0] = (bf16)(x0 * qscale);
+      qp[4 * c8 + u][1] = (bf16)(x1 * qscale);
+      dp[4 * c8 + u][0] = draw[c8][2 * u];
+      dp[4 * c8 + u][1] = draw[c8][2 * u + 1];
+    }
+  }
+  // u_j = <dO, v_j>, canonical offset order, from the staged values
+  float lg[27], uu[27];
+#pragma unroll
+  for (int kk = 0; kk < 27; kk++) {
+    const int hs = qc + halo_from_corner(kk, HY, HX);
+    const bf16x2 *vr = reinterpret_cast<const bf16x2 *>(sV + hs * D + hh * DH);
+    float a1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < DH / 2; j++) a1 = __builtin_amdgcn_fdot2_f32_bf16(dp[j], vr[j], a1, false);
+    uu[kk] = lane_sum<LPQ>(a1);
+    // a compiler-only fence per neighbour: the rows of the next ones are not
+    // loaded early, which would hold dozens of registers
+    asm volatile("" ::: "memory");
+  }
+  __syncthreads();  // the values are no longer read: the buffer takes the keys
+  // rotate the staged keys at their own coordinates, as the forward does
+#pragma unroll
+  for (int r = 0; r < RS; r++) {
+    const int e = (int)threadIdx.x + r * NT;
+    const int ec = min(e, NCK - 1);
+    const int hs = ec / CPS, ch = ec % CPS;
+    const int rc3[3] = {hs / (HY * HX), (hs / HX) % HY, hs % HX};
+    const int a = (ch * 8) / DA, p0 = ((ch * 8) % DA) / 2;
+    bf16x8 ko;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      float k0 = (float)kraw[r][2 * u], k1 = (float)kraw[r][2 * u + 1];
+      rotate(k0, k1, cs_at(a, rc3[a], p0 + u));
+      ko[2 * u] = (bf16)k0;
+      ko[2 * u + 1] = (bf16)k1;
+    }
+    *reinterpret_cast<bf16x8 *>(&sK[e * 8]) = ko;
+  }
+  __syncthreads();
+  // logits (log2 units), canonical offset order
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kk = 0; kk < 27; kk++) {
+    const int hs = qc + halo_from_corner(kk, HY, HX);
+    const bf16x2 *kr = reinterpret_cast<const bf16x2 *>(sK + hs * D + hh * DH);
+    float a0 = 0.f;
+#pragma unroll
+    for (int j = 0; j < DH / 2; j++) a0 = __builtin_amdgcn_fdot2_f32_bf16(qp[j], kr[j], a0, false);
+    a0 = lane_sum<LPQ>(a0);
+    lg[kk] = sSlot[hs] >= 0 ? a0 : -INFINITY;
+    mx = fmaxf(mx, lg[kk]);
+    asm volatile("" ::: "memory");
+  }
+  float den = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < 27; kk++) {
+    lg[kk] = __builtin_amdgcn_exp2f(lg[kk] - mx);  // 0 for an invalid neighbour
+    den += lg[kk];
+  }
+  const float inv = 1.0f / den;
+  asm volatile("" ::: "memory");  // the next phase re-reads its rows from LDS
+  float dol = 0.f;  // <dO, O_loc>
+#pragma unroll
+  for (int kk = 0; kk < 27; kk++) {
+    lg[kk] *= inv;
+    dol += lg[kk] * uu[kk];
+  }
+  const float gg = 1.0f / (1.0f + expf(-gl)), omg = 1.0f - gg;
+  const float delta = omg * dol;
+  // dq~ = sum_j dS_j k~_j on the matrix cores: the bf16 weights dS as
+  // triples (dx = -1, 0, +1) of each (dz, dy), packed as the words (w-, w0)
+  // and (w+, 0), moved to the product layout (lanes n, n + 32 for query n),
+  // then dq~^T (two 32-row tiles of channels x 32 queries) += K~^T * dS^T
+  // over the 3 planes x 4 blocks of 16 sites a plane of queries can see
+  uint32_t tD[9][2];
+#pragma unroll
+  for (int r9 = 0; r9 < 9; r9++) {
+    float w3[3];
+#pragma unroll
+    for (int dx = 0; dx < 3; dx++) {
+      const int kk = 3 * r9 + dx;
+      w3[dx] = lg[kk] * (omg * uu[kk] - delta);  // 0 for an invalid neighbour
+    }
+    bf16x2 t0, t1;
+    t0[0] = (bf16)w3[0];
+    t0[1] = (bf16)w3[1];
+    t1[0] = (bf16)w3[2];
+    t1[1] = (bf16)0.0f;
+    tD[r9][0] = __builtin_bit_cast(uint32_t, t0);
+    tD[r9][1] = __builtin_bit_cast(uint32_t, t1);
+  }
+  const int lane = threadIdx.x & 63;
+  const int hi = lane >> 5, ql = lane & 31;
+  const int pty = ql >> 3, ptx = ql & 7;
+#pragma unroll
+  for (int r9 = 0; r9 < 9; r9++)
+#pragma unroll
+    for (int w = 0; w < 2; w++) tD[r9][w] = (uint32_t)__shfl((int)tD[r9][w], 2 * ql);
+  f32x16 acc2[2];
+#pragma unroll
+  for (int t2 = 0; t2 < 2; t2++)
+#pragma unroll
+    for (int e = 0; e < 16; e++) acc2[t2][e] = 0.f;
+  {
+    const int grp = (lane >> 4) & 1, rq = lane & 3, re = (lane >> 2) & 3;
+    const int abase = (tz * NPL + re) * D + 16 * grp + 4 * rq;  // elements
+#pragma unroll
+    for (int kb4 = 0; kb4 < 4; kb4++) {
+      // this lane's window: sites kappa0 = 16*kb4 + 8*hi .. +7 of a plane
+      // (kappa = y*10 + x); at most one run of the query's neighbour rows
+      // meets it, at slot offset o in [-2, 7]
+      const int k0 = 16 * kb4 + 8 * hi;
+      const int sm = pty * 10 + ptx;
+      const int rel = k0 - sm + 7;
+      const int di = rel >= 0 ? rel / 10 : -1;
+      const bool ok = di >= 0 && di <= 2;
+      const int o = sm + 10 * di - k0;
+      const int m = ok ? (o >> 1) : -8;
+      const bool odd = (o & 1) != 0;
+      const uint32_t s0 = odd ? 0x01000C0Cu : 0x03020100u, s1 = odd ? 0x05040302u : 0x07060504u;
+      uint32_t sel[4];
+#pragma unroll
+      for (int jd = 0; jd < 4; jd++) sel[jd] = jd == m ? s0 : (jd == m + 1 ? s1 : 0x0C0C0C0Cu);
+#pragma unroll
+      for (int dzi = 0; dzi < 3; dzi++) {
+        const uint32_t x0 = di == 0 ? tD[3 * dzi][0] : (di == 1 ? tD[3 * dzi + 1][0] : tD[3 * dzi + 2][0]);
+        const uint32_t x1 = di == 0 ? tD[3 * dzi][1] : (di == 1 ? tD[3 * dzi + 1][1] : tD[3 * dzi + 2][1]);
+        uint32_t bw[4];
+#pragma unroll
+        for (int jd = 0; jd < 4; jd++) bw[jd] = __builtin_amdgcn_perm(x1, x0, sel[jd]);
+        bf16x8 bop;
+        __builtin_memcpy(&bop, bw, 16);
+#pragma unroll
+        for (int t2 = 0; t2 < 2; t2++) {
+          const int ad = abase + (dzi * NPL + k0) * D + 32 * t2;
+          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(sK + ad));
+          const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(sK + ad + 4 * D));
+          bf16x8 aop;
+          __builtin_memcpy(&aop, &lo, 8);
+          __builtin_memcpy(reinterpret_cast<char *>(&aop) + 8, &hi4, 8);
+          acc2[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, acc2[t2], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // Lane (n, hi) holds channels 8*jj + 4*hi .. +3 of query n (tile jj / 4,
+  // registers 4*(jj % 4) ..); the halves trade pieces (v_permlane32_swap) so
+  // that each lane holds channels 16*mm + 8*hi .. +7, mm = 0, 1, 2.
+  float od[3][8];
+#pragma unroll
+  for (int mm = 0; mm < 3; mm++)
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      // elements copied out first: a bit cast applied straight to a vector
+      // element subscript compiles to a cast of element 0
+      const float e0 = acc2[(2 * mm) / 4][4 * ((2 * mm) % 4) + u];
+      const float e1 = acc2[(2 * mm + 1) / 4][4 * ((2 * mm + 1) % 4) + u];
+      const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, e0),
+                                                       __builtin_bit_cast(uint32_t, e1), false, false);
+      od[mm][u] = __builtin_bit_cast(float, (uint32_t)sw[0]);
+      od[mm][4 + u] = __builtin_bit_cast(float, (uint32_t)sw[1]);
+    }
+  // dq = R^T (s dq~_loc + dq~_glob) for query n = ql of plane tz
+  {
+    const int pi = sSlot[((tz + 1) * HY + (pty + 1)) * HX + (ptx + 1)];
+    if (pi >= 0) {
+      const int prc3[3] = {tz + 1, pty + 1, ptx + 1};
+      const int64_t poff = ((bN + pi) * g.H + h) * D;
+#pragma unroll
+      for (int mm = 0; mm < 3; mm++) {
+        const int d0 = 16 * mm + 8 * hi;  // axis chunk mm, its planes 4*hi ..
+        const f32x4 g0 = *reinterpret_cast<const f32x4 *>(dqg + poff + d0);
+        const f32x4 g1 = *reinterpret_cast<const f32x4 *>(dqg + poff + d0 + 4);
+        const float gf[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+        bf16x8 ov;
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          float x0 = g.scale * od[mm][2 * u] + gf[2 * u];
+          float x1 = g.scale * od[mm][2 * u + 1] + gf[2 * u + 1];
+          rotate_t(x0, x1, cs_at(mm, prc3[mm], 4 * hi + u));
+          ov[2 * u] = (bf16)x0;
+          ov[2 * u + 1] = (bf16)x1;
+        }
+        *reinterpret_cast<bf16x8 *>(dq + poff + d0) = ov;
+      }
+    }
+  }
+  if (i < 0) return;
+  // dG = g (1 - g) (<dO, O_glob> - <dO, O_loc>)
+  bf16x8 oraw[DH / 8];
+#pragma unroll
+  for (int c8 = 0; c8 < DH / 8; c8++) oraw[c8] = *reinterpret_cast<const bf16x8 *>(oglob + off + 8 * c8);
+  float dgo = 0.f;
+#pragma unroll
+  for (int c8 = 0; c8 < DH / 8; c8++)
+#pragma unroll
+    for (int e = 0; e < 8; e++) dgo += (float)draw[c8][e] * (float)oraw[c8][e];
   dgo = lane_sum<LPQ>(dgo);
   if (hh == 0) {
     dgate[row] = (bf16)(gg * omg * (dgo - dol));
@@ -874,8 +1161,14 @@ hipError_t run_local_bwd_pair(const Geo &g, const BwdArgs &a, hipStream_t s) {
   {
     const int ntz = (g.Z + TZ - 1) / TZ, nty = (g.Y + TY - 1) / TY, ntx = (g.X + TX - 1) / TX;
     const int nt = (D / 24) * TZ * TY * TX;
-    hipLaunchKernelGGL((k_bwd_local_q_pair<D, TZ, TY, TX>),
-                       dim3((unsigned)(g.B * ntz * nty * ntx * g.H)), dim3(nt), 0, s, g, a.geom,
+    // head dim 48: dq~ on the matrix cores
+    auto qk = [] {
+      if constexpr (D == 48 && TZ == 4 && TY == 4 && TX == 8)
+        return k_bwd_local_q_tr48;
+      else
+        return k_bwd_local_q_pair<D, TZ, TY, TX>;
+    }();
+    hipLaunchKernelGGL(qk, dim3((unsigned)(g.B * ntz * nty * ntx * g.H)), dim3(nt), 0, s, g, a.geom,
                        static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.k),
                        static_cast<const bf16 *>(a.v), static_cast<const bf16 *>(a.gate),
                        static_cast<const bf16 *>(a.dout), static_cast<const bf16 *>(a.oglob), a.dqg,
