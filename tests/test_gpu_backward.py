@@ -58,6 +58,11 @@ CASES = [
        "random", "raster"), "token", 0),
     (W(132, "bf16_d48_m300_ragged_tail", (10, 12, 20), 1, 4, 48, (2, 2, 2), "bf16", "iid", "block",
        "raster", Hkv=2), "token", 0),
+    # the matrix-core local backward at head dim 48 with the summary-centre
+    # variant (its key side routes dK~ through the block-centre rotation),
+    # grouped heads and boxes cut by the grid edge
+    (W(133, "bf16_d48_centre_gqa", (6, 9, 10), 1, 4, 48, (2, 3, 2), "bf16", "iid", "random",
+       "raster", Hkv=2), "centre", 0),
 ]
 IDS = [f"{w.name}-{sr}" for w, sr, _ in CASES]
 BY_NAME = {w.name: (w, sr, excl) for w, sr, excl in CASES}
